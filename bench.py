@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the MatMulNBits hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  * decode: Y[1, 8192] = X[1, 2048] . deq(W)^T + (X.A).B, INT4 block-32 weights with the
+    default zero point and a rank-32 F16 LoRA fused in the same launch (in-pass T);
+  * prefill: Y[1024, 4096] = X[1024, 4096] . deq(W)^T + (X.A).B, INT4 block-32 with explicit
+    zero points, rank-32 F16 LoRA (T projection launch + MFMA GEMM with the T.B epilogue).
+Inputs are resident in HBM before timing.  Decode rotates over enough copies of its
+weights and adapter (default >= 1 GiB, four times the 256 MB Infinity Cache) that every
+call streams from HBM; the prefill GEMM is MFMA-bound and uses one copy.
+
+`value` is the decode GEMV's effective HBM bandwidth (algorithmic bytes / mean call time,
+GB/s); the prefill TFLOP/s rides along in `prefill`.  Call times are HIP events recorded on
+the stream the kernels are launched on, around every call in the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP16_PEAK_TFLOPS = 2516.6       # MI355X dense FP16 MFMA (256 CUs x 2.4 GHz x 4096 flop/clk)
+METRIC = "decode GEMV effective HBM GB/s (M=1) + prefill TFLOP/s (M=1024), % roofline"
+
+
+def algorithmic_bytes(M, N, K, bits, has_zp, rank):
+    """Bytes the method must move once: codes + scales + zero points + X + Y + adapter."""
+    b = N * K * bits // 8 + (N * K // 32) * 2 + (N * K // 32 * bits // 8 if has_zp else 0)
+    b += M * K * 2 + M * N * 2
+    if rank:
+        b += K * rank * 2 + rank * N * 2
+    return b
+
+
+def algorithmic_flops(M, N, K, rank):
+    return 2 * M * N * K + (2 * M * K * rank + 2 * M * rank * N if rank else 0)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cold-mib", type=int, default=1024, help="bytes of rotated decode copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see the sharding paragraph of the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    lib_path = os.path.join(ROOT, "blockwise_bit_quantized_amd", "libmnb.so")
+    if not os.path.exists(lib_path):
+        from blockwise_bit_quantized_amd import build as b
+        b.build()
+    import blockwise_bit_quantized_amd as mnb
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def t16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(dev)
+
+    def weight(case):
+        zp = torch.from_numpy(case["zp"]).to(dev) if case["zp"] is not None else None
+        return mnb.pack(torch.from_numpy(case["codes"]).to(dev), t16(case["scales"]), zp, case["bits"])
+
+    # ---- decode workload, rotated copies ----
+    dec = si.make_config(2)
+    dM, dN, dK = dec["M"], dec["N"], dec["K"]
+    dbytes = algorithmic_bytes(dM, dN, dK, 4, False, 32)
+    copies = max(1, math.ceil(args.cold_mib * 2**20 / dbytes))
+    pw0 = weight(dec)
+    X0, A0, B0 = t16(dec["X"]), t16(dec["adapter"]["A"]), t16(dec["adapter"]["B"])
+    dcopies = []
+    for _ in range(copies):
+        pw = mnb.PackedWeight(pw0.wq.clone(), pw0.sc.clone(), None, dN, dK, 4)
+        dcopies.append((X0.clone(), pw, mnb.Adapter(mnb.MNB_ADAPTER_F16, A0.clone(), B0.clone())))
+    Yd = torch.empty((dM, dN), dtype=torch.float16, device=dev)
+
+    # ---- prefill workload ----
+    pre = si.make_config(3)
+    pM, pN, pK = pre["M"], pre["N"], pre["K"]
+    pflops = algorithmic_flops(pM, pN, pK, 32)
+    pbytes = algorithmic_bytes(pM, pN, pK, 4, True, 32)
+    ppw = weight(pre)
+    pX = t16(pre["X"])
+    pad = mnb.Adapter(mnb.MNB_ADAPTER_F16, t16(pre["adapter"]["A"]), t16(pre["adapter"]["B"]))
+    Yp = torch.empty((pM, pN), dtype=torch.float16, device=dev)
+
+    ws = mnb.workspace(dev, max(mnb.mnb_workspace_bytes(dM, dN, dK, 4, 32),
+                                mnb.mnb_workspace_bytes(pM, pN, pK, 4, 32)))
+    torch.cuda.synchronize()
+
+    def decode(i):
+        X, pw, ad = dcopies[i % copies]
+        mnb.matmul(X, pw, ad, out=Yd, ws=ws)
+
+    def prefill():
+        mnb.matmul(pX, ppw, pad, out=Yp, ws=ws)
+
+    for i in range(args.warmup):
+        decode(i)
+        prefill()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        decode(args.warmup + i)
+        e[1].record()
+        e[2].record()
+        prefill()
+        e[3].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    pre_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    dec_s = float(dec_ms.mean()) * 1e-3
+    pre_s = float(pre_ms.mean()) * 1e-3
+    dec_gbps = dbytes / dec_s / 1e9
+    pre_tflops = pflops / pre_s / 1e12
+
+    # warm (Infinity-Cache resident) decode and the two-launch decode variant, for context
+    def timed(fn, n=200):
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for j in range(n):
+            a[j].record()
+            fn(j)
+            b[j].record()
+        torch.cuda.synchronize()
+        return float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)])) * 1e-3
+
+    warm_s = timed(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws))
+    tsep_s = timed(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd, ws=ws))
+    base_s = timed(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd, ws=ws))
+    dbytes_base = algorithmic_bytes(dM, dN, dK, 4, False, 0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(dec_gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; shapes of the pages' decode and prefill projections)",
+        "config": {
+            "workload": "decode GEMV M=1 N=8192 K=2048 int4 block-32 default-zp + rank-32 F16 LoRA "
+                        "(cold HBM, %d rotated copies) + prefill M=1024 N=4096 K=4096 int4 block-32 "
+                        "explicit-zp + rank-32 F16 LoRA" % copies,
+            "decode_bytes": dbytes, "prefill_flops": pflops,
+        },
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "gemv_kernel<4,false,1,0,8> (one launch per decode call)",
+                     "mean_us": round(dec_s * 1e6, 3)},
+        "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "mean_us": round(pre_s * 1e6, 3),
+                    "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": FP16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4),
+                                 "traffic": None},
+                    "bytes": pbytes},
+        "decode_context": {"warm_us": round(warm_s * 1e6, 3), "warm_GBps": round(dbytes / warm_s / 1e9, 1),
+                           "t_separate_us": round(tsep_s * 1e6, 3),
+                           "empty_adapter_us": round(base_s * 1e6, 3),
+                           "empty_adapter_GBps": round(dbytes_base / base_s / 1e9, 1)},
+        "wall_s": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(si, dec, pre, dbytes, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(si, dec, pre, dbytes, budget_s):
+    """The FP64 oracle as it stands, on this host's cores, on a bounded sample."""
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(threads)
+    oracle.matmul(dict(dec, X=dec["X"][:1], M=1, N=64, codes=dec["codes"][:64], scales=dec["scales"][:64],
+                       adapter=None))                       # load + warm
+    t = []
+    t_end = time.perf_counter() + budget_s * 0.6
+    while time.perf_counter() < t_end or len(t) < 2:
+        a = time.perf_counter()
+        oracle.matmul(dec)
+        t.append(time.perf_counter() - a)
+    dec_s = float(np.median(t))
+    rows = 8
+    a = time.perf_counter()
+    oracle.matmul(dict(pre, X=pre["X"][:rows], M=rows))
+    pre_s = time.perf_counter() - a
+    pre_flops = algorithmic_flops(rows, pre["N"], pre["K"], 32)
+    return {"value": round(dbytes / dec_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "decode 8192x2048 int4 + F16 LoRA, full call, median of %d runs (%.3f s each); "
+                      "prefill sample %d of 1024 rows of 1024x4096x4096: %.4f TFLOP/s"
+                      % (len(t), dec_s, rows, pre_flops / pre_s / 1e12),
+            "decode_s": round(dec_s, 4), "prefill_rows_s": round(pre_s, 3),
+            "prefill_TFLOPs": round(pre_flops / pre_s / 1e12, 6)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,212 @@
+"""Python binding of libmnb: MatMulNBits with a fused rank-32 LoRA term on MI355X (gfx950).
+
+The C ABI (``include/mnb.h``) is exposed under its own names (``mnb_pack``,
+``mnb_matmul`` ...) taking plain integers for device pointers and the stream.  The
+convenience wrappers (``pack``, ``unpack``, ``matmul``) only marshal torch tensors into
+those calls: every step of the computation runs in the HIP kernels of ``libmnb.so``.
+Importing this package fails if ``libmnb.so`` has not been built (there is no fallback).
+
+Operation (onnxruntime PR #33370 "[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits";
+PR #33800 "Fuse DQ->MatMulNBits for shared initializers and skip outer-scope weights"):
+    Y[M,N] = X[M,K] . deq(W)^T + (X . A) . B,   deq(W)[n,k] = (q[n,k] - z[n,k/32]) * s[n,k/32]
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmnb.so")
+
+MNB_OK, MNB_ERR_INVALID_ARG, MNB_ERR_UNSUPPORTED, MNB_ERR_MISALIGNED = 0, 1, 2, 3
+MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP = 4, 5, 6
+MNB_ADAPTER_NONE, MNB_ADAPTER_F16, MNB_ADAPTER_Q8 = 0, 1, 2
+MNB_PATH_AUTO, MNB_PATH_GEMV, MNB_PATH_GEMM = 0, 1, 2
+MNB_FLAG_T_SEPARATE = 1
+
+
+class mnb_adapter(C.Structure):
+    _fields_ = [("kind", C.c_int), ("rank", C.c_int), ("A", C.c_void_p), ("A_scales", C.c_void_p),
+                ("B", C.c_void_p), ("B_scales", C.c_void_p)]
+
+
+class mnb_options(C.Structure):
+    _fields_ = [("path", C.c_int), ("flags", C.c_int)]
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmnb.so is not built (%s); run `python -m blockwise_bit_quantized_amd.build`"
+                          % LIB_PATH)
+    lib = C.CDLL(LIB_PATH)
+    P, I, S = C.c_void_p, C.c_int, C.c_size_t
+    lib.mnb_packed_sizes.argtypes = [I, I, I, I, I, C.POINTER(S), C.POINTER(S), C.POINTER(S)]
+    lib.mnb_pack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+    lib.mnb_unpack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+    lib.mnb_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.mnb_workspace_bytes.restype = S
+    lib.mnb_matmul.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P]
+    lib.mnb_matmul_ex.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P,
+                                  C.POINTER(mnb_options)]
+    lib.mnb_describe_route.argtypes = [I, I, I, I, I, I, C.POINTER(mnb_options), C.c_char_p, S]
+    lib.mnb_status_string.argtypes = [I]
+    lib.mnb_status_string.restype = C.c_char_p
+    lib.mnb_version.argtypes = []
+    for f in ("mnb_packed_sizes", "mnb_pack", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
+              "mnb_describe_route", "mnb_version"):
+        getattr(lib, f).restype = I
+    return lib
+
+
+lib = _load()
+
+# ---------------------------------------------------------------------------------------
+# The C ABI under its own names (integers for pointers and the stream)
+# ---------------------------------------------------------------------------------------
+
+
+def mnb_version() -> int:
+    return lib.mnb_version()
+
+
+def mnb_status_string(status: int) -> str:
+    return lib.mnb_status_string(status).decode()
+
+
+def mnb_packed_sizes(N, K, bits, block, has_zp):
+    a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    st = lib.mnb_packed_sizes(N, K, bits, block, int(bool(has_zp)), C.byref(a), C.byref(b), C.byref(c))
+    return st, a.value, b.value, c.value
+
+
+def mnb_pack(codes, scales, zp, N, K, bits, block, wq, sc, zpp, stream) -> int:
+    return lib.mnb_pack(codes, scales, zp, N, K, bits, block, wq, sc, zpp, stream)
+
+
+def mnb_unpack(wq, sc, zpp, N, K, bits, block, codes, scales, zp, stream) -> int:
+    return lib.mnb_unpack(wq, sc, zpp, N, K, bits, block, codes, scales, zp, stream)
+
+
+def mnb_workspace_bytes(M, N, K, bits, rank) -> int:
+    return lib.mnb_workspace_bytes(M, N, K, bits, rank)
+
+
+def mnb_matmul(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream) -> int:
+    return lib.mnb_matmul(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, Y, M, N, K, bits,
+                          block, workspace, ws_bytes, stream)
+
+
+def mnb_matmul_ex(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream, opt) -> int:
+    return lib.mnb_matmul_ex(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, Y, M, N, K, bits,
+                             block, workspace, ws_bytes, stream, C.byref(opt) if opt is not None else None)
+
+
+def mnb_describe_route(M, N, K, bits, has_zp, adapter_kind, opt=None):
+    buf = C.create_string_buffer(256)
+    st = lib.mnb_describe_route(M, N, K, bits, int(bool(has_zp)), adapter_kind,
+                                C.byref(opt) if opt is not None else None, buf, 256)
+    return st, buf.value.decode()
+
+
+# ---------------------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------------------
+
+
+def _check(st: int):
+    if st != MNB_OK:
+        raise RuntimeError(mnb_status_string(st))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    import torch
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+@dataclass
+class PackedWeight:
+    wq: object          # torch.uint8 device tensor
+    sc: object          # torch.float16 device tensor (scale bit patterns)
+    zp: object          # torch.uint8 device tensor or None (default zero point)
+    N: int
+    K: int
+    bits: int
+
+
+@dataclass
+class Adapter:
+    kind: int           # MNB_ADAPTER_F16 or MNB_ADAPTER_Q8
+    A: object
+    B: object
+    A_scales: object = None
+    B_scales: object = None
+    rank: int = 32
+
+    def struct(self) -> mnb_adapter:
+        return mnb_adapter(self.kind, self.rank, _ptr(self.A), _ptr(self.A_scales), _ptr(self.B),
+                           _ptr(self.B_scales))
+
+
+def pack(codes, scales, zp, bits: int) -> PackedWeight:
+    """Pack device tensors codes uint8 [N,K], scales fp16 [N,K/32], zp uint8 [N,K/32] | None."""
+    import torch
+    N, K = codes.shape
+    st, wqb, scb, zpb = mnb_packed_sizes(N, K, bits, 32, zp is not None)
+    _check(st)
+    dev = codes.device
+    wq = torch.empty(wqb, dtype=torch.uint8, device=dev)
+    sc = torch.empty(scb // 2, dtype=torch.float16, device=dev)
+    zpp = torch.empty(zpb, dtype=torch.uint8, device=dev) if zp is not None else None
+    _check(mnb_pack(_ptr(codes), _ptr(scales), _ptr(zp), N, K, bits, 32, _ptr(wq), _ptr(sc), _ptr(zpp),
+                    _stream(dev)))
+    return PackedWeight(wq, sc, zpp, N, K, bits)
+
+
+def unpack(pw: PackedWeight):
+    import torch
+    dev = pw.wq.device
+    codes = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=dev)
+    scales = torch.empty((pw.N, pw.K // 32), dtype=torch.float16, device=dev)
+    zp = torch.empty((pw.N, pw.K // 32), dtype=torch.uint8, device=dev) if pw.zp is not None else None
+    _check(mnb_unpack(_ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), pw.N, pw.K, pw.bits, 32, _ptr(codes),
+                      _ptr(scales), _ptr(zp), _stream(dev)))
+    return codes, scales, zp
+
+
+_ws_cache: dict = {}
+
+
+def workspace(dev, nbytes: int):
+    """A zero-initialised workspace of at least ``nbytes`` for ``dev``, reused across calls
+    made from this process on one stream at a time (the library keeps its counters zero)."""
+    import torch
+    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
+           flags: int = 0, out=None, ws=None):
+    """Y = X . deq(W)^T (+ (X.A).B) for a device fp16 X [M, K]; returns fp16 Y [M, N]."""
+    import torch
+    M, K = X.shape
+    if K != pw.K:
+        raise ValueError("X has K=%d, weight has K=%d" % (K, pw.K))
+    dev = X.device
+    Y = out if out is not None else torch.empty((M, pw.N), dtype=torch.float16, device=dev)
+    need = mnb_workspace_bytes(M, pw.N, K, pw.bits, 32 if adapter is not None else 0)
+    if ws is None:
+        ws = workspace(dev, need)
+    ad = adapter.struct() if adapter is not None else None
+    opt = mnb_options(path, flags)
+    _check(mnb_matmul_ex(_ptr(X), _ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), ad, _ptr(Y), M, pw.N, K, pw.bits,
+                         32, _ptr(ws), ws.numel(), _stream(dev), opt))
+    return Y

@@ -1,0 +1,393 @@
+// api.hip -- the exported C ABI of libmnb (declared in include/mnb.h): argument
+// validation, the M-based dispatcher, workspace layout and kernel launches.
+//
+// Dispatch (onnxruntime PR #33370 "[WebGPU] Fuse rank-32 quantized LoRA with
+// MatMulNBits", commit list: the automatic mode selects the prefill path for M > 1 and the
+// decode path for M == 1 on each invocation, from X's row count; a one-token prompt uses
+// the decode path; explicit overrides are kept for comparisons).
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "mnb.h"
+
+using namespace mnb;
+
+namespace {
+
+enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// ---- plan -------------------------------------------------------------------------------
+
+// K-split of the decode GEMV.  Each part holds at least one block per wave (4) and at most
+// 8 per wave (32), and the grid aims to cover the 256 CUs.  Forced GEMV with M > 1 uses
+// one part per group (no partial buffers) and loops over K inside each wave.
+constexpr int kMaxCounters = 4096;  // group / tile counters held in the workspace
+
+void gemv_split(int N, int K, int M, int *split, int *bpp) {
+  const int NG = cdiv(N, kGroup), KB = K / kBlock;
+  if (M != 1 || KB == 0 || NG == 0) {
+    *split = 1;
+    *bpp = std::max(KB, 1);
+    return;
+  }
+  if (NG > kMaxCounters) {
+    *split = 1;
+    *bpp = KB;
+    return;
+  }
+  const int need = cdiv(KB, 32);
+  const int fill = cdiv(kCUs, NG);
+  const int cap = std::max(1, KB / 4);
+  int s = std::max(need, std::min(fill, cap));
+  s = std::max(1, std::min(s, KB));
+  const int b = cdiv(KB, s);
+  *bpp = b;
+  *split = cdiv(KB, b);
+}
+
+constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice
+constexpr int kTprojKP = 512;     // T projection: K per workgroup part
+
+// Workspace: a fixed-size counter area first (its offsets depend on nothing, so a zeroed
+// workspace stays valid for calls of any shape), then data regions that need no init.
+constexpr size_t kCtrlBytes = CTRL_WORDS * sizeof(int);
+constexpr size_t kCntOff = kCtrlBytes;                                  // GEMV group counters
+constexpr size_t kTpCntOff = kCntOff + (size_t)kMaxCounters * sizeof(int);  // T tile counters
+constexpr size_t kDataOff = kTpCntOff + (size_t)kMaxCounters * sizeof(int);
+
+struct WsLayout {
+  size_t ctrl, tpart, tfin, part, cnt, tp_part, tp_cnt, t16, total;
+  int gt, split, bpp, tp_parts, tp_mt;
+};
+
+WsLayout ws_layout(int M, int N, int K, int rank) {
+  WsLayout w{};
+  const int NG = cdiv(N, kGroup);
+  gemv_split(N, K, M == 1 ? 1 : M, &w.split, &w.bpp);
+  w.gt = cdiv(K, kTSliceRows);
+  w.tp_mt = cdiv(M, 32);
+  w.tp_parts = w.tp_mt > kMaxCounters ? 1 : std::max(1, cdiv(K, kTprojKP));
+  w.ctrl = 0;
+  w.cnt = kCntOff;
+  w.tp_cnt = kTpCntOff;
+  size_t off = align_up(kDataOff);
+  w.tpart = off;
+  if (rank) off += align_up((size_t)w.gt * kRank * sizeof(float));
+  w.tfin = off;
+  if (rank) off += align_up(kRank * sizeof(float));
+  w.part = off;
+  if (M == 1 && w.split > 1) off += align_up((size_t)w.split * NG * kGroup * sizeof(float));
+  w.tp_part = off;
+  if (rank && w.tp_parts > 1) off += align_up((size_t)w.tp_parts * w.tp_mt * 32 * kRank * sizeof(float));
+  w.t16 = off;
+  if (rank) off += align_up((size_t)M * kRank * sizeof(uint16_t));
+  w.total = off;
+  return w;
+}
+
+struct Route {
+  int path;      // MNB_PATH_GEMV / MNB_PATH_GEMM
+  int lora;      // LORA_*
+  int tmode;     // 0 in-pass, 1 precomputed by the T projection launch
+  bool tproj;
+};
+
+Route route(int M, int lora, const mnb_options *opt) {
+  Route r{};
+  const int path = opt ? opt->path : MNB_PATH_AUTO;
+  const int flags = opt ? opt->flags : 0;
+  r.path = path != MNB_PATH_AUTO ? path : (M == 1 ? MNB_PATH_GEMV : MNB_PATH_GEMM);
+  r.lora = lora;
+  r.tmode = 1;
+  r.tproj = false;
+  if (lora) {
+    if (r.path == MNB_PATH_GEMV && M == 1 && !(flags & MNB_FLAG_T_SEPARATE)) r.tmode = 0;
+    else r.tproj = true;
+  }
+  return r;
+}
+
+// ---- validation ---------------------------------------------------------------------------
+
+bool misaligned(const void *p) { return p && ((uintptr_t)p & 15u); }
+
+struct Range {
+  const void *p;
+  size_t n;
+};
+bool overlap(const void *a, size_t an, Range b) {
+  if (!a || !b.p || an == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + an;
+}
+
+int effective_lora(const mnb_adapter *ad) {
+  if (!ad || ad->kind == MNB_ADAPTER_NONE || ad->rank == 0 || !ad->A || !ad->B) return LORA_NONE;
+  return ad->kind == MNB_ADAPTER_F16 ? LORA_F16 : LORA_Q8;
+}
+
+int check_common(int M, int N, int K, int bits, int block) {
+  if (M < 0 || N < 0 || K < 0) return MNB_ERR_INVALID_ARG;
+  if (bits != 4 && bits != 8) return MNB_ERR_UNSUPPORTED;
+  if (block != kBlock || K % kBlock) return MNB_ERR_UNSUPPORTED;
+  return MNB_OK;
+}
+
+int validate(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad,
+             const void *Y, int M, int N, int K, int bits, int block, const void *ws, size_t ws_bytes,
+             const mnb_options *opt) {
+  int st = check_common(M, N, K, bits, block);
+  if (st) return st;
+  if (opt) {
+    if (opt->path < MNB_PATH_AUTO || opt->path > MNB_PATH_GEMM) return MNB_ERR_INVALID_ARG;
+    if (opt->flags & ~MNB_FLAG_T_SEPARATE) return MNB_ERR_INVALID_ARG;
+  }
+  if (ad) {
+    if (ad->kind < MNB_ADAPTER_NONE || ad->kind > MNB_ADAPTER_Q8 || ad->rank < 0) return MNB_ERR_INVALID_ARG;
+  }
+  const int lora = effective_lora(ad);
+  if (lora && ad->rank != kRank) return MNB_ERR_UNSUPPORTED;
+  if (lora == LORA_Q8 && (!ad->A_scales || !ad->B_scales)) return MNB_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return MNB_OK;
+  if (!Y) return MNB_ERR_INVALID_ARG;
+  if (K > 0 && (!X || !wq || !sc)) return MNB_ERR_INVALID_ARG;
+  if (misaligned(X) || misaligned(wq) || misaligned(sc) || misaligned(zpp) || misaligned(Y) || misaligned(ws))
+    return MNB_ERR_MISALIGNED;
+  if (lora && (misaligned(ad->A) || misaligned(ad->B) || misaligned(ad->A_scales) || misaligned(ad->B_scales)))
+    return MNB_ERR_MISALIGNED;
+  if (K > 0) {
+    const size_t need = mnb_workspace_bytes(M, N, K, bits, lora ? kRank : 0);
+    if (need > 0 && (!ws || ws_bytes < need)) return MNB_ERR_WORKSPACE;
+  }
+  size_t wqb = 0, scb = 0, zpb = 0;
+  mnb_packed_sizes(N, K, bits, block, zpp != nullptr, &wqb, &scb, &zpb);
+  const size_t ybytes = (size_t)M * N * 2;
+  Range ins[] = {{X, (size_t)M * K * 2}, {wq, wqb}, {sc, scb}, {zpp, zpb}, {ws, ws_bytes},
+                 {lora ? ad->A : nullptr, (size_t)K * kRank * (lora == LORA_F16 ? 2 : 1)},
+                 {lora ? ad->B : nullptr, (size_t)kRank * N * (lora == LORA_F16 ? 2 : 1)},
+                 {lora == LORA_Q8 ? ad->A_scales : nullptr, (size_t)(K / kBlock) * kRank * 2},
+                 {lora == LORA_Q8 ? ad->B_scales : nullptr, (size_t)N * 2}};
+  for (const Range &r : ins)
+    if (overlap(Y, ybytes, r)) return MNB_ERR_ALIAS;
+  return MNB_OK;
+}
+
+void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, const Route &r) {
+  const WsLayout w = ws_layout(M, N, K, r.lora ? kRank : 0);
+  const char *ln = r.lora == LORA_NONE ? "none" : (r.lora == LORA_F16 ? "f16" : "q8");
+  char tp[96] = "";
+  if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tp_mt * w.tp_parts, w.tp_parts);
+  if (r.path == MNB_PATH_GEMV) {
+    const int NG = cdiv(N, kGroup);
+    const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
+    snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d split=%d bpp=%d bpw=%d gt=%d", tp, bits,
+             has_zp ? "x" : "def", ln, r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base",
+             NG * w.split + extra, M, w.split, w.bpp, cdiv(w.bpp, 4) <= 4 ? 4 : 8, extra);
+  } else {
+    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64", tp, bits, has_zp ? "x" : "def", ln,
+             cdiv(M, 128) * cdiv(N, 128));
+  }
+}
+
+bool log_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char *e = getenv("MNB_LOG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mnb_version(void) { return 100; }
+
+const char *mnb_status_string(int status) {
+  switch (status) {
+    case MNB_OK: return "MNB_OK";
+    case MNB_ERR_INVALID_ARG: return "MNB_ERR_INVALID_ARG: invalid argument";
+    case MNB_ERR_UNSUPPORTED: return "MNB_ERR_UNSUPPORTED: unsupported setting (bits 4/8, block 32, K%32==0, rank 0/32)";
+    case MNB_ERR_MISALIGNED: return "MNB_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
+    case MNB_ERR_WORKSPACE: return "MNB_ERR_WORKSPACE: workspace missing or too small";
+    case MNB_ERR_ALIAS: return "MNB_ERR_ALIAS: output overlaps an input or the workspace";
+    case MNB_ERR_HIP: return "MNB_ERR_HIP: HIP runtime error";
+    default: return "unknown mnb status";
+  }
+}
+
+int mnb_packed_sizes(int N, int K, int bits, int block, int has_zp, size_t *wq_bytes, size_t *sc_bytes,
+                     size_t *zp_bytes) {
+  const int st = check_common(0, N, K, bits, block);
+  if (st) return st;
+  const size_t tiles = (size_t)cdiv(N, kGroup) * (K / kBlock);
+  if (wq_bytes) *wq_bytes = tiles * kGroup * 16 * (bits / 4);
+  if (sc_bytes) *sc_bytes = tiles * kGroup * 2;
+  if (zp_bytes) *zp_bytes = has_zp ? tiles * kGroup * bits / 8 : 0;
+  return MNB_OK;
+}
+
+size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank) {
+  (void)bits;
+  if (M <= 0 || N <= 0 || K < 0) return 0;
+  return ws_layout(M, N, K, rank ? kRank : 0).total;
+}
+
+int mnb_pack(const uint8_t *codes, const void *scales, const uint8_t *zp, int N, int K, int bits, int block,
+             void *wq, void *sc, void *zpp, void *stream) {
+  int st = check_common(0, N, K, bits, block);
+  if (st) return st;
+  if (N == 0 || K == 0) return MNB_OK;
+  if (!codes || !scales || !wq || !sc || (zp && !zpp)) return MNB_ERR_INVALID_ARG;
+  if (misaligned(codes) || misaligned(scales) || misaligned(zp) || misaligned(wq) || misaligned(sc) ||
+      (zp && misaligned(zpp)))
+    return MNB_ERR_MISALIGNED;
+  PackParams p{codes, static_cast<const uint16_t *>(scales), zp, static_cast<uint8_t *>(wq),
+               static_cast<uint16_t *>(sc), static_cast<uint8_t *>(zpp), N, K, cdiv(N, kGroup), K / kBlock};
+  if (!zp) p.zpp = nullptr;
+  return launch_pack(bits, p, static_cast<hipStream_t>(stream)) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+}
+
+int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, int bits, int block,
+               uint8_t *codes, void *scales, uint8_t *zp, void *stream) {
+  int st = check_common(0, N, K, bits, block);
+  if (st) return st;
+  if ((zp == nullptr) != (zpp == nullptr)) return MNB_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return MNB_OK;
+  if (!wq || !sc || !codes || !scales) return MNB_ERR_INVALID_ARG;
+  if (misaligned(codes) || misaligned(scales) || misaligned(zp) || misaligned(wq) || misaligned(sc) ||
+      misaligned(zpp))
+    return MNB_ERR_MISALIGNED;
+  PackParams p{nullptr, nullptr, static_cast<const uint8_t *>(zpp), const_cast<uint8_t *>(static_cast<const uint8_t *>(wq)),
+               const_cast<uint16_t *>(static_cast<const uint16_t *>(sc)), nullptr, N, K, cdiv(N, kGroup), K / kBlock};
+  return launch_unpack(bits, p, codes, static_cast<uint16_t *>(scales), zp, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? MNB_OK
+             : MNB_ERR_HIP;
+}
+
+int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapter_kind, const mnb_options *opt,
+                       char *buf, size_t buf_len) {
+  int st = check_common(M, N, K, bits, kBlock);
+  if (st) return st;
+  if (has_adapter_kind < 0 || has_adapter_kind > 2 || !buf || buf_len == 0) return MNB_ERR_INVALID_ARG;
+  if (opt && (opt->path < 0 || opt->path > 2 || (opt->flags & ~MNB_FLAG_T_SEPARATE))) return MNB_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) {
+    snprintf(buf, buf_len, "noop");
+    return MNB_OK;
+  }
+  if (K == 0) {
+    snprintf(buf, buf_len, "fill_zero");
+    return MNB_OK;
+  }
+  describe(buf, buf_len, M, N, K, bits, has_zp, route(M, has_adapter_kind, opt));
+  return MNB_OK;
+}
+
+int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad, void *Y,
+                  int M, int N, int K, int bits, int block, void *workspace, size_t ws_bytes, void *stream,
+                  const mnb_options *opt) {
+  int st = validate(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, opt);
+  if (st) return st;
+  if (M == 0 || N == 0) return MNB_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t *Yh = static_cast<uint16_t *>(Y);
+  if (K == 0) return launch_fill_zero(Yh, (long)M * N, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+
+  const int lora = effective_lora(ad);
+  const Route r = route(M, lora, opt);
+  const WsLayout w = ws_layout(M, N, K, lora ? kRank : 0);
+  char *ws = static_cast<char *>(workspace);
+  const int NG = cdiv(N, kGroup), KB = K / kBlock;
+  const bool has_zp = zpp != nullptr;
+  if (log_enabled()) {
+    char b[256];
+    describe(b, sizeof b, M, N, K, bits, has_zp, r);
+    fprintf(stderr, "[mnb] M=%d N=%d K=%d bits=%d: %s\n", M, N, K, bits, b);
+  }
+
+  uint16_t *t16 = lora ? reinterpret_cast<uint16_t *>(ws + w.t16) : nullptr;
+  if (r.tproj) {
+    TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), t16,
+                   reinterpret_cast<float *>(ws + w.tp_part), reinterpret_cast<int *>(ws + w.tp_cnt), M, K,
+                   w.tp_mt, w.tp_parts, kTprojKP};
+    if (launch_tproj(lora, tp, s) != hipSuccess) return MNB_ERR_HIP;
+  }
+
+  if (r.path == MNB_PATH_GEMV) {
+    GemvParams p{};
+    p.X = static_cast<const uint16_t *>(X);
+    p.wq = static_cast<const uint8_t *>(wq);
+    p.sc = static_cast<const uint16_t *>(sc);
+    p.zp = static_cast<const uint8_t *>(zpp);
+    if (lora) {
+      p.A = ad->A;
+      p.sA = static_cast<const uint16_t *>(ad->A_scales);
+      p.B = ad->B;
+      p.sB = static_cast<const uint16_t *>(ad->B_scales);
+    }
+    p.Y = Yh;
+    p.N = N;
+    p.K = K;
+    p.NG = NG;
+    p.KB = KB;
+    p.split = w.split;
+    p.bpp = w.bpp;
+    p.gt = (lora && r.tmode == 0) ? w.gt : 0;
+    p.kt = kTSliceRows;
+    p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
+    p.tpart = reinterpret_cast<float *>(ws + w.tpart);
+    p.tfin = reinterpret_cast<float *>(ws + w.tfin);
+    p.part = reinterpret_cast<float *>(ws + w.part);
+    p.cnt = reinterpret_cast<int *>(ws + w.cnt);
+    p.t16 = t16;
+    // rows in chunks that respect the grid's y limit
+    const int kMaxY = 65535;
+    for (int m0 = 0; m0 < M; m0 += kMaxY) {
+      const int mc = std::min(kMaxY, M - m0);
+      GemvParams q = p;
+      q.X = p.X + (size_t)m0 * K;
+      q.Y = p.Y + (size_t)m0 * N;
+      if (t16) q.t16 = t16 + (size_t)m0 * kRank;
+      q.M = mc;
+      const int gx = NG * w.split + p.gt;
+      if (launch_gemv(bits, has_zp, lora, r.tmode, q, gx, mc, s) != hipSuccess) return MNB_ERR_HIP;
+    }
+    return MNB_OK;
+  }
+
+  GemmParams g{};
+  g.X = static_cast<const uint16_t *>(X);
+  g.wq = static_cast<const uint8_t *>(wq);
+  g.sc = static_cast<const uint16_t *>(sc);
+  g.zp = static_cast<const uint8_t *>(zpp);
+  if (lora) {
+    g.B = ad->B;
+    g.sB = static_cast<const uint16_t *>(ad->B_scales);
+  }
+  g.t16 = t16;
+  g.Y = Yh;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.NG = NG;
+  g.KB = KB;
+  g.MT = cdiv(M, 128);
+  g.NT = cdiv(N, 128);
+  return launch_gemm(bits, has_zp, lora, g, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+}
+
+int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad, void *Y, int M,
+               int N, int K, int bits, int block, void *workspace, size_t ws_bytes, void *stream) {
+  return mnb_matmul_ex(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"

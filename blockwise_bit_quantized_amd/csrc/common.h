@@ -1,0 +1,144 @@
+// common.h -- types, packed-layout geometry and launch parameters shared by the libmnb
+// kernels (gfx950 / CDNA4, wave64).
+//
+// Packed layout (this library's own; the pages fix only "INT4/INT8 codes in blocks of 32
+// along K with an FP16 scale and an optional zero point per block"):
+//   * weight rows are grouped by 64 (NG = ceil(N/64) groups, padded rows are zero);
+//   * K is split in KB = K/32 blocks; one block of one row is C = bits/4 chunks of 16 B;
+//   * chunk (g, kb, c, r) lives at byte ((((g*KB + kb)*C + c)*64 + r) * 16), so one
+//     wave64 load instruction of 16 B per lane reads 1 KiB of contiguous codes: 64 rows of
+//     one block (4-bit) or 64 rows of half a block (8-bit);
+//   * 4-bit chunk: 32-bit word j (bytes 4j..4j+3, little-endian) holds k = 8j..8j+7 with
+//     nibble i = k 8j+2i (bits 4i..4i+3) and nibble 4+i = k 8j+2i+1 (bits 16+4i..).  The
+//     mask 0x000F000F applied to (word >> 4i) then yields the pair (k, k+1) in the two
+//     16-bit halves, which is exactly the packed-fp16 pair order of natural X;
+//   * 8-bit chunk c: byte b holds k = 16c + b;
+//   * scales fp16 at ((g*KB + kb)*64 + r); zero points (4-bit) two per byte at
+//     ((g*KB + kb)*32 + r/2), low nibble for even r; (8-bit) one byte at ((g*KB+kb)*64 + r).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mnb {
+
+constexpr int kGroup = 64;   // weight rows per interleaved group (= wave64 lanes)
+constexpr int kBlock = 32;   // quantization block along K
+constexpr int kRank = 32;    // LoRA rank supported by the kernels
+constexpr int kCUs = 256;    // MI355X compute units (planning constant)
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f16x_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2_t, v); }
+__device__ __forceinline__ uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Device-scope (all XCDs) ordering.  Partial sums written by one workgroup and read by
+// another that may sit on another XCD go through release/acquire at agent scope.
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ int atomic_add_agent(int *p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int atomic_load_agent(const int *p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(int *p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Convert 4-bit codes to fp16 pairs: 0x6400 is 1024.0 in binary16, so OR-ing a 4-bit
+// code into the low mantissa bits gives exactly 1024 + code; subtracting 1024 + z (also
+// exact) yields the exact integer (code - z).
+__device__ __forceinline__ h2_t nib_pair(uint32_t w, int i) {
+  return as_h2(((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
+}
+// Same for two 8-bit codes (bytes b0, b1 of w -> halves), via v_perm_b32 with the
+// constant byte 0x64 taken from the first operand.
+__device__ __forceinline__ h2_t byte_pair_lo(uint32_t w) {
+  return as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04010400u));
+}
+__device__ __forceinline__ h2_t byte_pair_hi(uint32_t w) {
+  return as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
+}
+
+// Control words at the start of the workspace (counters return to zero after each call).
+enum { CTRL_TCOUNT = 0, CTRL_TFLAG = 1, CTRL_TDONE = 2, CTRL_ERROR = 3, CTRL_WORDS = 64 };
+
+// Bounded wait for the in-pass T handoff; on expiry the kernel records CTRL_ERROR and
+// uses NaN for T so the failure is visible in Y rather than hanging the device.
+constexpr int kSpinLimit = 1 << 22;
+
+// ----------------------------------------------------------------------------------------
+// Launch parameter blocks
+// ----------------------------------------------------------------------------------------
+
+struct GemvParams {
+  const uint16_t *X;      // [M, K]
+  const uint8_t *wq;      // packed codes
+  const uint16_t *sc;     // packed scales
+  const uint8_t *zp;      // packed zero points or null
+  const void *A;          // adapter factors (kind-dependent)
+  const uint16_t *sA;
+  const void *B;
+  const uint16_t *sB;
+  uint16_t *Y;            // [M, N]
+  int M, N, K, NG, KB;
+  int split;              // K-parts per 64-row group (M == 1 only)
+  int bpp;                // blocks per part
+  int gt;                 // in-pass T: number of T slices (first gt workgroups)
+  int kt;                 // in-pass T: k rows per slice
+  int *ctrl;              // control words
+  float *tpart;           // [gt, 32]
+  float *tfin;            // [32]
+  float *part;            // [split, NG*64]
+  int *cnt;               // [NG]
+  const uint16_t *t16;    // precomputed T [M, 32] fp16
+};
+
+struct TprojParams {
+  const uint16_t *X;
+  const void *A;
+  const uint16_t *sA;
+  uint16_t *t16;          // [M, 32]
+  float *tpart;           // [parts, MT*32, 32]
+  int *cnt;               // [MT]
+  int M, K, MT, parts, kp;
+};
+
+struct GemmParams {
+  const uint16_t *X;
+  const uint8_t *wq;
+  const uint16_t *sc;
+  const uint8_t *zp;
+  const void *B;
+  const uint16_t *sB;
+  const uint16_t *t16;
+  uint16_t *Y;
+  int M, N, K, NG, KB, MT, NT;
+};
+
+struct PackParams {
+  const uint8_t *codes;
+  const uint16_t *scales;
+  const uint8_t *zp;
+  uint8_t *wq;
+  uint16_t *sc;
+  uint8_t *zpp;
+  int N, K, NG, KB;
+};
+
+// Host-side launchers (each returns hipGetLastError() of its launch).
+hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p,
+                       int grid_x, int grid_y, hipStream_t s);
+hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
+hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
+hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
+hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
+                         uint8_t *zp, hipStream_t s);
+hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s);
+
+}  // namespace mnb

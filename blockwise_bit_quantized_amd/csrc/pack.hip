@@ -1,0 +1,139 @@
+// pack.hip -- weight packer and unpacker for the 64-row interleaved layout described in
+// common.h, plus the zero-fill used for K == 0.
+//
+// The packer plays the role of the offline "new transposed initializers" of onnxruntime
+// PR #33800 ("Fuse DQ->MatMulNBits for shared initializers and skip outer-scope weights",
+// Description): it reads already-quantized codes, block scales and zero points once and
+// writes the layout the matmul kernels stream.  One thread per (group, block, row).
+#include "common.h"
+
+namespace mnb {
+namespace {
+
+template <int BITS>
+__global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)p.NG * p.KB * kGroup;
+  if (idx >= total) return;
+  const int r = (int)(idx % kGroup);
+  const long tile = idx / kGroup;
+  const int kb = (int)(tile % p.KB);
+  const int g = (int)(tile / p.KB);
+  const int n = g * kGroup + r;
+  const bool ok = n < p.N;
+  u4_t c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
+  if (ok) {
+    const uint8_t *src = p.codes + (size_t)n * p.K + (size_t)kb * kBlock;
+    c0 = *reinterpret_cast<const u4_t *>(src);
+    c1 = *reinterpret_cast<const u4_t *>(src + 16);
+  }
+  auto code = [&](int k) -> uint32_t {  // code k (0..31) of this row-block
+    const u4_t &v = k < 16 ? c0 : c1;
+    const int kk = k & 15;
+    return (v[kk >> 2] >> (8 * (kk & 3))) & 0xffu;
+  };
+  if constexpr (BITS == 4) {
+    u4_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w |= (code(8 * j + 2 * i) & 0xFu) << (4 * i);
+        w |= (code(8 * j + 2 * i + 1) & 0xFu) << (16 + 4 * i);
+      }
+      out[j] = w;
+    }
+    *reinterpret_cast<u4_t *>(p.wq + ((size_t)tile * kGroup + r) * 16) = out;
+  } else {
+    *reinterpret_cast<u4_t *>(p.wq + (((size_t)tile * 2 + 0) * kGroup + r) * 16) = c0;
+    *reinterpret_cast<u4_t *>(p.wq + (((size_t)tile * 2 + 1) * kGroup + r) * 16) = c1;
+  }
+  p.sc[(size_t)tile * kGroup + r] = ok ? p.scales[(size_t)n * p.KB + kb] : (uint16_t)0;
+  if (p.zp) {
+    if constexpr (BITS == 4) {
+      if ((r & 1) == 0) {
+        const uint32_t z0 = ok ? (p.zp[(size_t)n * p.KB + kb] & 0xFu) : 0u;
+        const uint32_t z1 = (n + 1 < p.N) ? (p.zp[(size_t)(n + 1) * p.KB + kb] & 0xFu) : 0u;
+        p.zpp[(size_t)tile * 32 + (r >> 1)] = (uint8_t)(z0 | (z1 << 4));
+      }
+    } else {
+      p.zpp[(size_t)tile * kGroup + r] = ok ? p.zp[(size_t)n * p.KB + kb] : (uint8_t)0;
+    }
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_kernel(PackParams p, uint8_t *codes, uint16_t *scales,
+                                                     uint8_t *zp) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;   // over N * KB
+  if (idx >= (long)p.N * p.KB) return;
+  const int n = (int)(idx / p.KB), kb = (int)(idx % p.KB);
+  const int g = n / kGroup, r = n % kGroup;
+  const size_t tile = (size_t)g * p.KB + kb;
+  u4_t o0, o1;
+  if constexpr (BITS == 4) {
+    const u4_t w = *reinterpret_cast<const u4_t *>(p.wq + (tile * kGroup + r) * 16);
+    uint32_t b[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b[8 * j + 2 * i] = (w[j] >> (4 * i)) & 0xFu;
+        b[8 * j + 2 * i + 1] = (w[j] >> (16 + 4 * i)) & 0xFu;
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o0[q] = b[4 * q] | (b[4 * q + 1] << 8) | (b[4 * q + 2] << 16) | (b[4 * q + 3] << 24);
+      o1[q] = b[16 + 4 * q] | (b[16 + 4 * q + 1] << 8) | (b[16 + 4 * q + 2] << 16) | (b[16 + 4 * q + 3] << 24);
+    }
+  } else {
+    o0 = *reinterpret_cast<const u4_t *>(p.wq + ((tile * 2 + 0) * kGroup + r) * 16);
+    o1 = *reinterpret_cast<const u4_t *>(p.wq + ((tile * 2 + 1) * kGroup + r) * 16);
+  }
+  uint8_t *dst = codes + (size_t)n * p.K + (size_t)kb * kBlock;
+  *reinterpret_cast<u4_t *>(dst) = o0;
+  *reinterpret_cast<u4_t *>(dst + 16) = o1;
+  scales[(size_t)n * p.KB + kb] = p.sc[tile * kGroup + r];
+  if (zp && p.zp) {
+    if constexpr (BITS == 4) zp[(size_t)n * p.KB + kb] = (p.zp[tile * 32 + (r >> 1)] >> (4 * (r & 1))) & 0xFu;
+    else zp[(size_t)n * p.KB + kb] = p.zp[tile * kGroup + r];
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t *Y, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nv = n / 8;
+  if (i < nv) reinterpret_cast<u4_t *>(Y)[i] = u4_t{0u, 0u, 0u, 0u};
+  if (i < n - nv * 8) Y[nv * 8 + i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s) {
+  const long total = (long)p.NG * p.KB * kGroup;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (bits == 4) hipLaunchKernelGGL(pack_kernel<4>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(pack_kernel<8>, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales, uint8_t *zp,
+                         hipStream_t s) {
+  const long total = (long)p.N * p.KB;
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (bits == 4) hipLaunchKernelGGL(unpack_kernel<4>, grid, dim3(256), 0, s, p, codes, scales, zp);
+  else hipLaunchKernelGGL(unpack_kernel<8>, grid, dim3(256), 0, s, p, codes, scales, zp);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long work = n / 8 > 8 ? n / 8 : 8;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, Y, n);
+  return hipGetLastError();
+}
+
+}  // namespace mnb

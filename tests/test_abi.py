@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+ - libmnb.so loads and exports every function include/mnb.h declares;
+ - packed sizes agree with the oracle's independent implementation of the layout;
+ - argument validation returns the documented status before any HIP call (these calls
+   use fake, never-dereferenced pointer values and launch nothing);
+ - the dispatcher's route description follows the automatic rule (M == 1 decode GEMV
+   with in-pass T; M > 1 T projection + MFMA GEMM) and the overrides.
+"""
+from __future__ import annotations
+
+import os
+import re
+
+import pytest
+
+import oracle
+from _util import ROOT, ensure_lib
+
+mnb = ensure_lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mnb.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mnb_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = header_functions()
+    for n in ("mnb_pack", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex", "mnb_workspace_bytes",
+              "mnb_packed_sizes", "mnb_status_string", "mnb_describe_route", "mnb_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    for name in header_functions():
+        assert hasattr(mnb.lib, name), name                      # ctypes dlsym
+        assert callable(getattr(mnb, name)), name                # binding uses the same names
+
+
+def test_version_and_status_strings():
+    assert mnb.mnb_version() == 100
+    for st in range(7):
+        assert mnb.mnb_status_string(st).startswith("MNB_")
+    assert "unknown" in mnb.mnb_status_string(99)
+
+
+@pytest.mark.parametrize("N,K,bits,zp", [(1, 32, 4, 1), (64, 64, 8, 0), (65, 96, 4, 1), (896, 896, 4, 1),
+                                          (8192, 2048, 4, 0), (49152, 576, 8, 1), (9728, 2560, 4, 0)])
+def test_packed_sizes_match_oracle_layout(N, K, bits, zp):
+    st, wq, sc, zpb = mnb.mnb_packed_sizes(N, K, bits, 32, zp)
+    assert st == 0
+    assert (wq, sc, zpb) == oracle.packed_sizes(N, K, bits, zp)
+
+
+def test_packed_sizes_rejects():
+    assert mnb.mnb_packed_sizes(64, 33, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
+    assert mnb.mnb_packed_sizes(64, 64, 3, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
+    assert mnb.mnb_packed_sizes(64, 64, 4, 64, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
+    assert mnb.mnb_packed_sizes(-1, 64, 4, 32, 0)[0] == mnb.MNB_ERR_INVALID_ARG
+
+
+def test_workspace_bytes():
+    assert mnb.mnb_workspace_bytes(0, 64, 64, 4, 32) == 0
+    a = mnb.mnb_workspace_bytes(1, 8192, 2048, 4, 0)
+    b = mnb.mnb_workspace_bytes(1, 8192, 2048, 4, 32)
+    c = mnb.mnb_workspace_bytes(1024, 4096, 4096, 4, 32)
+    assert 0 < a < b and c > b
+    assert a % 256 == 0 and c % 256 == 0
+
+
+# fake device addresses: 16-byte aligned, far apart, never dereferenced by validation
+BASE = 1 << 40
+X, WQ, SC, ZP, Y, WS, A, B = (BASE * (i + 1) for i in range(8))
+
+
+def call(M=1, N=64, K=64, bits=4, block=32, x=X, wq=WQ, sc=SC, zp=ZP, y=Y, ws=WS, ws_bytes=1 << 30, ad=None,
+         opt=None):
+    return mnb.mnb_matmul_ex(x, wq, sc, zp, ad, y, M, N, K, bits, block, ws, ws_bytes, None, opt)
+
+
+def test_validation_status_codes():
+    E = mnb
+    assert call(bits=3) == E.MNB_ERR_UNSUPPORTED
+    assert call(block=64) == E.MNB_ERR_UNSUPPORTED
+    assert call(K=48) == E.MNB_ERR_UNSUPPORTED
+    assert call(M=-1) == E.MNB_ERR_INVALID_ARG
+    assert call(N=-5) == E.MNB_ERR_INVALID_ARG
+    assert call(x=None) == E.MNB_ERR_INVALID_ARG
+    assert call(y=None) == E.MNB_ERR_INVALID_ARG
+    assert call(wq=None) == E.MNB_ERR_INVALID_ARG
+    assert call(x=X + 2) == E.MNB_ERR_MISALIGNED
+    assert call(y=Y + 8) == E.MNB_ERR_MISALIGNED
+    assert call(ws=None) == E.MNB_ERR_WORKSPACE
+    assert call(ws_bytes=16) == E.MNB_ERR_WORKSPACE
+    assert call(y=X) == E.MNB_ERR_ALIAS
+    assert call(y=WS + 4096) == E.MNB_ERR_ALIAS
+    assert call(opt=mnb.mnb_options(7, 0)) == E.MNB_ERR_INVALID_ARG
+    assert call(opt=mnb.mnb_options(0, 8)) == E.MNB_ERR_INVALID_ARG
+    assert call(ad=mnb.mnb_adapter(1, 16, A, None, B, None)) == E.MNB_ERR_UNSUPPORTED
+    assert call(ad=mnb.mnb_adapter(2, 32, A, None, B, None)) == E.MNB_ERR_INVALID_ARG
+    assert call(ad=mnb.mnb_adapter(5, 32, A, None, B, None)) == E.MNB_ERR_INVALID_ARG
+    assert call(ad=mnb.mnb_adapter(1, 32, A + 4, None, B, None)) == E.MNB_ERR_MISALIGNED
+    assert call(y=B, ad=mnb.mnb_adapter(1, 32, A, None, B, None)) == E.MNB_ERR_ALIAS
+
+
+def test_degenerate_sizes_enqueue_nothing():
+    # M == 0 or N == 0 returns before any device call, even with NULL tensors
+    assert call(M=0, x=None, y=None, wq=None, sc=None, ws=None) == 0
+    assert call(N=0, x=None, y=None, wq=None, sc=None, ws=None) == 0
+
+
+def test_pack_validation():
+    P = 1 << 41
+    assert mnb.mnb_pack(P, P * 2, None, 64, 33, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_UNSUPPORTED
+    assert mnb.mnb_pack(P + 1, P * 2, None, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_MISALIGNED
+    assert mnb.mnb_pack(None, P * 2, None, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_INVALID_ARG
+    assert mnb.mnb_pack(P, P * 2, P * 5, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_INVALID_ARG
+    assert mnb.mnb_pack(None, None, None, 0, 64, 4, 32, None, None, None, None) == 0
+    assert mnb.mnb_unpack(P, P, P, 64, 64, 8, 32, P, P, None, None) == mnb.MNB_ERR_INVALID_ARG
+
+
+def route(M, N=4096, K=4096, bits=4, zp=1, kind=1, path=0, flags=0):
+    st, text = mnb.mnb_describe_route(M, N, K, bits, zp, kind, mnb.mnb_options(path, flags))
+    assert st == 0
+    return text
+
+
+def test_dispatcher_rule():
+    assert route(1).startswith("gemv_b4_zpx_f16_inpass")
+    assert route(1, kind=0).startswith("gemv_b4_zpx_none_base")
+    assert route(2).startswith("tproj_f16") and "gemm_b4_zpx_f16" in route(2)
+    assert route(1024, kind=2).startswith("tproj_q8") and "gemm_b4_zpx_q8" in route(1024, kind=2)
+    assert route(8, N=49152, K=576, bits=8, kind=0).startswith("gemm_b8_zpx_none")
+    # overrides, as the pages keep explicit path overrides for comparisons
+    assert route(1, path=2).startswith("tproj_f16") and "gemm" in route(1, path=2)
+    assert route(7, path=1).startswith("tproj_f16") and "gemv_b4_zpx_f16_tprecomp" in route(7, path=1)
+    assert "tprecomp" in route(1, flags=1) and route(1, flags=1).startswith("tproj")
+    assert route(0) == "noop" and route(3, K=0) == "fill_zero"
+
+
+def test_gemv_grid_covers_the_chip():
+    # decode 8192x2048 int4: 128 row groups x K-split fill the 256 CUs, plus T slices
+    t = route(1, N=8192, K=2048, zp=0)
+    grid = int(re.search(r"grid=(\d+)x1", t).group(1))
+    split = int(re.search(r"split=(\d+)", t).group(1))
+    gt = int(re.search(r"gt=(\d+)", t).group(1))
+    assert grid == 128 * split + gt and 128 * split >= 256

@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Bars: packing and indexing bit-exact; exact-arithmetic cases bit-exact; FP16 outputs within
+max-abs 2e-2 and normwise relative 1e-2 of the oracle (FP32 accumulation).  The five
+workloads run at their full sizes in the launch configuration the benchmark times; where
+the oracle would take too long (M = 1024) it checks a seeded sample of rows, all columns.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+from _util import compare, ensure_lib, f16_to_f64, same_bits
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+mnb = ensure_lib()
+DEV = torch.device("cuda:0")
+
+
+# ------------------------------------------------------------------------------------------
+# marshalling
+# ------------------------------------------------------------------------------------------
+
+def t16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.float16)).to(DEV)
+
+
+def tu8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(DEV)
+
+
+def ti8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int8)).to(DEV)
+
+
+def dev_weight(case):
+    zp = tu8(case["zp"]) if case.get("zp") is not None else None
+    return mnb.pack(tu8(case["codes"]), t16(case["scales"]), zp, case["bits"])
+
+
+def dev_adapter(ad):
+    if ad is None:
+        return None
+    if ad["kind"] == "f16":
+        return mnb.Adapter(mnb.MNB_ADAPTER_F16, t16(ad["A"]), t16(ad["B"]), rank=ad.get("rank", 32))
+    return mnb.Adapter(mnb.MNB_ADAPTER_Q8, ti8(ad["A"]), ti8(ad["B"]), t16(ad["A_scales"]), t16(ad["B_scales"]),
+                       rank=ad.get("rank", 32))
+
+
+def run(case, path=0, flags=0, pw=None, ad="case", X=None):
+    pw = pw or dev_weight(case)
+    a = dev_adapter(case.get("adapter")) if ad == "case" else ad
+    Xd = t16(case["X"]) if X is None else X
+    Y = mnb.matmul(Xd, pw, a, path=path, flags=flags)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy().view(np.uint16)
+
+
+def rows_case(case, rows):
+    return dict(case, X=case["X"][rows], M=len(rows))
+
+
+PATHS = [(0, 0, "auto"), (1, 0, "gemv"), (1, 1, "gemv_tsep"), (2, 0, "gemm")]
+
+
+# ------------------------------------------------------------------------------------------
+# packing (bit-exact)
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,K,bits,zp", [(1, 32, 4, True), (64, 64, 4, False), (100, 96, 8, True),
+                                          (130, 160, 4, True), (896, 896, 4, True), (8192, 2048, 4, False),
+                                          (49152, 576, 8, True), (257, 1024, 8, False)])
+def test_pack_matches_oracle_bytes(N, K, bits, zp):
+    case = si.make_random(11, 1, N, K, bits, zp, None)
+    pw = dev_weight(case)
+    torch.cuda.synchronize()
+    wq, sc, zpp = oracle.pack(case["codes"], case["scales"], case["zp"], N, K, bits)
+    assert np.array_equal(pw.wq.cpu().numpy(), wq)
+    assert np.array_equal(pw.sc.cpu().numpy().view(np.uint16), sc)
+    if zp:
+        assert np.array_equal(pw.zp.cpu().numpy(), zpp)
+    codes, scales, z2 = mnb.unpack(pw)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), case["codes"])
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), case["scales"])
+    if zp:
+        assert np.array_equal(z2.cpu().numpy(), case["zp"])
+
+
+def test_pack_is_deterministic():
+    case = si.make_random(12, 1, 300, 256, 4, True, None)
+    a, b = dev_weight(case), dev_weight(case)
+    torch.cuda.synchronize()
+    assert torch.equal(a.wq, b.wq) and torch.equal(a.sc.view(torch.int16), b.sc.view(torch.int16))
+
+
+# ------------------------------------------------------------------------------------------
+# the five workloads at full size
+# ------------------------------------------------------------------------------------------
+
+def test_cfg1_tiny_decode():
+    case = si.make_config(1)
+    compare(run(case), oracle.matmul(case), what="cfg1")
+
+
+@pytest.mark.parametrize("with_adapter", [True, False], ids=["lora", "empty"])
+def test_cfg2_decode(with_adapter):
+    case = si.make_config(2, adapter=with_adapter)
+    ref = oracle.matmul(case)
+    compare(run(case), ref, what="cfg2")
+    if with_adapter:
+        compare(run(case, flags=mnb.MNB_FLAG_T_SEPARATE), ref, what="cfg2 T separate")
+
+
+def test_cfg3_prefill_and_dispatcher_rows():
+    case = si.make_config(3)
+    pw = dev_weight(case)
+    Y = run(case, pw=pw)
+    rng = np.random.default_rng(31)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 1023], rng.choice(1024, 48, replace=False)]))
+    ref = oracle.matmul(rows_case(case, rows))
+    compare(Y[rows], ref, what="cfg3 M=1024 sampled rows")
+    # same weights, M = 256 and M = 1 as prefix rows of X (GEMM and GEMV by the dispatcher)
+    c256 = si.make_config(3, M=256)
+    Y256 = run(c256, pw=pw)
+    r256 = [r for r in rows if r < 256]
+    compare(Y256[r256], ref[[i for i, r in enumerate(rows) if r < 256]], what="cfg3 M=256")
+    c1 = si.make_config(3, M=1)
+    compare(run(c1, pw=pw), ref[:1], what="cfg3 M=1")
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_cfg4_lm_head(M):
+    case = si.make_config(4, M=M)
+    compare(run(case), oracle.matmul(case), what="cfg4 M=%d" % M)
+
+
+def test_cfg5_batched_prefill_q8():
+    case = si.make_config(5)
+    Y = run(case)
+    rng = np.random.default_rng(51)
+    rows = np.unique(np.concatenate([[0, 255, 256, 1023], rng.choice(1024, 40, replace=False)]))
+    ref = oracle.matmul(rows_case(case, rows))
+    compare(Y[rows], ref, what="cfg5 sampled rows")
+    # the zero half of B: those columns equal the base-only output bitwise
+    base = run(case, ad=None)
+    half = case["N"] // 2
+    assert same_bits(Y[:, half:], base[:, half:])
+    assert not same_bits(Y[:, :half], base[:, :half])
+
+
+# ------------------------------------------------------------------------------------------
+# small shapes: every variant, every path, ragged tails
+# ------------------------------------------------------------------------------------------
+
+SHAPES = [(1, 64, 32), (1, 100, 96), (1, 1, 32), (3, 130, 160), (7, 32, 64), (2, 200, 1024), (129, 257, 320),
+          (256, 384, 512), (1, 4096, 4096)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("zp", [True, False], ids=["zp", "zpdef"])
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_small_shapes_all_paths(bits, zp, adapter):
+    for i, (M, N, K) in enumerate(SHAPES):
+        case = si.make_random(40 + i, M, N, K, bits, zp, adapter)
+        ref = oracle.matmul(case)
+        pw = dev_weight(case)
+        for path, flags, name in PATHS:
+            compare(run(case, path, flags, pw=pw), ref, what="%s M=%d N=%d K=%d" % (name, M, N, K))
+
+
+# ------------------------------------------------------------------------------------------
+# bit-exact pins on the GPU
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,zp", [(4, True), (4, False), (8, True), (8, False)])
+def test_one_hot_bit_exact(bits, zp):
+    """X = rows of the identity: each output is one dequantized weight rounded once."""
+    N, K = 200, 256
+    case = si.make_random(60 + bits, K, N, K, bits, zp, None)
+    X = np.eye(K, dtype=np.float16).view(np.uint16)
+    c = dict(case, X=X, M=K)
+    want = oracle.f64_to_f16(oracle.matmul(c))
+    pw = dev_weight(c)
+    for path, flags, name in PATHS:
+        assert same_bits(run(c, path, flags, pw=pw), want), name
+
+
+def exact_case(seed, M, N, K, bits, zp, kind):
+    """Inputs whose every product and partial sum is exact in FP32 (P-e)."""
+    r = np.random.default_rng(seed)
+    X = np.zeros((M, K), np.float16)
+    for m in range(M):
+        ks = r.choice(K, size=min(8, K), replace=False)
+        X[m, ks] = r.choice([-2.0, -1.0, 1.0, 2.0], size=len(ks))
+    z = r.integers(0, 16, size=(N, K // 32)) if bits == 4 else r.integers(100, 157, size=(N, K // 32))
+    zfull = np.repeat(z if zp else np.full_like(z, 2 ** (bits - 1)), 32, axis=1)
+    codes = (np.clip(zfull + r.integers(-15, 16, size=(N, K)), 0, 2 ** bits - 1)).astype(np.uint8)
+    scales = np.full((N, K // 32), 0x3000, np.uint16)                  # 2^-3
+    ad = None
+    if kind == "f16":
+        ad = dict(kind="f16", A=si.to_f16_bits(r.integers(-3, 4, size=(K, 32)) * 0.25),
+                  B=si.to_f16_bits(r.integers(-3, 4, size=(32, N)) * 0.25))
+    elif kind == "q8":
+        ad = dict(kind="q8", A=r.integers(-3, 4, size=(K, 32)).astype(np.int8),
+                  A_scales=np.full((K // 32, 32), 0x3400, np.uint16),       # 2^-2
+                  B=r.integers(-3, 4, size=(32, N)).astype(np.int8),
+                  B_scales=np.full((1, N), 0x3400, np.uint16))
+    return dict(M=M, N=N, K=K, bits=bits, X=X.view(np.uint16), codes=codes, scales=scales,
+                zp=z.astype(np.uint8) if zp else None, adapter=ad)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("kind", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+@pytest.mark.parametrize("M", [1, 5, 130])
+def test_exact_arithmetic_bit_exact(bits, kind, M):
+    case = exact_case(70 + M + bits, M, 192, 320, bits, True, kind)
+    want = oracle.f64_to_f16(oracle.matmul(case))
+    pw = dev_weight(case)
+    for path, flags, name in PATHS:
+        assert same_bits(run(case, path, flags, pw=pw), want), name
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_empty_and_zero_adapter_equal_base_bitwise(M):
+    case = si.make_random(80 + M, M, 320, 512, 4, True, "f16")
+    pw = dev_weight(case)
+    for path, flags, name in PATHS:
+        base = run(case, path, flags, pw=pw, ad=None)
+        ad = case["adapter"]
+        A, B = t16(ad["A"]), t16(ad["B"])
+        zA, zB = torch.zeros_like(A), torch.zeros_like(B)
+        variants = [mnb.Adapter(mnb.MNB_ADAPTER_F16, A, B, rank=0),
+                    mnb.Adapter(mnb.MNB_ADAPTER_NONE, A, B),
+                    mnb.Adapter(mnb.MNB_ADAPTER_F16, None, B),
+                    mnb.Adapter(mnb.MNB_ADAPTER_F16, zA, B),
+                    mnb.Adapter(mnb.MNB_ADAPTER_F16, A, zB)]
+        for v in variants:
+            assert same_bits(run(case, path, flags, pw=pw, ad=v), base), name
+        assert not same_bits(run(case, path, flags, pw=pw), base), name
+
+
+def test_code_equal_zero_point_gives_zero():
+    for bits in (4, 8):
+        case = si.make_random(90 + bits, 3, 130, 256, bits, True, "f16")
+        codes = np.repeat(case["zp"], 32, axis=1).astype(np.uint8)
+        c = dict(case, codes=codes)
+        pw = dev_weight(c)
+        for path, flags, name in PATHS:
+            y = run(c, path, flags, pw=pw, ad=None)
+            assert np.all(f16_to_f64(y) == 0.0), name
+            compare(run(c, path, flags, pw=pw), oracle.matmul(c), what=name)
+
+
+def test_default_zero_point_equals_explicit():
+    for bits in (4, 8):
+        case = si.make_random(95 + bits, 3, 130, 256, bits, False, "q8")
+        explicit = dict(case, zp=np.full(case["scales"].shape, 2 ** (bits - 1), np.uint8))
+        for path, flags, name in PATHS:
+            assert same_bits(run(case, path, flags), run(explicit, path, flags)), name
+
+
+# ------------------------------------------------------------------------------------------
+# degenerate sizes, determinism, workspace reuse
+# ------------------------------------------------------------------------------------------
+
+def test_degenerate_sizes():
+    case = si.make_random(100, 4, 70, 64, 4, True, "f16")
+    pw = dev_weight(case)
+    X = t16(case["X"])
+    sentinel = torch.full((4, 70), 7.0, dtype=torch.float16, device=DEV)
+    ws = mnb.workspace(DEV, 1 << 20)
+    # M == 0: nothing written
+    st = mnb.mnb_matmul(X.data_ptr(), pw.wq.data_ptr(), pw.sc.data_ptr(), pw.zp.data_ptr(), None,
+                        sentinel.data_ptr(), 0, 70, 64, 4, 32, ws.data_ptr(), ws.numel(), 0)
+    torch.cuda.synchronize()
+    assert st == 0 and bool((sentinel == 7.0).all())
+    # K == 0: zeros
+    st = mnb.mnb_matmul(X.data_ptr(), pw.wq.data_ptr(), pw.sc.data_ptr(), None, None,
+                        sentinel.data_ptr(), 4, 70, 0, 4, 32, ws.data_ptr(), ws.numel(), 0)
+    torch.cuda.synchronize()
+    assert st == 0 and bool((sentinel == 0).all())
+
+
+def test_determinism_and_workspace_reuse():
+    shapes = [(1, 8192, 2048, 4, False, "f16"), (1024, 1024, 1024, 4, True, "f16"), (1, 896, 896, 4, True, "q8"),
+              (1, 49152, 576, 8, True, None), (3, 300, 512, 8, False, "f16")]
+    cases = [si.make_random(110 + i, *s) for i, s in enumerate(shapes)]
+    first = [run(c) for c in cases]
+    for _ in range(3):                       # interleaved shapes share one workspace
+        for c, y0 in zip(cases, first):
+            assert np.array_equal(run(c), y0)
+    for c, y0 in zip(cases, first):
+        rows = list(range(c["M"])) if c["M"] <= 8 else [0, 5, c["M"] - 1]
+        compare(y0[rows], oracle.matmul(rows_case(c, rows)), what="reuse %s" % (c["M"],))
