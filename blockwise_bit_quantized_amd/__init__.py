@@ -35,11 +35,31 @@ class mnb_options(C.Structure):
     _fields_ = [("path", C.c_int), ("flags", C.c_int)]
 
 
+def _hip_runtimes() -> set:
+    """Paths of every HIP runtime library mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            return {line.split()[-1] for line in f if "libamdhip64" in line and "/" in line}
+    except OSError:
+        return set()
+
+
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError("libmnb.so is not built (%s); run `python -m blockwise_bit_quantized_amd.build`"
                           % LIB_PATH)
+    # torch ships its own HIP runtime with the same soname as the system one.  Loading torch
+    # first makes libmnb bind to that runtime, so device memory, streams and kernels of both
+    # live in one runtime; loading libmnb first would leave two runtimes in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(LIB_PATH)
+    runtimes = {os.path.realpath(p) for p in _hip_runtimes()}
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s); import torch before loading libmnb"
+                          % ", ".join(sorted(runtimes)))
     P, I, S = C.c_void_p, C.c_int, C.c_size_t
     lib.mnb_packed_sizes.argtypes = [I, I, I, I, I, C.POINTER(S), C.POINTER(S), C.POINTER(S)]
     lib.mnb_pack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]

@@ -19,6 +19,8 @@ ARCH = os.environ.get("MNB_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # code object v5 loads under both the system ROCm runtime and the one torch bundles
+    "-mcode-object-version=5",
     # packed FP32 ops are disabled for every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
@@ -52,7 +54,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     with ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, "--offload-arch=" + ARCH, "-mcode-object-version=5", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
