@@ -10,9 +10,10 @@ Inputs are resident in HBM before timing.  Decode rotates over enough copies of 
 weights and adapter (default >= 1 GiB, four times the 256 MB Infinity Cache) that every
 call streams from HBM; the prefill GEMM is MFMA-bound and uses one copy.
 
-`value` is the decode GEMV's effective HBM bandwidth (algorithmic bytes / mean call time,
-GB/s); the prefill TFLOP/s rides along in `prefill`.  Call times are HIP events recorded on
-the stream the kernels are launched on, around every call in the timed region.
+The timed region replays two captured HIP graphs on one stream: K decode calls, then K
+prefill calls; HIP events bracket each graph.  `value` is the decode GEMV's effective HBM
+bandwidth (algorithmic bytes / mean decode call time, GB/s); the prefill TFLOP/s rides
+along in `prefill`.
 """
 from __future__ import annotations
 
@@ -121,46 +122,61 @@ def main():
         prefill()
     torch.cuda.synchronize()
 
+    # The timed region replays two captured graphs: K decode calls (rotating over the cold
+    # copies) and then K prefill calls.  Graph replay keeps Python launch overhead out of
+    # the measurement; events bracket each graph on the stream the kernels run on.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    cap = torch.cuda.Stream()
+    g_dec, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_dec, stream=cap):
+        for i in range(K):
+            decode(i)
+    with torch.cuda.graph(g_pre, stream=cap):
+        for i in range(K):
+            prefill()
     torch.cuda.synchronize()
+    g_dec.replay()                          # first replay (untimed): graph upload
+    g_pre.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     wall0 = time.perf_counter()
-    t0.record()
-    for i in range(K):
-        e = ev[i]
-        e[0].record()
-        decode(args.warmup + i)
-        e[1].record()
-        e[2].record()
-        prefill()
-        e[3].record()
-    t1.record()
+    with torch.cuda.stream(cap):
+        ev[0].record()
+        g_dec.replay()
+        ev[1].record()
+        g_pre.replay()
+        ev[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = t0.elapsed_time(t1)
-    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    pre_ms = np.array([e[2].elapsed_time(e[3]) for e in ev])
-    dec_s = float(dec_ms.mean()) * 1e-3
-    pre_s = float(pre_ms.mean()) * 1e-3
+    dec_s = ev[0].elapsed_time(ev[1]) * 1e-3 / K
+    pre_s = ev[1].elapsed_time(ev[2]) * 1e-3 / K
+    total_ms = ev[0].elapsed_time(ev[2])
     dec_gbps = dbytes / dec_s / 1e9
     pre_tflops = pflops / pre_s / 1e12
 
-    # warm (Infinity-Cache resident) decode and the two-launch decode variant, for context
-    def timed(fn, n=200):
-        a = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        b = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        for j in range(n):
-            a[j].record()
-            fn(j)
-            b[j].record()
+    # context: warm (Infinity-Cache resident) decode, the two-launch decode variant and the
+    # empty-adapter decode, each as a replayed graph of K calls
+    def graph_time(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for j in range(n):
+                fn(j)
+        g.replay()
         torch.cuda.synchronize()
-        return float(np.mean([x.elapsed_time(y) for x, y in zip(a, b)])) * 1e-3
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(cap):
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / n
 
-    warm_s = timed(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws))
-    tsep_s = timed(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd, ws=ws))
-    base_s = timed(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd, ws=ws))
+    n_ctx = min(K, 100)
+    warm_s = graph_time(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws), n_ctx)
+    tsep_s = graph_time(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd, ws=ws),
+                        n_ctx)
+    base_s = graph_time(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd, ws=ws),
+                        n_ctx)
     dbytes_base = algorithmic_bytes(dM, dN, dK, 4, False, 0)
 
     out = {

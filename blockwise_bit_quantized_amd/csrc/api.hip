@@ -25,69 +25,29 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ---- plan -------------------------------------------------------------------------------
 
-// K-split of the decode GEMV.  Each part holds at least one block per wave (4) and at most
-// 8 per wave (32), and the grid aims to cover the 256 CUs.  Forced GEMV with M > 1 uses
-// one part per group (no partial buffers) and loops over K inside each wave.
-constexpr int kMaxCounters = 4096;  // group / tile counters held in the workspace
+constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 
-void gemv_split(int N, int K, int M, int *split, int *bpp) {
-  const int NG = cdiv(N, kGroup), KB = K / kBlock;
-  if (M != 1 || KB == 0 || NG == 0) {
-    *split = 1;
-    *bpp = std::max(KB, 1);
-    return;
-  }
-  if (NG > kMaxCounters) {
-    *split = 1;
-    *bpp = KB;
-    return;
-  }
-  const int need = cdiv(KB, 32);
-  const int fill = cdiv(kCUs, NG);
-  const int cap = std::max(1, KB / 4);
-  int s = std::max(need, std::min(fill, cap));
-  s = std::max(1, std::min(s, KB));
-  const int b = cdiv(KB, s);
-  *bpp = b;
-  *split = cdiv(KB, b);
-}
-
-constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice
-constexpr int kTprojKP = 512;     // T projection: K per workgroup part
-
-// Workspace: a fixed-size counter area first (its offsets depend on nothing, so a zeroed
+// Workspace: a fixed control area first (its offsets depend on nothing, so a zeroed
 // workspace stays valid for calls of any shape), then data regions that need no init.
 constexpr size_t kCtrlBytes = CTRL_WORDS * sizeof(int);
-constexpr size_t kCntOff = kCtrlBytes;                                  // GEMV group counters
-constexpr size_t kTpCntOff = kCntOff + (size_t)kMaxCounters * sizeof(int);  // T tile counters
-constexpr size_t kDataOff = kTpCntOff + (size_t)kMaxCounters * sizeof(int);
 
 struct WsLayout {
-  size_t ctrl, tpart, tfin, part, cnt, tp_part, tp_cnt, t16, total;
-  int gt, split, bpp, tp_parts, tp_mt;
+  size_t ctrl, tinpass, tproj, total;
+  int gt, q, tparts, tmt;
 };
 
 WsLayout ws_layout(int M, int N, int K, int rank) {
   WsLayout w{};
-  const int NG = cdiv(N, kGroup);
-  gemv_split(N, K, M == 1 ? 1 : M, &w.split, &w.bpp);
+  w.q = gemv_rows_split(N);
   w.gt = cdiv(K, kTSliceRows);
-  w.tp_mt = cdiv(M, 32);
-  w.tp_parts = w.tp_mt > kMaxCounters ? 1 : std::max(1, cdiv(K, kTprojKP));
+  w.tparts = std::max(1, tproj_parts(K));
+  w.tmt = cdiv(M, 32);
+  size_t off = align_up(kCtrlBytes);
   w.ctrl = 0;
-  w.cnt = kCntOff;
-  w.tp_cnt = kTpCntOff;
-  size_t off = align_up(kDataOff);
-  w.tpart = off;
-  if (rank) off += align_up((size_t)w.gt * kRank * sizeof(float));
-  w.tfin = off;
-  if (rank) off += align_up(kRank * sizeof(float));
-  w.part = off;
-  if (M == 1 && w.split > 1) off += align_up((size_t)w.split * NG * kGroup * sizeof(float));
-  w.tp_part = off;
-  if (rank && w.tp_parts > 1) off += align_up((size_t)w.tp_parts * w.tp_mt * 32 * kRank * sizeof(float));
-  w.t16 = off;
-  if (rank) off += align_up((size_t)M * kRank * sizeof(uint16_t));
+  w.tinpass = off;
+  if (rank) off += align_up((size_t)w.gt * kRank * sizeof(unsigned long long));
+  w.tproj = off;
+  if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
   w.total = off;
   return w;
 }
@@ -183,13 +143,13 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   const WsLayout w = ws_layout(M, N, K, r.lora ? kRank : 0);
   const char *ln = r.lora == LORA_NONE ? "none" : (r.lora == LORA_F16 ? "f16" : "q8");
   char tp[96] = "";
-  if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tp_mt * w.tp_parts, w.tp_parts);
+  if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tmt * w.tparts, w.tparts);
   if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
-    snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d split=%d bpp=%d bpw=%d gt=%d", tp, bits,
-             has_zp ? "x" : "def", ln, r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base",
-             NG * w.split + extra, M, w.split, w.bpp, cdiv(w.bpp, 4) <= 4 ? 4 : 8, extra);
+    snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
+             r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * w.q + extra, M, kGroup / w.q, w.q,
+             extra);
   } else {
     snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64", tp, bits, has_zp ? "x" : "def", ln,
              cdiv(M, 128) * cdiv(N, 128));
@@ -314,11 +274,10 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     fprintf(stderr, "[mnb] M=%d N=%d K=%d bits=%d: %s\n", M, N, K, bits, b);
   }
 
-  uint16_t *t16 = lora ? reinterpret_cast<uint16_t *>(ws + w.t16) : nullptr;
+  float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   if (r.tproj) {
-    TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), t16,
-                   reinterpret_cast<float *>(ws + w.tp_part), reinterpret_cast<int *>(ws + w.tp_cnt), M, K,
-                   w.tp_mt, w.tp_parts, kTprojKP};
+    TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), tproj_out,
+                   M, K, w.tmt, w.tparts};
     if (launch_tproj(lora, tp, s) != hipSuccess) return MNB_ERR_HIP;
   }
 
@@ -339,26 +298,25 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     p.K = K;
     p.NG = NG;
     p.KB = KB;
-    p.split = w.split;
-    p.bpp = w.bpp;
+    p.q = w.q;
     p.gt = (lora && r.tmode == 0) ? w.gt : 0;
     p.kt = kTSliceRows;
+    p.nepi = NG * w.q;
+    p.tparts = w.tparts;
+    p.tmpad = M;
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
-    p.tpart = reinterpret_cast<float *>(ws + w.tpart);
-    p.tfin = reinterpret_cast<float *>(ws + w.tfin);
-    p.part = reinterpret_cast<float *>(ws + w.part);
-    p.cnt = reinterpret_cast<int *>(ws + w.cnt);
-    p.t16 = t16;
-    // rows in chunks that respect the grid's y limit
+    p.tin = tproj_out;
+    p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
+    // rows in chunks that respect the grid's y limit (the in-pass T path has M == 1)
     const int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
       const int mc = std::min(kMaxY, M - m0);
       GemvParams q = p;
       q.X = p.X + (size_t)m0 * K;
       q.Y = p.Y + (size_t)m0 * N;
-      if (t16) q.t16 = t16 + (size_t)m0 * kRank;
+      if (tproj_out) q.tin = tproj_out + (size_t)m0 * kRank;
       q.M = mc;
-      const int gx = NG * w.split + p.gt;
+      const int gx = NG * w.q + p.gt;
       if (launch_gemv(bits, has_zp, lora, r.tmode, q, gx, mc, s) != hipSuccess) return MNB_ERR_HIP;
     }
     return MNB_OK;
@@ -373,7 +331,8 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     g.B = ad->B;
     g.sB = static_cast<const uint16_t *>(ad->B_scales);
   }
-  g.t16 = t16;
+  g.tpart = tproj_out;
+  g.tparts = w.tparts;
   g.Y = Yh;
   g.M = M;
   g.N = N;

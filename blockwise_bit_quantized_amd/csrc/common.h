@@ -65,8 +65,10 @@ __device__ __forceinline__ h2_t byte_pair_hi(uint32_t w) {
   return as_h2(__builtin_amdgcn_perm(0x64646464u, w, 0x04030402u));
 }
 
-// Control words at the start of the workspace (counters return to zero after each call).
-enum { CTRL_TCOUNT = 0, CTRL_TFLAG = 1, CTRL_TDONE = 2, CTRL_ERROR = 3, CTRL_WORDS = 64 };
+// Control words at the start of the workspace: the in-pass T call epoch, the counts of
+// epilogues that have read T and of T slices written (both back to zero after each call),
+// and a sticky error word.
+enum { CTRL_EPOCH = 0, CTRL_TDONE = 1, CTRL_ERROR = 2, CTRL_TCOUNT = 3, CTRL_WORDS = 64 };
 
 // Bounded wait for the in-pass T handoff; on expiry the kernel records CTRL_ERROR and
 // uses NaN for T so the failure is visible in Y rather than hanging the device.
@@ -87,26 +89,23 @@ struct GemvParams {
   const uint16_t *sB;
   uint16_t *Y;            // [M, N]
   int M, N, K, NG, KB;
-  int split;              // K-parts per 64-row group (M == 1 only)
-  int bpp;                // blocks per part
-  int gt;                 // in-pass T: number of T slices (first gt workgroups)
+  int q;                  // chunk-columns per wave load; a workgroup owns 64/q rows
+  int gt;                 // in-pass T: number of T-slice workgroups (first in the grid)
   int kt;                 // in-pass T: k rows per slice
+  int nepi;               // in-pass T: number of row workgroups (epilogues)
+  int tparts;             // precomputed T: number of K-part partials
+  int tmpad;              // precomputed T: rows per partial (= M of the T launch)
   int *ctrl;              // control words
-  float *tpart;           // [gt, 32]
-  float *tfin;            // [32]
-  float *part;            // [split, NG*64]
-  int *cnt;               // [NG]
-  const uint16_t *t16;    // precomputed T [M, 32] fp16
+  const float *tin;       // precomputed T partials [tparts, tmpad, 32]
+  unsigned long long *tword;  // in-pass T: [gt, 32] words (FP32 value | call tag << 32)
 };
 
 struct TprojParams {
   const uint16_t *X;
   const void *A;
   const uint16_t *sA;
-  uint16_t *t16;          // [M, 32]
-  float *tpart;           // [parts, MT*32, 32]
-  int *cnt;               // [MT]
-  int M, K, MT, parts, kp;
+  float *tpart;           // [parts, M, 32] FP32 partial sums
+  int M, K, MT, parts;
 };
 
 struct GemmParams {
@@ -116,9 +115,9 @@ struct GemmParams {
   const uint8_t *zp;
   const void *B;
   const uint16_t *sB;
-  const uint16_t *t16;
+  const float *tpart;     // T partials [tparts, M, 32]
   uint16_t *Y;
-  int M, N, K, NG, KB, MT, NT;
+  int M, N, K, NG, KB, MT, NT, tparts;
 };
 
 struct PackParams {
@@ -140,5 +139,9 @@ hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
                          uint8_t *zp, hipStream_t s);
 hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s);
+
+// planning helpers shared by the dispatcher and the launchers
+int gemv_rows_split(int N);                    // q: 1, 2 or 4
+int tproj_parts(int K);                        // K parts of the T projection
 
 }  // namespace mnb

@@ -1,62 +1,139 @@
-// gemv.hip -- decode path of MatMulNBits (M == 1; also any M when forced): one HBM pass
-// over the packed weights with dequantization in registers, FP32 accumulation, and the
-// rank-32 LoRA term fused in the same launch.
+// gemv.hip -- decode path of MatMulNBits (M == 1; any M when forced): one HBM pass over
+// the packed weights with dequantization in registers, FP32 accumulation, and the rank-32
+// LoRA term fused into the same launch.
 //
 // Operation (onnxruntime PR #33370 "[WebGPU] Fuse rank-32 quantized LoRA with
-// MatMulNBits", commit list: decode uses base + T followed by base + T*Bt^T, sharing the
-// decode GEMV reduction; here both steps run in one launch):
+// MatMulNBits", commit list: decode computes base + T and then base + T*Bt^T, sharing the
+// decode GEMV reduction; here both happen in one launch):
 //   y[n] = sum_kb s[n,kb] * sum_{k in kb} x[k] * (q[n,k] - z[n,kb])  +  sum_r t[r] * b[r,n]
 //   t[r] = sum_k x[k] * a[k,r]
 //
-// Work decomposition (gfx950, wave64):
-//  * a workgroup of 4 waves owns one 64-row group and one K-part of `bpp` blocks; lane l
-//    owns row 64g + l, so one 16-byte load per lane streams 1 KiB of contiguous codes and
-//    no cross-lane reduction is needed for the base sum;
-//  * wave w takes blocks kb_beg + w, + 4, ...; all of a wave's loads (codes, scale, zero
-//    point) are issued before any arithmetic so the whole problem is in flight at once;
-//  * X is wave-uniform per block (scalar loads); (q - z) is formed exactly in fp16 and
-//    dotted with X pairs by v_dot2_f32_f16; the block partial is scaled once in FP32;
-//  * the 4 wave partials are summed through LDS in fixed order; with split > 1 the parts
-//    of a group meet in the workspace and the last arriving workgroup (one device-scope
-//    counter per group) adds them in part order, so results do not depend on timing;
-//  * in-pass T: the first `gt` workgroups of the grid compute T over K-slices and publish
-//    partials; the last of them adds the partials in slice order and raises a flag.  The
-//    epilogue of each group waits on that flag (bounded) only after its base sum is done.
-//    Those workgroups are dispatched first and never wait, so the wait always ends.
+// Work decomposition (gfx950, wave64, kWaves waves per workgroup):
+//  * a workgroup owns R = 64/Q rows of one 64-row group over the whole of K, so no partial
+//    sums leave the workgroup.  One wave load of 16 B per lane covers R rows x Q
+//    chunk-columns (Q contiguous segments of R*16 B inside the 1 KiB chunks of the packed
+//    layout); Q is chosen so the grid has enough workgroups to spread over the 256 CUs;
+//  * every wave issues all of its code, scale and zero-point loads first; the X slice the
+//    workgroup needs is staged into LDS meanwhile, so the only memory round trip before
+//    the arithmetic is the weight stream itself;
+//  * (q - z) is formed exactly in fp16 and dotted with X pairs by v_dot2_f32_f16; each
+//    chunk's partial is scaled once in FP32.  The Q lanes that share a row are combined by
+//    lane exchange, the waves through LDS, both in fixed order;
+//  * in-pass T: the first `gt` workgroups of the grid compute T over K-slices of `kt` rows.
+//    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
+//    where the tag identifies this call (a per-call epoch kept in the workspace, never 0).
+//    A slice workgroup then bumps a counter.  Each row workgroup, once its base sum is
+//    done, polls that one word from one lane and then reads the tagged words, accepting
+//    them when every tag matches (no fence on either side: the tags make a stale or early
+//    read detectable, the counter only keeps the polling cheap).  The T workgroups are
+//    dispatched first and never wait, so the bounded wait always ends.  The last epilogue
+//    resets the counters and advances the epoch.
+#include <algorithm>
+
 #include "common.h"
+
+#ifndef MNB_GEMV_WAVES
+#define MNB_GEMV_WAVES 8
+#endif
 
 namespace mnb {
 namespace {
 
 enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
 enum { T_INPASS = 0, T_PRECOMP = 1 };
+constexpr int kWaves = MNB_GEMV_WAVES;
+constexpr int kThreads = kWaves * 64;
+constexpr int kMaxSlicesUnrolled = 16;
+constexpr int kTSliceMax = 256;     // k rows per in-pass T slice (the host passes kt <= this)
 
-// One in-pass T slice: t_j[r] = sum_{k in slice j} x[k] * a[k,r]  (M == 1).
+__device__ __forceinline__ uint32_t call_tag(uint32_t epoch) { return (epoch & 0x7fffffffu) + 1u; }
+
+// sum_{j < n} src[j * stride], in j order.  The first U loads are issued together (from
+// clamped addresses) before any is consumed, so they cost one memory round trip.
+template <int U>
+__device__ __forceinline__ float sum_parts(const float *src, size_t stride, int n) {
+  float v[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) v[j] = src[(size_t)(j < n ? j : 0) * stride];
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < U; ++j)
+    if (j < n) t += v[j];
+  for (int j = U; j < n; ++j) t += src[(size_t)j * stride];
+  return t;
+}
+
+// In-pass T for rank r (lanes 0..31): sum over the gt slices of the tagged words, in slice
+// order; false if some slice of this call has not landed yet.  Lanes 32..63 load nothing.
+__device__ __forceinline__ bool gather_t(const unsigned long long *tw, int gt, uint32_t tag, int lane, float &t) {
+  if (lane >= kRank) {
+    t = 0.f;
+    return true;
+  }
+  unsigned long long v[kMaxSlicesUnrolled];
+#pragma unroll
+  for (int j = 0; j < kMaxSlicesUnrolled; ++j)
+    if (j < gt) v[j] = __hip_atomic_load(tw + (size_t)j * kRank + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool ok = true;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxSlicesUnrolled; ++j)
+    if (j < gt) {
+      ok = ok && (uint32_t)(v[j] >> 32) == tag;
+      s += __builtin_bit_cast(float, (uint32_t)v[j]);
+    }
+  for (int j = kMaxSlicesUnrolled; j < gt; ++j) {
+    const unsigned long long w =
+        __hip_atomic_load(tw + (size_t)j * kRank + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ok = ok && (uint32_t)(w >> 32) == tag;
+    s += __builtin_bit_cast(float, (uint32_t)w);
+  }
+  t = s;
+  return ok;
+}
+
+// One in-pass T slice: words[j][r] = (sum_{k in slice j} x[k] * a[k,r], tag)   (M == 1)
 template <int LORA>
-__device__ void t_slice(const GemvParams &p, int j, float (*tsh)[32]) {
+__device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT));
   const int kbeg = j * p.kt;
   const int kend = min(p.K, kbeg + p.kt);
   const _Float16 *x = reinterpret_cast<const _Float16 *>(p.X);
-  if constexpr (LORA == LORA_F16) {
-    // a wave step covers 16 k-rows of A (1 KiB): lane -> (k = k0 + lane/4, 8 ranks)
+  if (wave >= kWaves) {
+    // the workgroup's extra wave (it exists for the row workgroups) only joins the barrier
+  } else if constexpr (LORA == LORA_F16) {
+    // a wave step covers 16 k-rows of A (1 KiB): lane -> (k = k0 + lane/4, 8 ranks); the
+    // slice's steps are unrolled so every load is in flight before the first FMA
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const int r8 = (lane & 3) * 8;
+    constexpr int kSteps = kTSliceMax / (16 * kWaves);
+    u4_t a[kSteps];
+    _Float16 xv[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int k0 = kbeg + wave * 16 + i * 16 * kWaves;
+      const int k = k0 < kend ? k0 + (lane >> 2) : 0;
+      a[i] = *reinterpret_cast<const u4_t *>(A + (size_t)k * kRank + r8);
+      xv[i] = x[k];
+      if (k0 >= kend) {           // past the slice: contributes exactly nothing
+        a[i] = u4_t{0u, 0u, 0u, 0u};
+        xv[i] = (_Float16)0.f;
+      }
+    }
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int k0 = kbeg + wave * 16; k0 < kend; k0 += 64) {
-      const int k = k0 + (lane >> 2);
-      const u4_t a = *reinterpret_cast<const u4_t *>(A + (size_t)k * kRank + r8);
-      const float xv = (float)x[k];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const h2_t ap = as_h2(a[e]);
-        acc[2 * e] = fmaf(xv, (float)ap[0], acc[2 * e]);
-        acc[2 * e + 1] = fmaf(xv, (float)ap[1], acc[2 * e + 1]);
+        const h2_t ap = as_h2(a[i][e]);
+        acc[2 * e] = fmaf((float)xv[i], (float)ap[0], acc[2 * e]);
+        acc[2 * e + 1] = fmaf((float)xv[i], (float)ap[1], acc[2 * e + 1]);
       }
-    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       acc[e] += __shfl_xor(acc[e], 4);
@@ -72,23 +149,34 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[32]) {
     // INT8 A: a wave step covers 32 k-rows (1 KiB): lane -> (k = k0 + lane/2, 16 ranks)
     const int8_t *A = static_cast<const int8_t *>(p.A);
     const int r16 = (lane & 1) * 16;
+    constexpr int kSteps = kTSliceMax / (32 * kWaves) > 0 ? kTSliceMax / (32 * kWaves) : 1;
+    u4_t a[kSteps], s0[kSteps], s1[kSteps];
+    _Float16 xv[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int k0 = kbeg + wave * 32 + i * 32 * kWaves;
+      const int k = k0 < kend ? k0 + (lane >> 1) : 0;
+      a[i] = *reinterpret_cast<const u4_t *>(A + (size_t)k * kRank + r16);
+      s0[i] = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k / kBlock) * kRank + r16);
+      s1[i] = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k / kBlock) * kRank + r16 + 8);
+      xv[i] = x[k];
+      if (k0 >= kend) {
+        a[i] = u4_t{0u, 0u, 0u, 0u};
+        xv[i] = (_Float16)0.f;
+      }
+    }
     float acc[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    for (int k0 = kbeg + wave * 32; k0 < kend; k0 += 128) {
-      const int k = k0 + (lane >> 1);
-      const u4_t a = *reinterpret_cast<const u4_t *>(A + (size_t)k * kRank + r16);
-      const u4_t s0 = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k / kBlock) * kRank + r16);
-      const u4_t s1 = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k / kBlock) * kRank + r16 + 8);
-      const float xv = (float)x[k];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int8_t v = (int8_t)((a[e >> 2] >> (8 * (e & 3))) & 0xff);
-        const uint32_t sw = (e < 8) ? s0[e >> 1] : s1[(e - 8) >> 1];
-        const float s = (float)as_h2(sw)[e & 1];
-        acc[e] = fmaf(xv, (float)v * s, acc[e]);
+        const int8_t v = (int8_t)((a[i][e >> 2] >> (8 * (e & 3))) & 0xff);
+        const uint32_t sw = (e < 8) ? s0[i][e >> 1] : s1[i][(e - 8) >> 1];
+        const float sc = (float)as_h2(sw)[e & 1];
+        acc[e] = fmaf((float)xv[i], (float)v * sc, acc[e]);
       }
-    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       acc[e] += __shfl_xor(acc[e], 2);
@@ -103,35 +191,34 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[32]) {
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    if (lane < 32) p.tpart[(size_t)j * kRank + lane] = tsh[0][lane] + tsh[1][lane] + tsh[2][lane] + tsh[3][lane];
-    fence_release();
-    int old = 0;
-    if (lane == 0) old = atomic_add_agent(&p.ctrl[CTRL_TCOUNT], 1);
-    old = __shfl(old, 0);
-    if (old == p.gt - 1) {
-      fence_acquire();
-      if (lane < 32) {
-        float t = 0.f;
-        for (int q = 0; q < p.gt; ++q) t += p.tpart[(size_t)q * kRank + lane];
-        p.tfin[lane] = t;
-      }
-      fence_release();
-      if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_TFLAG], 1);
-    }
+  if (wave == 0 && lane < kRank) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += tsh[w][lane];
+    const unsigned long long word = (unsigned long long)__builtin_bit_cast(uint32_t, t) |
+                                    ((unsigned long long)tag << 32);
+    __hip_atomic_store(p.tword + (size_t)j * kRank + lane, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
+  // a hint for the epilogues' single-word poll (correctness rests on the tags)
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(&p.ctrl[CTRL_TCOUNT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BITS, bool HAS_ZP, int LORA, int TMODE, int BPW>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
-  constexpr int C = BITS / 4;                // 16-byte chunks per block and row
-  __shared__ float red[4][kGroup];
-  __shared__ float tsh[4][kRank];
+template <int BITS, bool HAS_ZP, int LORA, int TMODE, int Q, int LPW>
+__global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
+  constexpr int C = BITS / 4;       // 16-byte chunks per block and row
+  constexpr int R = kGroup / Q;     // rows per workgroup
+  constexpr int KPC = 32 / C;       // k values per chunk (32 for 4-bit, 16 for 8-bit)
+  constexpr int XW = LPW * Q * KPC; // halfs of X one wave needs per round
+  constexpr bool kTWave = LORA != LORA_NONE && TMODE == T_INPASS;
+  __shared__ float red[kWaves][kGroup];
+  __shared__ float tsh[kWaves][kRank];
+  __shared__ float tfin[kRank];
+  __shared__ __attribute__((aligned(16))) _Float16 xs[kWaves][XW];   // per-wave X slices
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int bid = blockIdx.x;
-  if constexpr (LORA != LORA_NONE && TMODE == T_INPASS) {
+  if constexpr (kTWave) {
     if (bid < p.gt) {
       t_slice<LORA>(p, bid, tsh);
       return;
@@ -139,166 +226,263 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvParams p) {
     bid -= p.gt;
   }
   const int m = blockIdx.y;
-  const int g = bid / p.split;
-  const int part = bid - g * p.split;
-  const int kb_beg = part * p.bpp;
-  const int kb_end = min(p.KB, kb_beg + p.bpp);
+  const int g = bid / Q;
+  const int rowoff = (bid - g * Q) * R;
+  const int rl = lane % R;              // row within this workgroup
+  const int qi = lane / R;              // chunk-column slot within a wave load
+  const int row = rowoff + rl;          // row within the 64-row group
+  const int n = g * kGroup + row;       // this lane's output column
+  const bool active = wave == 0 && lane < R && n < p.N;
+
+  if constexpr (kTWave) {
+    if (wave == kWaves) {
+      // T wave: carries no weight loads, so its loads return at once.  It waits for the
+      // slice workgroups (one lane polls one word), gathers the tagged words, leaves T in
+      // LDS for the epilogue and reports that it has read T.
+      const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT));
+      int spins = 0;
+      if (lane == 0)
+        while (__hip_atomic_load(&p.ctrl[CTRL_TCOUNT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < p.gt &&
+               spins < kSpinLimit) {
+          ++spins;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      float tv = 0.f;
+      bool ok = false;
+      for (; spins <= kSpinLimit; ++spins) {
+        ok = __all(gather_t(p.tword, p.gt, tag, lane, tv));
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (!ok) {
+        tv = __builtin_nanf("");
+        if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
+      }
+      if (lane < kRank) tfin[lane] = tv;
+      // once every row workgroup has read T, the last one resets the counters and
+      // advances the epoch for the next call
+      if (lane == 0 && __hip_atomic_fetch_add(&p.ctrl[CTRL_TDONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                           p.nepi - 1) {
+        __hip_atomic_store(&p.ctrl[CTRL_TDONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.ctrl[CTRL_TCOUNT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.ctrl[CTRL_EPOCH], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      return;
+    }
+  }
+
+  const int ncc = p.KB * C;             // chunk-columns per row
+  const int nloads = (ncc + Q - 1) / Q; // wave loads per workgroup
   const _Float16 *xrow = reinterpret_cast<const _Float16 *>(p.X) + (size_t)m * p.K;
   const size_t tile0 = (size_t)g * p.KB;
 
-  float acc = 0.f;
-  for (int kb0 = kb_beg + wave; kb0 < kb_end; kb0 += 4 * BPW) {
-    u4_t cw[BPW][C];
-    uint32_t sraw[BPW];
-    uint32_t zraw[BPW];
+  // LoRA: this lane's column of B, loaded with the weight stream (independent of T)
+  uint32_t bpk[kRank / 2];
+  float bscale = 0.f;
+  if constexpr (LORA != LORA_NONE) {
+    if (wave == 0) {
+      const size_t nb = active ? n : 0;
+      if constexpr (LORA == LORA_F16) {
+        const uint16_t *Bp = static_cast<const uint16_t *>(p.B);
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int kb = kb0 + 4 * i;
-      if (kb < kb_end) {
-        const size_t tile = tile0 + kb;
+        for (int r = 0; r < kRank; r += 2)
+          bpk[r / 2] = Bp[(size_t)r * p.N + nb] | ((uint32_t)Bp[(size_t)(r + 1) * p.N + nb] << 16);
+      } else {
+        const uint8_t *Bp = static_cast<const uint8_t *>(p.B);
 #pragma unroll
-        for (int c = 0; c < C; ++c)
-          cw[i][c] = *reinterpret_cast<const u4_t *>(p.wq + ((tile * C + c) * kGroup + lane) * 16);
-        sraw[i] = p.sc[tile * kGroup + lane];
-        if constexpr (HAS_ZP) {
-          if constexpr (BITS == 4) zraw[i] = (p.zp[tile * 32 + (lane >> 1)] >> ((lane & 1) * 4)) & 0xFu;
-          else zraw[i] = p.zp[tile * kGroup + lane];
-        }
+        for (int r = 0; r < kRank; r += 2)
+          bpk[r / 2] = Bp[(size_t)r * p.N + nb] | ((uint32_t)Bp[(size_t)(r + 1) * p.N + nb] << 16);
+        bscale = h2f(p.sB[nb]);
       }
     }
+  }
+
+  float acc = 0.f;
+  // rounds of up to kWaves*LPW wave loads (one round at the decode workloads)
+  for (int l0 = 0; l0 < nloads; l0 += kWaves * LPW) {
+    const int lend = min(nloads, l0 + kWaves * LPW);
+    // 1. weight stream: all of this wave's loads of the round (clamped addresses)
+    u4_t cw[LPW];
+    uint32_t sraw[LPW], zraw[LPW];
 #pragma unroll
-    for (int i = 0; i < BPW; ++i) {
-      const int kb = kb0 + 4 * i;
-      if (kb < kb_end) {
-        const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow + (size_t)kb * kBlock);
-        const uint32_t z = HAS_ZP ? zraw[i] : (1u << (BITS - 1));
-        const _Float16 zz = (_Float16)(float)(1024u + z);      // exact: 1024 + z < 2048
+    for (int i = 0; i < LPW; ++i) {
+      const int l = l0 + wave + kWaves * i;
+      const int cc = l * Q + qi;
+      const bool ok = l < lend && cc < ncc;
+      const int kb = ok ? cc / C : 0;
+      const int c = ok ? cc - kb * C : 0;
+      const size_t tile = tile0 + kb;
+      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + ((tile * C + c) * kGroup + row) * 16);
+      sraw[i] = p.sc[tile * kGroup + row];
+      zraw[i] = 0;
+      if constexpr (HAS_ZP) {
+        if constexpr (BITS == 4) zraw[i] = p.zp[tile * 32 + (row >> 1)];
+        else zraw[i] = p.zp[tile * kGroup + row];
+      }
+    }
+    // 2. this wave's X: slot j = i*Q + qi holds the KPC values of chunk-column
+    //    (l0 + wave + kWaves*i)*Q + qi, loaded 16 B per lane (clamped past the end)
+    constexpr int kPieces = XW / 8;
+#pragma unroll
+    for (int pc = lane; pc < kPieces; pc += 64) {
+      const int j = pc / (KPC / 8), sub = pc % (KPC / 8);
+      const int i = j / Q, q = j % Q;
+      const int cc = (l0 + wave + kWaves * i) * Q + q;
+      const int k = cc < ncc ? cc * KPC + sub * 8 : 0;
+      *reinterpret_cast<u4_t *>(&xs[wave][pc * 8]) = *reinterpret_cast<const u4_t *>(xrow + k);
+    }
+    // 3. arithmetic (xs[wave] is written and read by this wave only: LDS order suffices)
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int l = l0 + wave + kWaves * i;
+      const int cc = l * Q + qi;
+      if (l < lend && cc < ncc) {
+        const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xs[wave][(i * Q + qi) * KPC]);
+        uint32_t z = 1u << (BITS - 1);
+        if constexpr (HAS_ZP) z = BITS == 4 ? (zraw[i] >> ((row & 1) * 4)) & 0xFu : zraw[i];
+        const _Float16 zz = (_Float16)(float)(1024u + z);   // exact: 1024 + z < 2048
         const h2_t zz2 = {zz, zz};
         float p0 = 0.f, p1 = 0.f;
         if constexpr (BITS == 4) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t w = cw[i][0][j];
-            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 0) - zz2, as_h2(xw[4 * j + 0]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 1) - zz2, as_h2(xw[4 * j + 1]), p1, false);
-            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 2) - zz2, as_h2(xw[4 * j + 2]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 3) - zz2, as_h2(xw[4 * j + 3]), p1, false);
+            const u4_t xv = *reinterpret_cast<const u4_t *>(xw + 4 * j);
+            const uint32_t w = cw[i][j];
+            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 0) - zz2, as_h2(xv[0]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 1) - zz2, as_h2(xv[1]), p1, false);
+            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 2) - zz2, as_h2(xv[2]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 3) - zz2, as_h2(xv[3]), p1, false);
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int j = 0; j < 4; j += 2) {
+            const u4_t xv = *reinterpret_cast<const u4_t *>(xw + 2 * j);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t w = cw[i][c][j];
-              p0 = __builtin_amdgcn_fdot2(byte_pair_lo(w) - zz2, as_h2(xw[8 * c + 2 * j]), p0, false);
-              p1 = __builtin_amdgcn_fdot2(byte_pair_hi(w) - zz2, as_h2(xw[8 * c + 2 * j + 1]), p1, false);
+            for (int jj = 0; jj < 2; ++jj) {
+              const uint32_t w = cw[i][j + jj];
+              p0 = __builtin_amdgcn_fdot2(byte_pair_lo(w) - zz2, as_h2(xv[2 * jj]), p0, false);
+              p1 = __builtin_amdgcn_fdot2(byte_pair_hi(w) - zz2, as_h2(xv[2 * jj + 1]), p1, false);
             }
+          }
         }
         acc = fmaf(p0 + p1, h2f((uint16_t)sraw[i]), acc);
       }
     }
   }
-
+  // lanes sharing a row, then waves, in fixed order
+  if constexpr (Q >= 8) acc += __shfl_xor(acc, 8);
+  if constexpr (Q >= 4) acc += __shfl_xor(acc, 16);
+  if constexpr (Q >= 2) acc += __shfl_xor(acc, 32);
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  float total = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
-  const int n = g * kGroup + lane;
-  const size_t npad = (size_t)p.NG * kGroup;
-
-  if (p.split > 1) {
-    p.part[(size_t)part * npad + n] = total;
-    fence_release();
-    int old = 0;
-    if (lane == 0) old = atomic_add_agent(&p.cnt[g], 1);
-    old = __shfl(old, 0);
-    if (old != p.split - 1) return;
-    if (lane == 0) atomic_store_agent(&p.cnt[g], 0);
-    fence_acquire();
-    total = 0.f;
-    for (int q = 0; q < p.split; ++q) total += p.part[(size_t)q * npad + n];
-  }
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += red[w][rl];
 
   float lora = 0.f;
   if constexpr (LORA != LORA_NONE) {
-    // B column of this lane's output (independent of T: issued before any wait)
-    float bcol[kRank];
-    if (n < p.N) {
-#pragma unroll
-      for (int r = 0; r < kRank; ++r) {
-        if constexpr (LORA == LORA_F16) bcol[r] = h2f(static_cast<const uint16_t *>(p.B)[(size_t)r * p.N + n]);
-        else bcol[r] = (float)static_cast<const int8_t *>(p.B)[(size_t)r * p.N + n];
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kRank; ++r) bcol[r] = 0.f;
-    }
     float tv;
     if constexpr (TMODE == T_INPASS) {
-      int spins = 0;
-      bool ok = true;
-      while (atomic_load_agent(&p.ctrl[CTRL_TFLAG]) == 0) {
-        if (++spins > kSpinLimit) { ok = false; break; }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      tv = ok ? p.tfin[lane & 31] : __builtin_nanf("");
-      if (!ok && lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
-      int done = 0;
-      if (lane == 0) done = atomic_add_agent(&p.ctrl[CTRL_TDONE], 1);
-      done = __shfl(done, 0);
-      if (done == p.NG - 1 && lane == 0) {      // every epilogue has read T: reset
-        atomic_store_agent(&p.ctrl[CTRL_TFLAG], 0);
-        atomic_store_agent(&p.ctrl[CTRL_TCOUNT], 0);
-        atomic_store_agent(&p.ctrl[CTRL_TDONE], 0);
-      }
+      tv = tfin[lane & 31];
     } else {
-      tv = h2f(p.t16[(size_t)m * kRank + (lane & 31)]);
+      // T from the T-projection launch: FP32 partials per K-part, added in part order
+      tv = sum_parts<4>(p.tin + (size_t)m * kRank + (lane & 31), (size_t)p.tmpad * kRank, p.tparts);
     }
 #pragma unroll
     for (int r = 0; r < kRank; ++r) {
       const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
-      lora = fmaf(tr, bcol[r], lora);
+      float b;
+      if constexpr (LORA == LORA_F16) b = (float)__builtin_bit_cast(_Float16, (uint16_t)(bpk[r / 2] >> (16 * (r & 1))));
+      else b = (float)(int8_t)((bpk[r / 2] >> (16 * (r & 1))) & 0xff);
+      lora = fmaf(tr, b, lora);
     }
-    if constexpr (LORA == LORA_Q8) lora *= (n < p.N) ? h2f(p.sB[n]) : 0.f;
+    if constexpr (LORA == LORA_Q8) lora *= bscale;
   }
-  if (n < p.N) {
+  if (active) {
     const _Float16 y = (_Float16)(total + lora);
     p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, y);
   }
 }
 
-template <int BITS, bool HAS_ZP, int LORA, int TMODE>
-hipError_t launch4(const GemvParams &p, int bpw, int gx, int gy, hipStream_t s) {
-  if (bpw <= 4)
-    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, 4>), dim3(gx, gy), dim3(256), 0, s, p);
+template <int BITS, bool HAS_ZP, int LORA, int TMODE, int Q>
+hipError_t launch5(const GemvParams &p, int lpw, int gx, int gy, size_t lds, hipStream_t s) {
+  (void)lds;
+  const int nt = kThreads + ((LORA != LORA_NONE && TMODE == T_INPASS) ? 64 : 0);
+  if (lpw <= 2)
+    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 2>), dim3(gx, gy), dim3(nt), 0, s, p);
+  else if (lpw <= 4)
+    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 4>), dim3(gx, gy), dim3(nt), 0, s, p);
   else
-    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, 8>), dim3(gx, gy), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 8>), dim3(gx, gy), dim3(nt), 0, s, p);
   return hipGetLastError();
 }
 
-template <int BITS, bool HAS_ZP>
-hipError_t launch3(int lora, int tmode, const GemvParams &p, int bpw, int gx, int gy, hipStream_t s) {
-  switch (lora) {
-    case LORA_NONE: return launch4<BITS, HAS_ZP, LORA_NONE, T_PRECOMP>(p, bpw, gx, gy, s);
-    case LORA_F16:
-      return tmode == T_INPASS ? launch4<BITS, HAS_ZP, LORA_F16, T_INPASS>(p, bpw, gx, gy, s)
-                               : launch4<BITS, HAS_ZP, LORA_F16, T_PRECOMP>(p, bpw, gx, gy, s);
-    default:
-      return tmode == T_INPASS ? launch4<BITS, HAS_ZP, LORA_Q8, T_INPASS>(p, bpw, gx, gy, s)
-                               : launch4<BITS, HAS_ZP, LORA_Q8, T_PRECOMP>(p, bpw, gx, gy, s);
+template <int BITS, bool HAS_ZP, int LORA, int TMODE>
+hipError_t launch4(const GemvParams &p, int lpw, int gx, int gy, size_t lds, hipStream_t s) {
+  switch (p.q) {
+    case 1: return launch5<BITS, HAS_ZP, LORA, TMODE, 1>(p, lpw, gx, gy, lds, s);
+    case 2: return launch5<BITS, HAS_ZP, LORA, TMODE, 2>(p, lpw, gx, gy, lds, s);
+    case 4: return launch5<BITS, HAS_ZP, LORA, TMODE, 4>(p, lpw, gx, gy, lds, s);
+    default: return launch5<BITS, HAS_ZP, LORA, TMODE, 8>(p, lpw, gx, gy, lds, s);
   }
+}
+
+template <int BITS, bool HAS_ZP>
+hipError_t launch3(int lora, int tmode, const GemvParams &p, int lpw, int gx, int gy, size_t lds, hipStream_t s) {
+  switch (lora) {
+    case LORA_NONE: return launch4<BITS, HAS_ZP, LORA_NONE, T_PRECOMP>(p, lpw, gx, gy, lds, s);
+    case LORA_F16:
+      return tmode == T_INPASS ? launch4<BITS, HAS_ZP, LORA_F16, T_INPASS>(p, lpw, gx, gy, lds, s)
+                               : launch4<BITS, HAS_ZP, LORA_F16, T_PRECOMP>(p, lpw, gx, gy, lds, s);
+    default:
+      return tmode == T_INPASS ? launch4<BITS, HAS_ZP, LORA_Q8, T_INPASS>(p, lpw, gx, gy, lds, s)
+                               : launch4<BITS, HAS_ZP, LORA_Q8, T_PRECOMP>(p, lpw, gx, gy, lds, s);
+  }
+}
+
+int loads_per_wave(int K, int bits, int q) {
+  const int ncc = (K / kBlock) * (bits / 4);
+  const int nloads = (ncc + q - 1) / q;
+  const int lpw = (nloads + kWaves - 1) / kWaves;
+  return lpw <= 2 ? 2 : (lpw <= 4 ? 4 : 8);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p,
-                       int grid_x, int grid_y, hipStream_t s) {
-  const int bpw = (p.bpp + 3) / 4;
+#ifndef MNB_GEMV_MIN_WG
+#define MNB_GEMV_MIN_WG 512
+#endif
+
+// rows per workgroup = 64 / q: the smallest q in {1, 2, 4, 8} that gives at least
+// MNB_GEMV_MIN_WG row workgroups
+int gemv_rows_split(int N) {
+  const int NG = (N + kGroup - 1) / kGroup;
+  int q = 1;
+  while (q < 8 && NG * q < MNB_GEMV_MIN_WG) q *= 2;
+  return q;
+}
+
+size_t gemv_lds_bytes(int K, int bits, int q) {
+  const int lpw = loads_per_wave(K, bits, q);
+  const int ncc = (K / kBlock) * (bits / 4);
+  const int nloads = (ncc + q - 1) / q;
+  const int per_round = std::min(nloads, kWaves * lpw);
+  const int kpc = 32 / (bits / 4);
+  return (size_t)per_round * q * kpc * sizeof(uint16_t);
+}
+
+hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p, int grid_x, int grid_y,
+                       hipStream_t s) {
+  const int lpw = loads_per_wave(p.K, bits, p.q);
+  const size_t lds = gemv_lds_bytes(p.K, bits, p.q);
   if (bits == 4)
-    return has_zp ? launch3<4, true>(lora, tmode, p, bpw, grid_x, grid_y, s)
-                  : launch3<4, false>(lora, tmode, p, bpw, grid_x, grid_y, s);
-  return has_zp ? launch3<8, true>(lora, tmode, p, bpw, grid_x, grid_y, s)
-                : launch3<8, false>(lora, tmode, p, bpw, grid_x, grid_y, s);
+    return has_zp ? launch3<4, true>(lora, tmode, p, lpw, grid_x, grid_y, lds, s)
+                  : launch3<4, false>(lora, tmode, p, lpw, grid_x, grid_y, lds, s);
+  return has_zp ? launch3<8, true>(lora, tmode, p, lpw, grid_x, grid_y, lds, s)
+                : launch3<8, false>(lora, tmode, p, lpw, grid_x, grid_y, lds, s);
 }
 
 }  // namespace mnb

@@ -1,107 +1,146 @@
-// tproj.hip -- LoRA down-projection T[M, 32] = X[M, K] . A[K, 32] for the prefill path
-// (and for decode when T is computed in its own launch).  T is stored in fp16, rounded
-// once from FP32 accumulation, and is read by the GEMM epilogue as an MFMA operand.
+// tproj.hip -- LoRA down-projection T = X[M, K] . A[K, 32] for the prefill path (and for
+// decode when T runs in its own launch).  The output is FP32 partial sums per K-part,
+// tpart[part][m][r]; the consumer (GEMM or GEMV epilogue) adds the parts in part order.
 //
 // onnxruntime PR #33370 ("[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits"), commit
 // list: fuse_up computes T first, then the base GEMM with an integrated T*Bt^T epilogue;
-// a later commit keeps a "K-parallel narrow-N" path for this projection.  Here: the output
-// is only 32 wide, so the grid is (32-row M tiles) x (K parts of 512); each wave runs
-// v_mfma_f32_32x32x16_f16 over 128 k; the four waves meet in LDS and the K parts meet in
-// the workspace, where the last arriving workgroup of an M tile adds them in part order.
+// a later commit keeps a "K-parallel narrow-N" path for this projection.  Here the output
+// is only 32 wide, so the grid is (32-row M tiles) x (K parts of kp).  Per workgroup:
+//  * the A-part [kp, 32] is read once with 16-byte loads and written transposed into LDS
+//    (8x8 half tiles transposed in registers, one ds_write_b128 per rank row), so the
+//    MFMA B operand (8 consecutive k of one rank) is a single ds_read_b128;
+//  * each wave owns kp/4 consecutive k and issues all of its X loads (MFMA A operand,
+//    8 consecutive k of one row per lane) before waiting on anything;
+//  * v_mfma_f32_32x32x16_f16 per 16 k; the four waves meet in LDS in fixed order.
+// No counters and no cross-workgroup waits.
 #include "common.h"
 
 namespace mnb {
 namespace {
 
+constexpr int kKP = 1024;             // K per part
+constexpr int kStepsPerWave = kKP / 4 / 16;
+constexpr int kLdA = kKP + 8;         // halfs per transposed A row (pad keeps lanes on distinct banks)
+
 template <int KIND>  // 1: F16 A, 2: INT8 A with block-32 fp16 scales
 __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
-  __shared__ float red[4][kRank * kRank];
-  __shared__ int last_sh;
+  __shared__ __attribute__((aligned(16))) _Float16 sAT[kRank * kLdA];   // 66 KB
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int mt = blockIdx.x / p.parts;
   const int part = blockIdx.x - mt * p.parts;
-  const int kbeg = part * p.kp;
-  const int kend = min(p.K, kbeg + p.kp);
+  const int kbeg = part * kKP;
+  const int kend = min(p.K, kbeg + kKP);
   const int mrow = mt * 32 + (lane & 31);
-  const int hk = 8 * (lane >> 5);            // this lane's 8 k within a 16-k step
-  const int r = lane & 31;
+  const bool mok = mrow < p.M;
+  const int hk = 8 * (lane >> 5);
+
+  // X operand loads for this wave's k range (all issued first)
+  const int kw = kbeg + wave * (kKP / 4);
+  const _Float16 *xr = reinterpret_cast<const _Float16 *>(p.X) + (size_t)(mok ? mrow : 0) * p.K;
+  h8_t xa[kStepsPerWave];
+#pragma unroll
+  for (int s = 0; s < kStepsPerWave; ++s) {
+    const int k = kw + 16 * s + hk;
+    xa[s] = *reinterpret_cast<const h8_t *>(xr + (k < kend ? k : 0));
+  }
+
+  // A part -> LDS transposed: thread handles 8x8 tiles (k octet, r octet)
+  constexpr int kTiles = kKP / 8 * 4;
+#pragma unroll
+  for (int t = tid; t < kTiles; t += 256) {
+    const int ko = t >> 2, ro = t & 3;
+    const int k0 = kbeg + ko * 8;
+    uint32_t v[8][4];   // v[row e][dword d] = halves (r = 2d, 2d+1) of A[k0+e][8*ro ..]
+    if (k0 < kend) {
+      if constexpr (KIND == 1) {
+        const uint16_t *A = static_cast<const uint16_t *>(p.A);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const u4_t a = *reinterpret_cast<const u4_t *>(A + (size_t)(k0 + e) * kRank + ro * 8);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) v[e][d] = a[d];
+        }
+      } else {
+        const int8_t *A = static_cast<const int8_t *>(p.A);
+        const u4_t sv = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k0 / kBlock) * kRank + ro * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint2 a = *reinterpret_cast<const uint2 *>(A + (size_t)(k0 + e) * kRank + ro * 8);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t bytes = d < 2 ? a.x : a.y;
+            const int8_t lo = (int8_t)((bytes >> (16 * (d & 1))) & 0xff);
+            const int8_t hi = (int8_t)((bytes >> (16 * (d & 1) + 8)) & 0xff);
+            const h2_t s2 = as_h2(sv[d]);
+            const h2_t q = {(_Float16)((float)lo * (float)s2[0]), (_Float16)((float)hi * (float)s2[1])};
+            v[e][d] = as_u32(q);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) v[e][d] = 0u;
+    }
+    // transpose: rank row rr = 2d + h gets k = e (8 halves) -> one 16-byte store
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u4_t o;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const uint32_t lo = (v[2 * e2][d] >> (16 * h)) & 0xffffu;
+          const uint32_t hi = (v[2 * e2 + 1][d] >> (16 * h)) & 0xffffu;
+          o[e2] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u4_t *>(&sAT[(ro * 8 + 2 * d + h) * kLdA + ko * 8]) = o;
+      }
+  }
+  __syncthreads();
 
   f16x_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-  for (int kk = kbeg + wave * 16; kk < kend; kk += 64) {
-    const int k = kk + hk;
-    h8_t a, b;
-    if (mrow < p.M) {
-      a = *reinterpret_cast<const h8_t *>(reinterpret_cast<const _Float16 *>(p.X) + (size_t)mrow * p.K + k);
-    } else {
+  const int r = lane & 31;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a[e] = (_Float16)0.f;
+  for (int s = 0; s < kStepsPerWave; ++s) {
+    const int k = kw + 16 * s;
+    if (k < kend) {
+      const h8_t b = *reinterpret_cast<const h8_t *>(&sAT[r * kLdA + (k - kbeg) + hk]);
+      h8_t a = xa[s];
+      if (!mok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (_Float16)0.f;
+      }
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
     }
-    if constexpr (KIND == 1) {
-      const _Float16 *A = static_cast<const _Float16 *>(p.A);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = A[(size_t)(k + e) * kRank + r];
-    } else {
-      const int8_t *A = static_cast<const int8_t *>(p.A);
-      const float s = h2f(p.sA[(size_t)(k / kBlock) * kRank + r]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = (_Float16)((float)A[(size_t)(k + e) * kRank + r] * s);
-    }
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
   }
+  __syncthreads();   // sAT no longer needed: reuse it for the cross-wave sum
+  float *red = reinterpret_cast<float *>(sAT);   // [4][32*32]
   // accumulator layout of a 32x32 MFMA tile: column = lane % 32,
   // row = 8*(v/4) + 4*(lane/32) + v%4 for register v
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-    red[wave][i * kRank + r] = acc[v];
+    red[wave * 1024 + i * kRank + r] = acc[v];
   }
   __syncthreads();
-  float sum[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid + 256 * q;
-    sum[q] = red[0][e] + red[1][e] + red[2][e] + red[3][e];
-  }
-  if (p.parts == 1) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid + 256 * q;
-      const int m = mt * 32 + e / kRank;
-      if (m < p.M) p.t16[(size_t)m * kRank + (e % kRank)] = __builtin_bit_cast(uint16_t, (_Float16)sum[q]);
-    }
-    return;
-  }
-  const size_t mpad = (size_t)p.MT * 32;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + 256 * q;
-    p.tpart[((size_t)part * mpad + mt * 32) * kRank + e] = sum[q];
-  }
-  fence_release();
-  __syncthreads();
-  if (tid == 0) {
-    const int old = atomic_add_agent(&p.cnt[mt], 1);
-    last_sh = (old == p.parts - 1);
-    if (last_sh) atomic_store_agent(&p.cnt[mt], 0);
-  }
-  __syncthreads();
-  if (!last_sh) return;
-  fence_acquire();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + 256 * q;
-    float t = 0.f;
-    for (int pp = 0; pp < p.parts; ++pp) t += p.tpart[((size_t)pp * mpad + mt * 32) * kRank + e];
+    const float sum = red[e] + red[1024 + e] + red[2048 + e] + red[3072 + e];
     const int m = mt * 32 + e / kRank;
-    if (m < p.M) p.t16[(size_t)m * kRank + (e % kRank)] = __builtin_bit_cast(uint16_t, (_Float16)t);
+    if (m < p.M) p.tpart[((size_t)part * p.M + m) * kRank + (e % kRank)] = sum;
   }
 }
 
 }  // namespace
+
+int tproj_parts(int K) { return (K + kKP - 1) / kKP; }
 
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s) {
   const int grid = p.MT * p.parts;
