@@ -59,8 +59,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see the sharding paragraph of the design notes); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(how the path would shard is described in the design notes); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -68,7 +69,11 @@ def main():
 
     lib_path = os.path.join(ROOT, "blockwise_bit_quantized_amd", "libmnb.so")
     if not os.path.exists(lib_path):
-        from blockwise_bit_quantized_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_mnb_build", os.path.join(ROOT, "blockwise_bit_quantized_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     import blockwise_bit_quantized_amd as mnb
     import seeded_inputs as si

@@ -46,7 +46,7 @@ def _hip_runtimes() -> set:
 
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError("libmnb.so is not built (%s); run `python -m blockwise_bit_quantized_amd.build`"
+        raise ImportError("libmnb.so is not built (%s); run `python blockwise_bit_quantized_amd/build.py`"
                           % LIB_PATH)
     # torch ships its own HIP runtime with the same soname as the system one.  Loading torch
     # first makes libmnb bind to that runtime, so device memory, streams and kernels of both

@@ -1,6 +1,8 @@
 """Build libmnb.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m blockwise_bit_quantized_amd.build
+    python blockwise_bit_quantized_amd/build.py
+
+(run by path: importing the package loads the library this script builds)
 """
 from __future__ import annotations
 
@@ -60,8 +62,21 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    _check_undefined(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_undefined(path: str) -> None:
+    """A kernel whose host-side launch stub was not emitted links fine but cannot be
+    loaded; refuse such a library here instead of at import time."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", path], capture_output=True, text=True)
+    if r.returncode != 0:
+        return                                   # nm unavailable: the loader still checks
+    bad = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3mnb" in l]
+    if bad:
+        os.remove(path)
+        raise RuntimeError("libmnb links against undefined symbols of its own: " + ", ".join(bad[:4]))
 
 
 if __name__ == "__main__":

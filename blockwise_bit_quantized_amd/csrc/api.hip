@@ -27,12 +27,11 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 
-// Workspace: a fixed control area first (its offsets depend on nothing, so a zeroed
-// workspace stays valid for calls of any shape), then data regions that need no init.
-constexpr size_t kCtrlBytes = CTRL_WORDS * sizeof(int);
-
+// Workspace: a fixed control area and the final-T replicas first (their offsets depend
+// on nothing, so a zeroed workspace stays valid for calls of any shape), then data
+// regions that need no initialisation.
 struct WsLayout {
-  size_t ctrl, tinpass, tproj, total;
+  size_t ctrl, tfinal, tinpass, tproj, total;
   int gt, q, tparts, tmt;
 };
 
@@ -44,6 +43,8 @@ WsLayout ws_layout(int M, int N, int K, int rank) {
   w.tmt = cdiv(M, 32);
   size_t off = align_up(kCtrlBytes);
   w.ctrl = 0;
+  w.tfinal = off;
+  off += align_up(kTFinalBytes);
   w.tinpass = off;
   if (rank) off += align_up((size_t)w.gt * kRank * sizeof(unsigned long long));
   w.tproj = off;
@@ -307,6 +308,7 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
     p.tin = tproj_out;
     p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
+    p.tfinal = reinterpret_cast<unsigned long long *>(ws + w.tfinal);
     // rows in chunks that respect the grid's y limit (the in-pass T path has M == 1)
     const int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {

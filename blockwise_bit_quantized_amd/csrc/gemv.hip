@@ -22,12 +22,14 @@
 //  * in-pass T: the first `gt` workgroups of the grid compute T over K-slices of `kt` rows.
 //    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
 //    where the tag identifies this call (a per-call epoch kept in the workspace, never 0).
-//    A slice workgroup then bumps a counter.  Each row workgroup, once its base sum is
-//    done, polls that one word from one lane and then reads the tagged words, accepting
-//    them when every tag matches (no fence on either side: the tags make a stale or early
-//    read detectable, the counter only keeps the polling cheap).  The T workgroups are
-//    dispatched first and never wait, so the bounded wait always ends.  The last epilogue
-//    resets the counters and advances the epoch.
+//    The slice workgroup that counts itself last adds the slices in slice order and writes
+//    the final T, tagged the same way, into kTReplicas copies.  Each row workgroup has one
+//    extra wave that carries no weight loads: it polls one word of its copy, reads the 32
+//    words, accepts them when every tag matches (no fences: the tags make a stale or early
+//    read detectable) and leaves T in LDS for the epilogue.  The slice workgroups are
+//    dispatched first and wait only for each other, so every bounded wait ends.  Row
+//    workgroups report that they have read T through a two-level count (kDoneGroups
+//    counters, then one); the last one resets the counts and advances the epoch.
 #include <algorithm>
 
 #include "common.h"
@@ -47,6 +49,9 @@ constexpr int kMaxSlicesUnrolled = 16;
 constexpr int kTSliceMax = 256;     // k rows per in-pass T slice (the host passes kt <= this)
 
 __device__ __forceinline__ uint32_t call_tag(uint32_t epoch) { return (epoch & 0x7fffffffu) + 1u; }
+__device__ __forceinline__ unsigned long long tagged(float v, uint32_t tag) {
+  return (unsigned long long)__builtin_bit_cast(uint32_t, v) | ((unsigned long long)tag << 32);
+}
 
 // sum_{j < n} src[j * stride], in j order.  The first U loads are issued together (from
 // clamped addresses) before any is consumed, so they cost one memory round trip.
@@ -191,16 +196,38 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
     }
   }
   __syncthreads();
-  if (wave == 0 && lane < kRank) {
-    float t = 0.f;
+  if (wave == 0) {
+    if (lane < kRank) {
+      float t = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) t += tsh[w][lane];
-    const unsigned long long word = (unsigned long long)__builtin_bit_cast(uint32_t, t) |
-                                    ((unsigned long long)tag << 32);
-    __hip_atomic_store(p.tword + (size_t)j * kRank + lane, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int w = 0; w < kWaves; ++w) t += tsh[w][lane];
+      __hip_atomic_store(p.tword + (size_t)j * kRank + lane, tagged(t, tag), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the slice workgroup that counts itself last publishes the final T
+    int last = 0;
+    if (lane == 0)
+      last = __hip_atomic_fetch_add(&p.ctrl[CTRL_TCOUNT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.gt - 1;
+    if (__builtin_amdgcn_readfirstlane(last)) {
+      float tv = 0.f;
+      bool ok = false;
+      for (int spins = 0; spins <= kSpinLimit && !ok; ++spins) {
+        ok = __all(gather_t(p.tword, p.gt, tag, lane, tv));
+        if (!ok) __builtin_amdgcn_s_sleep(1);
+      }
+      if (!ok) {
+        tv = __builtin_nanf("");
+        if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
+      }
+      if (lane < kRank) {
+        const unsigned long long word = tagged(tv, tag);
+#pragma unroll
+        for (int c = 0; c < kTReplicas; ++c)
+          __hip_atomic_store(p.tfinal + c * kRank + lane, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (lane == 0) __hip_atomic_store(&p.ctrl[CTRL_TCOUNT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
-  // a hint for the epilogues' single-word poll (correctness rests on the tags)
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(&p.ctrl[CTRL_TCOUNT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int BITS, bool HAS_ZP, int LORA, int TMODE, int Q, int LPW>
@@ -236,37 +263,49 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
 
   if constexpr (kTWave) {
     if (wave == kWaves) {
-      // T wave: carries no weight loads, so its loads return at once.  It waits for the
-      // slice workgroups (one lane polls one word), gathers the tagged words, leaves T in
-      // LDS for the epilogue and reports that it has read T.
+      // T wave: carries no weight loads, so its loads return at once.  It polls one word
+      // of its replica of the final T, reads the 32 tagged words, leaves T in LDS for the
+      // epilogue and reports that it has read T.
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
+      const unsigned long long *rep = p.tfinal + (bid % kTReplicas) * kRank;
       int spins = 0;
       if (lane == 0)
-        while (__hip_atomic_load(&p.ctrl[CTRL_TCOUNT], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < p.gt &&
+        while ((uint32_t)(__hip_atomic_load(rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != tag &&
                spins < kSpinLimit) {
           ++spins;
           __builtin_amdgcn_s_sleep(2);
         }
+      spins = __builtin_amdgcn_readfirstlane(spins);   // lane 0's count: the loop below is uniform
       float tv = 0.f;
       bool ok = false;
-      for (; spins <= kSpinLimit; ++spins) {
-        ok = __all(gather_t(p.tword, p.gt, tag, lane, tv));
-        if (ok) break;
-        __builtin_amdgcn_s_sleep(2);
+      for (; spins <= kSpinLimit && !ok; ++spins) {
+        const unsigned long long w =
+            lane < kRank ? __hip_atomic_load(rep + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        tv = __builtin_bit_cast(float, (uint32_t)w);
+        ok = __all(lane >= kRank || (uint32_t)(w >> 32) == tag);
+        if (!ok) __builtin_amdgcn_s_sleep(1);
       }
       if (!ok) {
         tv = __builtin_nanf("");
         if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
       }
       if (lane < kRank) tfin[lane] = tv;
-      // once every row workgroup has read T, the last one resets the counters and
-      // advances the epoch for the next call
-      if (lane == 0 && __hip_atomic_fetch_add(&p.ctrl[CTRL_TDONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                           p.nepi - 1) {
-        __hip_atomic_store(&p.ctrl[CTRL_TDONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ctrl[CTRL_TCOUNT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.ctrl[CTRL_EPOCH], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // two-level count of the row workgroups that have read T; the last one resets the
+      // counts and advances the epoch for the next call
+      if (lane == 0) {
+        const int grp = bid % kDoneGroups;
+        const int members = (p.nepi - grp + kDoneGroups - 1) / kDoneGroups;
+        const int groups = min(kDoneGroups, p.nepi);
+        int *cnt = &p.ctrl[ctrl_done_word(grp)];
+        if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
+          __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (__hip_atomic_fetch_add(&p.ctrl[CTRL_TDONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              groups - 1) {
+            __hip_atomic_store(&p.ctrl[CTRL_TDONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&p.ctrl[CTRL_EPOCH], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
       __syncthreads();
       return;

@@ -16,7 +16,11 @@ def ensure_lib():
     """Import the binding, building libmnb.so first only if it is absent."""
     path = os.path.join(ROOT, "blockwise_bit_quantized_amd", "libmnb.so")
     if not os.path.exists(path):
-        from blockwise_bit_quantized_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_mnb_build", os.path.join(ROOT, "blockwise_bit_quantized_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     import blockwise_bit_quantized_amd as mnb
     return mnb
