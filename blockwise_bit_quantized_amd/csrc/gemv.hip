@@ -253,8 +253,17 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
     bid -= p.gt;
   }
   const int m = blockIdx.y;
-  const int g = bid / Q;
-  const int rowoff = (bid - g * Q) * R;
+  // The Q workgroups of one 64-row group read disjoint 128/Q-byte pieces of the same
+  // 128-byte scale lines (and zero-point and B lines).  Workgroups are dealt to the 8 XCDs by id modulo 8,
+  // so give the Q siblings ids 8 apart: they then share one XCD and its L2 fetches each
+  // line once instead of Q times.
+  int wgi = bid;
+  if (Q > 1 && (p.NG & 7) == 0) {
+    const int x = bid & 7, u = bid >> 3;
+    wgi = (x + 8 * (u / Q)) * Q + (u % Q);
+  }
+  const int g = wgi / Q;
+  const int rowoff = (wgi - g * Q) * R;
   const int rl = lane % R;              // row within this workgroup
   const int qi = lane / R;              // chunk-column slot within a wave load
   const int row = rowoff + rl;          // row within the 64-row group
