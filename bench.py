@@ -53,11 +53,46 @@ def parse():
     ap.add_argument("--cold-mib", type=int, default=1024, help="bytes of rotated decode copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the warm / two-launch / empty-adapter context runs (counter collection)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="only print per-kernel means of the rocprofv3 csv files under DIR (no GPU use)")
     return ap.parse_args()
+
+
+def summarize(root):
+    """Per-kernel means of rocprofv3 csv output under `root`: counter values per dispatch
+    (*_counter_collection.csv) or durations (*_kernel_trace.csv)."""
+    import csv
+    import glob
+    import re
+    rows = {}
+    for path in sorted(glob.glob(os.path.join(root, "**", "*.csv"), recursive=True)):
+        kind = "counter" if path.endswith("_counter_collection.csv") else (
+            "trace" if path.endswith("_kernel_trace.csv") else None)
+        if kind is None:
+            continue
+        for r in csv.DictReader(open(path)):
+            name = re.sub(r"\(anonymous namespace\)::|mnb::", "", r["Kernel_Name"])
+            name = re.sub(r"\(.*", "", name)
+            if kind == "counter":
+                key, val = (name, r["Grid_Size"], r["Counter_Name"]), float(r["Counter_Value"])
+            else:
+                key = (name, "%sx%s" % (r.get("Grid_Size_X", r.get("Grid_Size", "")), r.get("Grid_Size_Y", "")),
+                       "duration_us")
+                val = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
+            rows.setdefault(key, []).append(val)
+    for (name, grid, what), v in sorted(rows.items()):
+        print("%-60s grid=%-12s %-14s n=%-5d mean=%.6g" % (name[:60], grid, what, len(v), sum(v) / len(v)))
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(how the path would shard is described in the design notes); run with --gpus 1",
@@ -80,6 +115,17 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        # a plain copy of known size: the counters' reading for it calibrates their units
+        n = args.copy_probe * 2**20
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(10):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 10}), flush=True)
+        return
 
     def t16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).to(dev)
@@ -176,13 +222,22 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e-3 / n
 
-    n_ctx = min(K, 100)
-    warm_s = graph_time(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws), n_ctx)
-    tsep_s = graph_time(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd, ws=ws),
-                        n_ctx)
-    base_s = graph_time(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd, ws=ws),
-                        n_ctx)
     dbytes_base = algorithmic_bytes(dM, dN, dK, 4, False, 0)
+    context = None
+    if not args.no_context:
+        n_ctx = min(K, 100)
+        warm_s = graph_time(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws), n_ctx)
+        tsep_s = graph_time(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd,
+                                                 ws=ws), n_ctx)
+        base_s = graph_time(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd,
+                                                 ws=ws), n_ctx)
+        context = {"warm_us": round(warm_s * 1e6, 3), "warm_GBps": round(dbytes / warm_s / 1e9, 1),
+                   "t_separate_us": round(tsep_s * 1e6, 3),
+                   "empty_adapter_us": round(base_s * 1e6, 3),
+                   "empty_adapter_GBps": round(dbytes_base / base_s / 1e9, 1)}
+    dec_route = mnb.mnb_describe_route(dM, dN, dK, 4, False, mnb.MNB_ADAPTER_F16)[1]
+    pre_route = mnb.mnb_describe_route(pM, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
+    traffic = recorded_traffic("gemv")
 
     out = {
         "metric": METRIC,
@@ -204,24 +259,48 @@ def main():
             "decode_bytes": dbytes, "prefill_flops": pflops,
         },
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "gemv_kernel<4,false,1,0,8> (one launch per decode call)",
-                     "mean_us": round(dec_s * 1e6, 3)},
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": dec_route, "mean_us": round(dec_s * 1e6, 3)},
         "prefill": {"value": round(pre_tflops, 2), "unit": "TFLOP/s", "mean_us": round(pre_s * 1e6, 3),
+                    "route": pre_route,
                     "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": FP16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4),
                                  "traffic": None},
                     "bytes": pbytes},
-        "decode_context": {"warm_us": round(warm_s * 1e6, 3), "warm_GBps": round(dbytes / warm_s / 1e9, 1),
-                           "t_separate_us": round(tsep_s * 1e6, 3),
-                           "empty_adapter_us": round(base_s * 1e6, 3),
-                           "empty_adapter_GBps": round(dbytes_base / base_s / 1e9, 1)},
+        "decode_context": context,
         "wall_s": round(wall, 3),
     }
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(si, dec, pre, dbytes, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    profiles/<kernel>_*_traffic.md, if the kernel sources still hash to the recorded value
+    (else None: the counters describe a kernel that no longer exists)."""
+    import glob
+    import hashlib
+    import re
+    for path in glob.glob(os.path.join(ROOT, "profiles", kernel + "_*_traffic.md")):
+        text = open(path).read()
+        h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+        b = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+        if not (h and b):
+            continue
+        if h.group(1) == kernel_source_hash(kernel):
+            return int(b.group(1))
+    return None
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    csrc = os.path.join(ROOT, "blockwise_bit_quantized_amd", "csrc")
+    d = hashlib.sha256()
+    for f in (kernel + ".hip", "common.h"):
+        d.update(open(os.path.join(csrc, f), "rb").read())
+    return d.hexdigest()
 
 
 def cpu_baseline(si, dec, pre, dbytes, budget_s):

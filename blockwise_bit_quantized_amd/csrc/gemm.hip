@@ -1,19 +1,38 @@
-// gemm.hip -- prefill path of MatMulNBits (M > 1): FP16 MFMA GEMM over weights that are
-// dequantized once per workgroup into LDS, with the rank-32 LoRA up-projection T.B run
-// as two extra MFMA k-steps on the same accumulators before the fp16 store.
+// gemm.hip -- prefill path of MatMulNBits (M > 1): FP16 MFMA GEMM whose weight operand is
+// dequantized straight into MFMA operand registers, with the rank-32 LoRA up-projection
+// T.B run as two extra MFMA k-steps on the same accumulators before the fp16 store.
 //
 // onnxruntime PR #33370 ("[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits"), commit
 // list: prefill (fuse_up) computes T first, then the base GEMM "with an integrated
 // T * Bt^T epilogue"; a later commit names it the "fused LoRA-up output stage".
 //
-// Tile: 128 x 128 outputs per workgroup of 4 waves (2 x 2, 64 x 64 each as 2 x 2
-// v_mfma_f32_32x32x16_f16 blocks), K step 64 (two quantization blocks), LDS double buffer:
-//   global -> registers (X 64 B per thread; W 16 or 32 B of codes + scale + zero point)
-//   registers -> dequantize (q - z) * s to fp16 (exact subtraction, one rounding) -> LDS
-//   LDS -> MFMA operands (ds_read_b128; rows padded to 144 B so 8 consecutive lanes hit
-//   distinct banks)
-// Global loads run two K-steps ahead of the MFMAs (two register stages, the loop unrolled
-// by two so stages are chosen at compile time); one barrier per step.
+// Tile: 128 x 128 outputs per workgroup of 4 waves, K step 64 (two quantization blocks).
+// Wave w owns the column half nh = w & 1 (64 columns = one packed 64-row group) and the
+// block kh = w >> 1 of every K-step, and runs the MFMAs of its 128 x 64 piece over that
+// block's 32 k (4 x 2 v_mfma_f32_32x32x16_f16 blocks, two k16 steps).  So every weight is
+// dequantized exactly once, by the wave that multiplies it, directly into the B-operand
+// registers -- no fp16 weight tile goes through LDS -- and each X operand read from LDS
+// feeds two MFMAs.  After the K loop the two waves of a column half meet in LDS and the
+// kh = 0 wave adds the kh = 1 partial (fixed order: the result does not depend on timing).
+//
+// Memory pipeline.  Each K-step's inputs travel by direct-to-LDS loads
+// (global_load_lds_dwordx4 / _dword) into a 4-slot ring, three steps ahead of the MFMAs,
+// so the load latency (L2 / Infinity Cache / HBM) hides behind three steps of matrix work
+// without holding any of it in registers:
+//   * the X tile (128 rows x 64 halfs), shared by all waves: each 16-byte chunk is
+//     fetched into slot position chunk ^ ((row >> 1) & 7) (an XOR swizzle chosen through
+//     the source address, since a DMA writes lanes consecutively), so MFMA operand reads
+//     of 16 consecutive rows (256 bytes, one pass over the 64 LDS banks) hit distinct
+//     banks without padding;
+//   * the codes, scales and zero points of the wave's own 64 rows and block; the wave
+//     later reads only bytes its own lanes fetched, so it waits only on its own load
+//     counter.  Every lane issues every direct load (lanes past the useful ones fetch
+//     copies): loads narrower than 4 bytes, or under a lane mask, are not used.
+// One step ahead of its MFMAs each wave dequantizes (q - z) * s (exact subtraction, one
+// rounding) from the ring into registers.  Waits are explicit (s_waitcnt vmcnt for the
+// wave's own loads, then one barrier per step for the shared X tile); the compiler is kept
+// from moving memory accesses across the barrier.  Steps past the end issue loads from
+// clamped addresses into free slots, so every step has the same loads in flight.
 // Without an adapter the two epilogue k-steps are skipped, so the base accumulation order
 // is the same in every variant and a zero adapter reproduces the base output bitwise.
 #include "common.h"
@@ -22,19 +41,63 @@ namespace mnb {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;    // halfs per LDS row
+constexpr int kThreads = 256;
 constexpr int LDT = kRank + 8; // halfs per LDS row of the epilogue operands
+constexpr int kSlots = 4;      // ring depth: loads run kSlots - 1 steps ahead
+
+
+constexpr int kXBytes = BM * BK * 2;               // X tile of one step
+template <int C>
+struct Slot {
+  static constexpr int kX = 0;
+  static constexpr int kCodesWave = C * 1024;         // 64 rows x 16 B x C chunks
+  static constexpr int kCodes = kXBytes;
+  static constexpr int kScale = kCodes + 4 * kCodesWave;   // per wave 256 B: 64 scales, twice
+  static constexpr int kZp = kScale + 4 * 256;             // per wave 256 B: 32 or 64 B, repeated
+  static constexpr int kBytes = kZp + 4 * 256;
+};
+constexpr int kLdsBytes = kSlots * Slot<2>::kBytes;  // sized for 8-bit codes
+constexpr int kRedBytes = 2 * 128 * 64 * 4;          // the kh = 1 partials
+constexpr int kEpiOff = kRedBytes;                   // epilogue operands after them
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+static_assert(kEpiOff + 2 * BM * LDT * 2 <= kSlots * Slot<1>::kBytes, "epilogue buffers fit the ring");
+
+typedef __attribute__((address_space(3))) void lds_void;
+// direct-to-LDS load of 16 or 4 bytes per lane (lane i lands at dst + i * size); a plain
+// device function, so kernel templates instantiate for the host pass as well
+__device__ __forceinline__ void dma(const void *src, uint8_t *dst, int size) {
+  lds_void *d = (lds_void *)(dst);
+  if (size == 16) __builtin_amdgcn_global_load_lds(src, d, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
+}
+
+// s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits 3:0 and 15:14), other counters free
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// all of this wave's LDS accesses done, then the workgroup barrier; the asm memory clobber
+// keeps the compiler from moving memory accesses across it
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int BITS, bool HAS_ZP, int LORA>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   constexpr int C = BITS / 4;
-  __shared__ __attribute__((aligned(16))) _Float16 sX[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) _Float16 sW[2][BN * LDK];
+  using SL = Slot<C>;
+  // direct loads per wave per step: 4 X, C codes, 1 scale, 1 zero point
+  constexpr int kLoadsPerStep = 4 + C + 1 + (HAS_ZP ? 1 : 0);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nh = wave & 1;                   // column half: one packed 64-row group
+  const int kh = wave >> 1;                  // block of the K-step
+  const int l32 = lane & 31, hi = lane >> 5;
 
   // XCD-aware tile order: consecutive workgroup ids go to different XCDs, so give each XCD
   // a contiguous range of tiles (M fastest) that shares weight columns in its L2.
@@ -43,137 +106,141 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
   const int mt = tile % p.MT, nt = tile / p.MT;
   const int m0 = mt * BM, n0 = nt * BN;
-
-  // this thread's share of the global loads.  Every load is unconditional from a valid
-  // (clamped) address; out-of-range data is masked when it is written to LDS, so no wait
-  // is ever placed between issuing a load and the MFMAs of the current step.
-  const int xr = tid >> 1, xc = (tid & 1) * 32;
-  const bool xrow_ok = (m0 + xr) < p.M;
-  const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
-  const _Float16 *xsrc = X + (size_t)(xrow_ok ? m0 + xr : 0) * p.K + xc;
-  const int wblk = tid >> 7, wrr = tid & 127;
-  const int wg = (n0 >> 6) + (wrr >> 6), wr = wrr & 63;
-  const bool wrow_ok = wg < p.NG;
   const int nsteps = (p.KB + 1) / 2;
 
-  // register stages: global -> stage (two K-steps ahead) -> LDS (one step ahead) -> MFMA
-  struct Stage {
-    u4_t x[4];
-    u4_t c[C];
-    uint32_t s, z;
-    bool xok, wok;
-  };
-  const u4_t zero4 = {0u, 0u, 0u, 0u};
+  const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
+  const int wg = (n0 >> 6) + nh;             // packed row group of this wave
+  const bool wrow_ok = wg < p.NG;
 
-  auto gload = [&](Stage &st, int step) {
-    const bool live = step < nsteps;               // past the end: masked, from a valid address
-    step = live ? step : 0;
-    const int k0 = step * BK;
-    st.xok = live && xrow_ok && (k0 + xc) < p.K;
-    const _Float16 *xp = st.xok ? xsrc + k0 : X;
+  // ---- direct-to-LDS loads of one step into one ring slot ----
+  auto issue = [&](int step, int slot) {
+    const int sv = step < nsteps ? step : nsteps - 1;     // past the end: a valid address
+    const int k0 = sv * BK;
+    uint8_t *base = smem + slot * SL::kBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st.x[q] = *reinterpret_cast<const u4_t *>(xp + 8 * q);
-    const int kb = 2 * step + wblk;
-    st.wok = live && wrow_ok && kb < p.KB;
-    const size_t t = st.wok ? (size_t)wg * p.KB + kb : 0;
+    for (int q = 0; q < 4; ++q) {
+      const int r = 32 * wave + 8 * q + (lane >> 3);       // tile row of this lane's chunk
+      const int c = (lane & 7) ^ ((r >> 1) & 7);           // source chunk (swizzled position)
+      const int m = min(m0 + r, p.M - 1);
+      const int kk = k0 + c * 8 < p.K ? k0 + c * 8 : 0;
+      dma(X + (size_t)m * p.K + kk, base + SL::kX + (32 * wave + 8 * q) * 128, 16);
+    }
+    const int kb = 2 * sv + kh;
+    const bool ok = wrow_ok && kb < p.KB;
+    const size_t t = ok ? (size_t)wg * p.KB + kb : 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) st.c[c] = *reinterpret_cast<const u4_t *>(p.wq + ((t * C + c) * kGroup + wr) * 16);
-    st.s = p.sc[t * kGroup + wr];
-    st.z = 0;
+    for (int c = 0; c < C; ++c)
+      dma(p.wq + ((t * C + c) * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+    dma(p.sc + t * kGroup + 2 * l32, base + SL::kScale + wave * 256, 4);
     if constexpr (HAS_ZP) {
-      if constexpr (BITS == 4) st.z = p.zp[t * 32 + (wr >> 1)];
-      else st.z = p.zp[t * kGroup + wr];
+      const uint8_t *zsrc = BITS == 4 ? p.zp + t * 32 + 4 * (lane & 7) : p.zp + t * kGroup + 4 * (lane & 15);
+      dma(zsrc, base + SL::kZp + wave * 256, 4);
     }
   };
 
-  auto sstore = [&](const Stage &st, int buf) {
-    u4_t *dx = reinterpret_cast<u4_t *>(&sX[buf][xr * LDK + xc]);
+  // ---- dequantize this wave's block of one step into B operands [nb][kk] ----
+  // The k index of an MFMA is a summation index, so any assignment of the block's k to
+  // (k16 step kk, lane half hi) works if X uses the same one.  Here (kk, hi) takes the 8 k
+  // of 8-k chunk 2 * hi + kk: for 4-bit codes that is word 2 * hi + kk of the row's
+  // 16-byte chunk (pair i of a word = k 2i, 2i+1 of its 8), for 8-bit codes bytes
+  // 8 * kk .. 8 * kk + 7 of the row's 16-byte chunk hi, so a lane reads one contiguous
+  // piece and needs no selects.  B operand: lane holds 8 consecutive k of column l32;
+  // column = weight row 32 * nb + l32.
+  struct Raw {
+    u4_t cw[2];          // 4-bit: words (2hi, 2hi+1) in [0], [1]; 8-bit: chunk hi
+    uint32_t sraw[2], zb[2];
+  };
+  auto dq_read = [&](int slot, Raw &rw) {
+    const uint8_t *base = smem + slot * SL::kBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dx[q] = st.xok ? st.x[q] : zero4;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int r = 32 * nb + l32;
+      if constexpr (BITS == 4) {
+        const u2_t w2 = *reinterpret_cast<const u2_t *>(base + SL::kCodes + wave * SL::kCodesWave + r * 16 + hi * 8);
+        rw.cw[nb][0] = w2[0];
+        rw.cw[nb][1] = w2[1];
+      } else {
+        rw.cw[nb] = *reinterpret_cast<const u4_t *>(base + SL::kCodes + wave * SL::kCodesWave + hi * 1024 + r * 16);
+      }
+      rw.sraw[nb] = *reinterpret_cast<const uint16_t *>(base + SL::kScale + wave * 256 + r * 2);
+      rw.zb[nb] = 0;
+      if constexpr (HAS_ZP) rw.zb[nb] = BITS == 4 ? base[SL::kZp + wave * 256 + (r >> 1)] : base[SL::kZp + wave * 256 + r];
+    }
+  };
+  auto dq_compute = [&](int step, const Raw &rw, int nb, u4_t (&bo)[2][2]) {
+    const bool wok = wrow_ok && 2 * step + kh < p.KB;
+    const int r = 32 * nb + l32;
     uint32_t z = 1u << (BITS - 1);
-    if constexpr (HAS_ZP) z = BITS == 4 ? (st.z >> ((wr & 1) * 4)) & 0xFu : st.z;
+    if constexpr (HAS_ZP) z = BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
     const _Float16 zz = (_Float16)(float)(1024u + z);
     const h2_t zz2 = {zz, zz};
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(st.wok ? st.s : 0u));
+    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(wok ? rw.sraw[nb] : 0u));
     const h2_t s2 = {sv, sv};
-    u4_t out[4];
-    if constexpr (BITS == 4) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+    for (int kk = 0; kk < 2; ++kk) {
+      if constexpr (BITS == 4) {
+        const uint32_t w = rw.cw[nb][kk];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[j][i] = as_u32((nib_pair(st.c[0][j], i) - zz2) * s2);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d = 8 * c + 2 * j;   // dword index of k = 16c + 4j within the block
-          out[d >> 2][d & 3] = as_u32((byte_pair_lo(st.c[c][j]) - zz2) * s2);
-          out[(d + 1) >> 2][(d + 1) & 3] = as_u32((byte_pair_hi(st.c[c][j]) - zz2) * s2);
-        }
+        for (int i = 0; i < 4; ++i) bo[nb][kk][i] = as_u32((nib_pair(w, i) - zz2) * s2);
+      } else {
+        const uint32_t w0 = rw.cw[nb][2 * kk], w1 = rw.cw[nb][2 * kk + 1];
+        bo[nb][kk][0] = as_u32((byte_pair_lo(w0) - zz2) * s2);
+        bo[nb][kk][1] = as_u32((byte_pair_hi(w0) - zz2) * s2);
+        bo[nb][kk][2] = as_u32((byte_pair_lo(w1) - zz2) * s2);
+        bo[nb][kk][3] = as_u32((byte_pair_hi(w1) - zz2) * s2);
+      }
     }
-    u4_t *dw = reinterpret_cast<u4_t *>(&sW[buf][wrr * LDK + wblk * 32]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dw[q] = out[q];
   };
 
-  f16x_t acc[2][2];
+  f16x_t acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  const int arow = (lane & 31);
-  const int akof = 8 * (lane >> 5);
-  Stage sa, sb;                       // even steps use sa, odd steps use sb
-  gload(sa, 0);
-  gload(sb, 1);
-  // LoRA epilogue operands, fetched before the main loop so their latency is hidden:
-  // T rows (sum of the FP32 K-part partials, in part order) and this thread's slice of B.
+  // ---- X operands of this wave's block of one K-step (read right after the barrier
+  // that publishes the step, so their latency passes while the next step is prepared) ----
+  auto read_a = [&](int slot, h8_t (&af)[2][4]) {
+    const uint8_t *xs = smem + slot * SL::kBytes + SL::kX;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 4 * kh + 2 * hi + kk;      // 8-k chunk of the step (see the B operand)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = mb * 32 + l32;
+        af[kk][mb] = *reinterpret_cast<const h8_t *>(xs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      }
+    }
+  };
+  // ---- a quarter of this wave's block of one K-step: k16 step kk, row blocks 2h, 2h+1 ----
+  auto mfma_q = [&](const h8_t (&af)[2][4], const u4_t (&bo)[2][2], int kk, int h) {
+#pragma unroll
+    for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk][mb], __builtin_bit_cast(h8_t, bo[nb][kk]),
+                                                             acc[mb][nb], 0, 0, 0);
+  };
+
+  // LoRA epilogue operands, fetched first (ordinary loads that complete ahead of the ring
+  // loads): T rows (FP32 K-part partials, added in part order) and this thread's B slice
   float tsum[16];
   u4_t braw[2];
   uint32_t bsc[8];
   bool bvec = false;
   const int trow = tid >> 1, thh = (tid & 1) * 16;
   const int br = tid >> 3, bnc = (tid & 7) * 16;
+  float4 tv[4][4];
   if constexpr (LORA != 0) {
-    const int m = m0 + trow;
-    const size_t mrow = m < p.M ? (size_t)m : 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
-    // up to four parts in flight at once (clamped part index, masked), then any rest
-    float4 tv[4][4];
+    const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
       const int pc = pp < p.tparts ? pp : 0;
       const float *src = p.tpart + ((size_t)pc * p.M + mrow) * kRank + thh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) tv[pp][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
-    }
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      if (pp < p.tparts) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          tsum[4 * q + 0] += tv[pp][q].x;
-          tsum[4 * q + 1] += tv[pp][q].y;
-          tsum[4 * q + 2] += tv[pp][q].z;
-          tsum[4 * q + 3] += tv[pp][q].w;
-        }
-      }
-    }
-    for (int pp = 4; pp < p.tparts; ++pp) {
-      const float *src = p.tpart + ((size_t)pp * p.M + mrow) * kRank + thh;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
-        tsum[4 * q + 0] += v.x;
-        tsum[4 * q + 1] += v.y;
-        tsum[4 * q + 2] += v.z;
-        tsum[4 * q + 3] += v.w;
-      }
     }
     const int n = n0 + bnc;
     if constexpr (LORA == 1) {
@@ -198,92 +265,156 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
     }
   }
 
-  auto mfma_step = [&](int buf) {
-    h8_t af[BK / 16][2], bf[BK / 16][2];
+  // ---- prologue: steps 0..2 in flight, step 0 dequantized ----
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
+  for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
+  if constexpr (LORA != 0) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[kk][mb] = *reinterpret_cast<const h8_t *>(&sX[buf][(wm * 64 + mb * 32 + arow) * LDK + kk * 16 + akof]);
+    for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      if (pp < p.tparts) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          tsum[4 * q + 0] += tv[pp][q].x;
+          tsum[4 * q + 1] += tv[pp][q].y;
+          tsum[4 * q + 2] += tv[pp][q].z;
+          tsum[4 * q + 3] += tv[pp][q].w;
+        }
+      }
+    }
+    for (int pp = 4; pp < p.tparts; ++pp) {
+      const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
+        tsum[4 * q + 0] += v.x;
+        tsum[4 * q + 1] += v.y;
+        tsum[4 * q + 2] += v.z;
+        tsum[4 * q + 3] += v.w;
+      }
+    }
+  }
+  u4_t bcur[2][2], bnext[2][2];
+  h8_t acur[2][4];
+  wait_vmcnt<2 * kLoadsPerStep>();       // own loads of step 0 have landed
+  {
+    Raw rw;
+    dq_read(0, rw);
+    dq_compute(0, rw, 0, bcur);
+    dq_compute(0, rw, 1, bcur);
+  }
+  lds_barrier();                          // step 0's X tile (all waves) is in LDS
+  read_a(0, acur);
+
+  // ---- main loop: step s computes; step s+1 is dequantized; step s+3 is loaded ----
+  // Source order is issue order (scheduling barriers keep the compiler from regrouping):
+  // the step's 16 MFMAs come in quarters with the next step's dequantization arithmetic
+  // between them, so the VALU work runs while the matrix core is busy.
+  auto body = [&](int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2]) {
+    issue(s + kSlots - 1, (s + kSlots - 1) & (kSlots - 1));
+    wait_vmcnt<2 * kLoadsPerStep>();     // own loads of step s+1 have landed
+    Raw rw;
+    dq_read((s + 1) & (kSlots - 1), rw);  // past the end: unused, from a loaded slot
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(acur, bc, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(acur, bc, 0, 1);
+    dq_compute(s + 1, rw, 0, bn);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(acur, bc, 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_q(acur, bc, 1, 1);
+    dq_compute(s + 1, rw, 1, bn);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();                        // step s+1's X ready for all; slot s free
+    read_a((s + 1) & (kSlots - 1), acur); // past the end: unused
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    body(s, bcur, bnext);
+    body(s + 1, bnext, bcur);
+  }
+  if (s < nsteps) body(s, bcur, bnext);
+  wait_vmcnt<0>();                        // the trailing loads into free slots are done
+  lds_barrier();
+
+  // ---- the kh = 1 wave of each column half hands its partial to the kh = 0 wave ----
+  float4 *red = reinterpret_cast<float4 *>(smem);
+  if (kh == 1) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        bf[kk][nb] = *reinterpret_cast<const h8_t *>(&sW[buf][(wn * 64 + nb * 32 + arow) * LDK + kk * 16 + akof]);
-    }
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk][mb], bf[kk][nb], acc[mb][nb], 0, 0, 0);
-  };
-
-  // The pair loop is branch-free (a trailing odd step runs masked with zero data), so
-  // the loads of one stage stay in flight across the other stage's MFMAs.
-  sstore(sa, 0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; s += 2) {
-    gload(sa, s + 2);        // even step s: LDS buffer 0 holds step s, stage sb step s+1
-    mfma_step(0);
-    sstore(sb, 1);
-    __syncthreads();
-    gload(sb, s + 3);        // odd step s+1: LDS buffer 1 holds step s+1, stage sa step s+2
-    mfma_step(1);
-    sstore(sa, 0);
-    __syncthreads();
+        for (int v4 = 0; v4 < 4; ++v4)
+          red[((nh * 32 + (mb * 2 + nb) * 4 + v4) * 64) + lane] =
+              float4{acc[mb][nb][4 * v4], acc[mb][nb][4 * v4 + 1], acc[mb][nb][4 * v4 + 2], acc[mb][nb][4 * v4 + 3]};
   }
-
+  _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
+  _Float16 *sB = sT + BM * LDT;
   if constexpr (LORA != 0) {
     // epilogue operands: T tile [128 m][32 r] (fp16, rounded once from the FP32 sum) and
     // the B tile transposed to [128 n][32 r]
-    _Float16 *sT = &sX[0][0];
-    _Float16 *sB = &sW[0][0];
-    {
-      u4_t o[2];
+    u4_t o[2];
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const h2_t hv = {(_Float16)tsum[8 * q + 2 * d], (_Float16)tsum[8 * q + 2 * d + 1]};
-          o[q][d] = as_u32(hv);
-        }
-      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
-      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
-    }
-    {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int n = n0 + bnc + e;
-        _Float16 v = (_Float16)0.f;
-        if (bvec) {
-          if constexpr (LORA == 1) {
-            v = as_h2(braw[e >> 3][(e & 7) >> 1])[e & 1];
-          } else {
-            const int8_t b8 = (int8_t)((braw[0][e >> 2] >> (8 * (e & 3))) & 0xff);
-            v = (_Float16)((float)b8 * (float)as_h2(bsc[e >> 1])[e & 1]);
-          }
-        } else if (n < p.N) {
-          if constexpr (LORA == 1) {
-            v = __builtin_bit_cast(_Float16, static_cast<const uint16_t *>(p.B)[(size_t)br * p.N + n]);
-          } else {
-            v = (_Float16)((float)static_cast<const int8_t *>(p.B)[(size_t)br * p.N + n] * h2f(p.sB[n]));
-          }
-        }
-        sB[(bnc + e) * LDT + br] = v;
+      for (int d = 0; d < 4; ++d) {
+        const h2_t hv = {(_Float16)tsum[8 * q + 2 * d], (_Float16)tsum[8 * q + 2 * d + 1]};
+        o[q][d] = as_u32(hv);
       }
+    *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
+    *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int n = n0 + bnc + e;
+      _Float16 v = (_Float16)0.f;
+      if (bvec) {
+        if constexpr (LORA == 1) {
+          v = as_h2(braw[e >> 3][(e & 7) >> 1])[e & 1];
+        } else {
+          const int8_t b8 = (int8_t)((braw[0][e >> 2] >> (8 * (e & 3))) & 0xff);
+          v = (_Float16)((float)b8 * (float)as_h2(bsc[e >> 1])[e & 1]);
+        }
+      } else if (n < p.N) {
+        if constexpr (LORA == 1) {
+          v = __builtin_bit_cast(_Float16, static_cast<const uint16_t *>(p.B)[(size_t)br * p.N + n]);
+        } else {
+          v = (_Float16)((float)static_cast<const int8_t *>(p.B)[(size_t)br * p.N + n] * h2f(p.sB[n]));
+        }
+      }
+      sB[(bnc + e) * LDT + br] = v;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (kh == 1) return;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const float4 o = red[((nh * 32 + (mb * 2 + nb) * 4 + v4) * 64) + lane];
+        acc[mb][nb][4 * v4] += o.x;
+        acc[mb][nb][4 * v4 + 1] += o.y;
+        acc[mb][nb][4 * v4 + 2] += o.z;
+        acc[mb][nb][4 * v4 + 3] += o.w;
+      }
+
+  if constexpr (LORA != 0) {
+    const int akof = 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < kRank / 16; ++kk) {
-      h8_t af[2], bf[2];
+      h8_t af[4], bf[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        af[mb] = *reinterpret_cast<const h8_t *>(&sT[(wm * 64 + mb * 32 + arow) * LDT + kk * 16 + akof]);
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const h8_t *>(&sT[(mb * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(wn * 64 + nb * 32 + arow) * LDT + kk * 16 + akof]);
+        bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(nh * 64 + nb * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
@@ -293,13 +424,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
   // store: accumulator register v of a 32x32 block holds row 8*(v/4) + 4*(lane/32) + v%4,
   // column lane % 32
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int n = n0 + wn * 64 + nb * 32 + (lane & 31);
+      const int n = n0 + nh * 64 + nb * 32 + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + mb * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = m0 + mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
         if (m < p.M && n < p.N)
           p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[mb][nb][v]);
       }
@@ -308,7 +439,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
 template <int BITS, bool HAS_ZP>
 hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
-  const dim3 grid(p.MT * p.NT), block(256);
+  const dim3 grid(p.MT * p.NT), block(kThreads);
   switch (lora) {
     case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0>), grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 1>), grid, block, 0, s, p); break;
