@@ -71,6 +71,13 @@ __device__ __forceinline__ void dma(const void *src, uint8_t *dst, int size) {
   else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
 }
 
+// (x & mask) | (c & ~mask) in one v_bfi_b32 (the compiler splits the folded form into two)
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t c) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(x), "v"(c));
+  return d;
+}
+
 // s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits 3:0 and 15:14), other counters free
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -112,19 +119,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int wg = (n0 >> 6) + nh;             // packed row group of this wave
   const bool wrow_ok = wg < p.NG;
 
-  // ---- direct-to-LDS loads of one step into one ring slot ----
-  auto issue = [&](int step, int slot) {
+  // ---- direct-to-LDS loads of one step into one ring slot: X rows (two halves), then the
+  // wave's codes, scales and zero points ----
+  // per-lane X source of each of the wave's 4 chunk loads at k = 0: row min(m0 + r, M - 1),
+  // chunk c = position ^ ((r >> 1) & 7) of the swizzle; a step adds 64 k
+  const _Float16 *xsrc[4];
+  bool xhigh[4];                            // chunk in the step's second block
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 32 * wave + 8 * q + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    xsrc[q] = X + (size_t)min(m0 + r, p.M - 1) * p.K + c * 8;
+    xhigh[q] = c >= 4;
+  }
+  auto issue_x = [&](int step, int slot, int half) {
     const int sv = step < nsteps ? step : nsteps - 1;     // past the end: a valid address
-    const int k0 = sv * BK;
+    // with an odd block count the last step's second block lies past K: those chunks
+    // re-read the first block (any valid address; the block's scales are masked to 0)
+    const bool ragged = 2 * sv + 1 >= p.KB;
     uint8_t *base = smem + slot * SL::kBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 32 * wave + 8 * q + (lane >> 3);       // tile row of this lane's chunk
-      const int c = (lane & 7) ^ ((r >> 1) & 7);           // source chunk (swizzled position)
-      const int m = min(m0 + r, p.M - 1);
-      const int kk = k0 + c * 8 < p.K ? k0 + c * 8 : 0;
-      dma(X + (size_t)m * p.K + kk, base + SL::kX + (32 * wave + 8 * q) * 128, 16);
+    for (int q = 2 * half; q < 2 * half + 2; ++q) {
+      const int k0 = sv * BK - ((ragged && xhigh[q]) ? 32 : 0);
+      dma(xsrc[q] + k0, base + SL::kX + (32 * wave + 8 * q) * 128, 16);
     }
+  };
+  auto issue_w = [&](int step, int slot) {
+    const int sv = step < nsteps ? step : nsteps - 1;
+    uint8_t *base = smem + slot * SL::kBytes;
     const int kb = 2 * sv + kh;
     const bool ok = wrow_ok && kb < p.KB;
     const size_t t = ok ? (size_t)wg * p.KB + kb : 0;
@@ -136,6 +158,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       const uint8_t *zsrc = BITS == 4 ? p.zp + t * 32 + 4 * (lane & 7) : p.zp + t * kGroup + 4 * (lane & 15);
       dma(zsrc, base + SL::kZp + wave * 256, 4);
     }
+  };
+  auto issue = [&](int step, int slot) {
+    issue_x(step, slot, 0);
+    issue_x(step, slot, 1);
+    issue_w(step, slot);
   };
 
   // ---- dequantize this wave's block of one step into B operands [nb][kk] ----
@@ -172,16 +199,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     const int r = 32 * nb + l32;
     uint32_t z = 1u << (BITS - 1);
     if constexpr (HAS_ZP) z = BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
-    const _Float16 zz = (_Float16)(float)(1024u + z);
-    const h2_t zz2 = {zz, zz};
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(wok ? rw.sraw[nb] : 0u));
-    const h2_t s2 = {sv, sv};
+    // binary16 of 1024 + z is 0x6400 | z (z < 1024): both halves at once
+    const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);
+    const h2_t s2 = as_h2((wok ? rw.sraw[nb] : 0u) * 0x00010001u);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if constexpr (BITS == 4) {
+        // Nibbles 0 and 2 of each half sit in mantissa bits 0-3 (after a shift by 8 for
+        // 2): OR-ing 0x6400 gives 1024 + q.  Nibbles 1 and 3 are taken in place, at bits
+        // 4-7: 1024 + 16 q; minus (1024 + 16 z) that is 16 (q - z), exact, and the scale
+        // for them is s / 16 (exact unless s < 2^-10), so each product is (q - z) s
+        // rounded once either way.
+        const h2_t z162 = as_h2((z * 0x00100010u) | 0x64006400u);
+        const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const h2_t s162 = s2 * sixteenth;
         const uint32_t w = rw.cw[nb][kk];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bo[nb][kk][i] = as_u32((nib_pair(w, i) - zz2) * s2);
+        const uint32_t w8 = w >> 8;
+        bo[nb][kk][0] = as_u32((as_h2(bfi(0x000F000Fu, w, 0x64006400u)) - zz2) * s2);
+        bo[nb][kk][1] = as_u32((as_h2(bfi(0x00F000F0u, w, 0x64006400u)) - z162) * s162);
+        bo[nb][kk][2] = as_u32((as_h2(bfi(0x000F000Fu, w8, 0x64006400u)) - zz2) * s2);
+        bo[nb][kk][3] = as_u32((as_h2(bfi(0x00F000F0u, w8, 0x64006400u)) - z162) * s162);
       } else {
         const uint32_t w0 = rw.cw[nb][2 * kk], w1 = rw.cw[nb][2 * kk + 1];
         bo[nb][kk][0] = as_u32((byte_pair_lo(w0) - zz2) * s2);
@@ -220,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[kk][mb], __builtin_bit_cast(h8_t, bo[nb][kk]),
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, bo[nb][kk]), af[kk][mb],
                                                              acc[mb][nb], 0, 0, 0);
   };
 
@@ -311,31 +348,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // Source order is issue order (scheduling barriers keep the compiler from regrouping):
   // the step's 16 MFMAs come in quarters with the next step's dequantization arithmetic
   // between them, so the VALU work runs while the matrix core is busy.
-  auto body = [&](int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2]) {
-    issue(s + kSlots - 1, (s + kSlots - 1) & (kSlots - 1));
-    wait_vmcnt<2 * kLoadsPerStep>();     // own loads of step s+1 have landed
+  // slot: s mod kSlots, a compile-time constant at every call
+  auto body = [&](int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2], const int slot) {
+    const int ls = (slot + kSlots - 1) & (kSlots - 1);
+    const int ns = (slot + 1) & (kSlots - 1);
+    wait_vmcnt<kLoadsPerStep>();         // own loads of step s+1 have landed (s+2's may not)
     Raw rw;
-    dq_read((s + 1) & (kSlots - 1), rw);  // past the end: unused, from a loaded slot
+    dq_read(ns, rw);                      // past the end: unused, from a loaded slot
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 0);
+    issue_x(s + kSlots - 1, ls, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 1);
     dq_compute(s + 1, rw, 0, bn);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 1, 0);
+    issue_x(s + kSlots - 1, ls, 1);
+    issue_w(s + kSlots - 1, ls);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 1, 1);
     dq_compute(s + 1, rw, 1, bn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();                        // step s+1's X ready for all; slot s free
-    read_a((s + 1) & (kSlots - 1), acur); // past the end: unused
+    read_a(ns, acur);                     // past the end: unused
   };
+  // unrolled by the ring depth, so ring slots are compile-time constants
   int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    body(s, bcur, bnext);
-    body(s + 1, bnext, bcur);
+  for (; s + 3 < nsteps; s += 4) {
+    body(s, bcur, bnext, 0);
+    body(s + 1, bnext, bcur, 1);
+    body(s + 2, bcur, bnext, 2);
+    body(s + 3, bnext, bcur, 3);
   }
-  if (s < nsteps) body(s, bcur, bnext);
+  if (s < nsteps) body(s, bcur, bnext, 0);
+  if (s + 1 < nsteps) body(s + 1, bnext, bcur, 1);
+  if (s + 2 < nsteps) body(s + 2, bcur, bnext, 2);
   wait_vmcnt<0>();                        // the trailing loads into free slots are done
   lds_barrier();
 
@@ -417,24 +464,36 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[mb], acc[mb][nb], 0, 0, 0);
     }
   }
 
-  // store: accumulator register v of a 32x32 block holds row 8*(v/4) + 4*(lane/32) + v%4,
-  // column lane % 32
+  // store: the MFMAs computed Y^T blocks (weights as the row operand), so accumulator
+  // register v of block [mb][nb] holds output row m = 32 mb + lane % 32 and column
+  // n = 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per register
+  // quad, stored as one 8-byte vector
+  const bool vec = (p.N & 3) == 0;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + mb * 32 + l32;
+    if (m >= p.M) continue;
+    uint16_t *yrow = p.Y + (size_t)m * p.N;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int n = n0 + nh * 64 + nb * 32 + l32;
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + mb * 32 + 8 * (v >> 2) + 4 * hi + (v & 3);
-        if (m < p.M && n < p.N)
-          p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)acc[mb][nb][v]);
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi;
+        const h2_t lo = {(_Float16)acc[mb][nb][4 * j], (_Float16)acc[mb][nb][4 * j + 1]};
+        const h2_t hi2 = {(_Float16)acc[mb][nb][4 * j + 2], (_Float16)acc[mb][nb][4 * j + 3]};
+        if (vec && n + 4 <= p.N) {
+          *reinterpret_cast<u2_t *>(yrow + n) = u2_t{as_u32(lo), as_u32(hi2)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) yrow[n + e] = __builtin_bit_cast(uint16_t, e < 2 ? lo[e] : hi2[e - 2]);
+        }
       }
-    }
+  }
 }
 
 template <int BITS, bool HAS_ZP>
