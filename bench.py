@@ -265,7 +265,7 @@ def main():
                     "route": pre_route,
                     "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": FP16_PEAK_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4),
-                                 "traffic": None},
+                                 "traffic": recorded_traffic("gemm")},
                     "bytes": pbytes},
         "decode_context": context,
         "wall_s": round(wall, 3),
