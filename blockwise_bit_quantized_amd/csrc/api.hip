@@ -27,26 +27,23 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 
-// Workspace: a fixed control area and the final-T replicas first (their offsets depend
-// on nothing, so a zeroed workspace stays valid for calls of any shape), then data
-// regions that need no initialisation.
+// Workspace: a fixed control area first (its offsets depend on nothing, so a zeroed
+// workspace stays valid for calls of any shape), then data regions that need no
+// initialisation.
 struct WsLayout {
-  size_t ctrl, tfinal, tinpass, tproj, total;
-  int gt, q, tparts, tmt;
+  size_t ctrl, tinpass, tproj, total;
+  int gt, tparts, tmt;
 };
 
 WsLayout ws_layout(int M, int N, int K, int rank) {
   WsLayout w{};
-  w.q = gemv_rows_split(N);
   w.gt = cdiv(K, kTSliceRows);
   w.tparts = std::max(1, tproj_parts(K));
   w.tmt = cdiv(M, 32);
   size_t off = align_up(kCtrlBytes);
   w.ctrl = 0;
-  w.tfinal = off;
-  off += align_up(kTFinalBytes);
   w.tinpass = off;
-  if (rank) off += align_up((size_t)w.gt * kRank * sizeof(unsigned long long));
+  if (rank) off += align_up((size_t)kTReplicas * w.gt * kRank * sizeof(unsigned long long));
   w.tproj = off;
   if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
   w.total = off;
@@ -148,9 +145,9 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
+    const int q = gemv_rows_split(N, extra > 0);
     snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
-             r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * w.q + extra, M, kGroup / w.q, w.q,
-             extra);
+             r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
     snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64", tp, bits, has_zp ? "x" : "def", ln,
              cdiv(M, 128) * cdiv(N, 128));
@@ -299,16 +296,15 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     p.K = K;
     p.NG = NG;
     p.KB = KB;
-    p.q = w.q;
     p.gt = (lora && r.tmode == 0) ? w.gt : 0;
+    p.q = gemv_rows_split(N, p.gt > 0);
     p.kt = kTSliceRows;
-    p.nepi = NG * w.q;
+    p.nepi = NG * p.q;
     p.tparts = w.tparts;
     p.tmpad = M;
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
     p.tin = tproj_out;
     p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
-    p.tfinal = reinterpret_cast<unsigned long long *>(ws + w.tfinal);
     // rows in chunks that respect the grid's y limit (the in-pass T path has M == 1)
     const int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
@@ -318,7 +314,7 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
       q.Y = p.Y + (size_t)m0 * N;
       if (tproj_out) q.tin = tproj_out + (size_t)m0 * kRank;
       q.M = mc;
-      const int gx = NG * w.q + p.gt;
+      const int gx = NG * p.q + p.gt;
       if (launch_gemv(bits, has_zp, lora, r.tmode, q, gx, mc, s) != hipSuccess) return MNB_ERR_HIP;
     }
     return MNB_OK;

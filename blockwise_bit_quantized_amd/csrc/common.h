@@ -68,18 +68,17 @@ __device__ __forceinline__ h2_t byte_pair_hi(uint32_t w) {
 
 // Control area at the start of the workspace (its layout depends on no shape):
 //   * 64 words: the in-pass T call epoch, the count of done-groups that have finished
-//     reading T, a sticky error word and the count of T slices written;
+//     reading T and a sticky error word;
 //   * kDoneGroups counters of row workgroups that have read T, one per 256-byte line so
-//     that the increments of different groups do not queue on one address;
-//   * kTReplicas copies of the final T (32 words of FP32 value | call tag << 32 each), so
-//     that the row workgroups' reads spread over several lines.
-// Every counter is back to zero when a call ends.
-enum { CTRL_EPOCH = 0, CTRL_TDONE = 1, CTRL_ERROR = 2, CTRL_TCOUNT = 3, CTRL_WORDS = 64 };
+//     that the increments of different groups do not queue on one address.
+// Every counter is back to zero when a call ends.  The in-pass T slices are written in
+// kTReplicas copies (32 words of FP32 value | call tag << 32 per slice), so that the row
+// workgroups' reads spread over many lines.
+enum { CTRL_EPOCH = 0, CTRL_TDONE = 1, CTRL_ERROR = 2, CTRL_WORDS = 64 };
 constexpr int kDoneGroups = 16;
 constexpr int kCtrlLineInts = 64;                                        // 256 B
 constexpr int kTReplicas = 16;
 constexpr size_t kCtrlBytes = (size_t)(1 + kDoneGroups) * kCtrlLineInts * sizeof(int);
-constexpr size_t kTFinalBytes = (size_t)kTReplicas * kRank * sizeof(unsigned long long);
 __device__ __forceinline__ int ctrl_done_word(int group) { return (1 + group) * kCtrlLineInts; }
 
 // Bounded wait for the in-pass T handoff; on expiry the kernel records CTRL_ERROR and
@@ -109,8 +108,7 @@ struct GemvParams {
   int tmpad;              // precomputed T: rows per partial (= M of the T launch)
   int *ctrl;              // control words
   const float *tin;       // precomputed T partials [tparts, tmpad, 32]
-  unsigned long long *tword;  // in-pass T: [gt, 32] slice words (FP32 value | call tag << 32)
-  unsigned long long *tfinal; // in-pass T: [kTReplicas, 32] final words, same encoding
+  unsigned long long *tword;  // in-pass T: [kTReplicas, gt, 32] slice words (FP32 value | call tag << 32)
 };
 
 struct TprojParams {
@@ -154,7 +152,7 @@ hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t
 hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s);
 
 // planning helpers shared by the dispatcher and the launchers
-int gemv_rows_split(int N);                    // q: 1, 2, 4 or 8
+int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
 int tproj_parts(int K);                        // K parts of the T projection
 
 }  // namespace mnb

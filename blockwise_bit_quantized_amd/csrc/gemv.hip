@@ -21,13 +21,13 @@
 //    lane exchange, the waves through LDS, both in fixed order;
 //  * in-pass T: the first `gt` workgroups of the grid compute T over K-slices of `kt` rows.
 //    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
-//    where the tag identifies this call (a per-call epoch kept in the workspace, never 0).
-//    The slice workgroup that counts itself last adds the slices in slice order and writes
-//    the final T, tagged the same way, into kTReplicas copies.  Each row workgroup has one
-//    extra wave that carries no weight loads: it polls one word of its copy, reads the 32
-//    words, accepts them when every tag matches (no fences: the tags make a stale or early
-//    read detectable) and leaves T in LDS for the epilogue.  The slice workgroups are
-//    dispatched first and wait only for each other, so every bounded wait ends.  Row
+//    where the tag identifies this call (a per-call epoch kept in the workspace, never 0),
+//    into kTReplicas copies, so that the readers spread over many lines.  Each row
+//    workgroup has one extra wave that carries no weight loads: it polls the first word of
+//    every slice in its copy (one lane per slice), then reads all the words, accepts them
+//    when every tag matches (no fences: the tags make a stale or early read detectable),
+//    adds the slices in slice order and leaves T in LDS for the epilogue.  The slice
+//    workgroups are dispatched first and never wait, so every bounded wait ends.  Row
 //    workgroups report that they have read T through a two-level count (kDoneGroups
 //    counters, then one); the last one resets the counts and advances the epoch.
 #include <algorithm>
@@ -196,37 +196,15 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    if (lane < kRank) {
-      float t = 0.f;
+  if (wave == 0 && lane < kRank) {
+    float t = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) t += tsh[w][lane];
-      __hip_atomic_store(p.tword + (size_t)j * kRank + lane, tagged(t, tag), __ATOMIC_RELAXED,
+    for (int w = 0; w < kWaves; ++w) t += tsh[w][lane];
+    const unsigned long long word = tagged(t, tag);
+#pragma unroll
+    for (int c = 0; c < kTReplicas; ++c)
+      __hip_atomic_store(p.tword + ((size_t)c * p.gt + j) * kRank + lane, word, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
-    }
-    // the slice workgroup that counts itself last publishes the final T
-    int last = 0;
-    if (lane == 0)
-      last = __hip_atomic_fetch_add(&p.ctrl[CTRL_TCOUNT], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.gt - 1;
-    if (__builtin_amdgcn_readfirstlane(last)) {
-      float tv = 0.f;
-      bool ok = false;
-      for (int spins = 0; spins <= kSpinLimit && !ok; ++spins) {
-        ok = __all(gather_t(p.tword, p.gt, tag, lane, tv));
-        if (!ok) __builtin_amdgcn_s_sleep(1);
-      }
-      if (!ok) {
-        tv = __builtin_nanf("");
-        if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
-      }
-      if (lane < kRank) {
-        const unsigned long long word = tagged(tv, tag);
-#pragma unroll
-        for (int c = 0; c < kTReplicas; ++c)
-          __hip_atomic_store(p.tfinal + c * kRank + lane, word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (lane == 0) __hip_atomic_store(&p.ctrl[CTRL_TCOUNT], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
 }
 
@@ -277,22 +255,20 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       // epilogue and reports that it has read T.
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
-      const unsigned long long *rep = p.tfinal + (bid % kTReplicas) * kRank;
+      const unsigned long long *rep = p.tword + (size_t)(bid % kTReplicas) * p.gt * kRank;
+      // hint: one lane per slice (the first 64) polls the slice's first word
       int spins = 0;
-      if (lane == 0)
-        while ((uint32_t)(__hip_atomic_load(rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32) != tag &&
-               spins < kSpinLimit) {
-          ++spins;
-          __builtin_amdgcn_s_sleep(2);
-        }
-      spins = __builtin_amdgcn_readfirstlane(spins);   // lane 0's count: the loop below is uniform
+      for (; spins < kSpinLimit; ++spins) {
+        const bool seen = lane >= p.gt ||
+                          (uint32_t)(__hip_atomic_load(rep + (size_t)lane * kRank, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT) >> 32) == tag;
+        if (__all(seen)) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
       float tv = 0.f;
       bool ok = false;
       for (; spins <= kSpinLimit && !ok; ++spins) {
-        const unsigned long long w =
-            lane < kRank ? __hip_atomic_load(rep + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-        tv = __builtin_bit_cast(float, (uint32_t)w);
-        ok = __all(lane >= kRank || (uint32_t)(w >> 32) == tag);
+        ok = __all(gather_t(rep, p.gt, tag, lane, tv));
         if (!ok) __builtin_amdgcn_s_sleep(1);
       }
       if (!ok) {
@@ -500,16 +476,16 @@ int loads_per_wave(int K, int bits, int q) {
 
 }  // namespace
 
-#ifndef MNB_GEMV_MIN_WG
-#define MNB_GEMV_MIN_WG 512
-#endif
-
-// rows per workgroup = 64 / q: the smallest q in {1, 2, 4, 8} that gives at least
-// MNB_GEMV_MIN_WG row workgroups
-int gemv_rows_split(int N) {
+// Rows per workgroup = 64 / q: the smallest q in {1, 2, 4, 8} that gives at least 512 row
+// workgroups (two per CU), or 256 when the launch also computes T in-pass: the T slices'
+// loads then compete with fewer weight streams, and T arrives earlier (measured on the
+// 8192 x 2048 decode: 6.5 us at 256 against 6.9 us at 512; base-only 4.97 us at 512
+// against 5.29 us at 256).
+int gemv_rows_split(int N, bool inpass_t) {
   const int NG = (N + kGroup - 1) / kGroup;
+  const int target = inpass_t ? 256 : 512;
   int q = 1;
-  while (q < 8 && NG * q < MNB_GEMV_MIN_WG) q *= 2;
+  while (q < 8 && NG * q < target) q *= 2;
   return q;
 }
 

@@ -142,12 +142,14 @@ def test_dispatcher_rule():
 
 def test_gemv_grid_covers_the_chip():
     # decode: 64/q rows per workgroup with the smallest q in {1, 2, 4, 8} that gives at least
-    # 512 row workgroups (two per CU), plus the T-slice workgroups (K/256 of them)
+    # 512 row workgroups (two per CU), or 256 when T is computed in the same launch, plus
+    # the T-slice workgroups (K/256 of them)
     for N, K, bits in ((8192, 2048, 4), (4096, 4096, 4), (49152, 576, 8), (896, 896, 4)):
-        t = route(1, N=N, K=K, bits=bits, zp=0)
-        grid = int(re.search(r"grid=(\d+)x1", t).group(1))
-        q = int(re.search(r" q=(\d+)", t).group(1))
-        gt = int(re.search(r"gt=(\d+)", t).group(1))
-        ng = (N + 63) // 64
-        assert q in (1, 2, 4, 8) and (ng * q >= 512 or q == 8) and (q == 1 or ng * q // 2 < 512)
-        assert gt == (K + 255) // 256 and grid == ng * q + gt
+        for kind, target in ((1, 256), (0, 512)):
+            t = route(1, N=N, K=K, bits=bits, zp=0, kind=kind)
+            grid = int(re.search(r"grid=(\d+)x1", t).group(1))
+            q = int(re.search(r" q=(\d+)", t).group(1))
+            gt = int(re.search(r"gt=(\d+)", t).group(1))
+            ng = (N + 63) // 64
+            assert q in (1, 2, 4, 8) and (ng * q >= target or q == 8) and (q == 1 or ng * q // 2 < target)
+            assert gt == ((K + 255) // 256 if kind else 0) and grid == ng * q + gt
