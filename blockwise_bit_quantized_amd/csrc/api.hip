@@ -31,14 +31,14 @@ constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 // workspace stays valid for calls of any shape), then data regions that need no
 // initialisation.
 struct WsLayout {
-  size_t ctrl, tinpass, tproj, total;
+  size_t ctrl, tinpass, tproj, tfinal, total;
   int gt, tparts, tmt;
 };
 
 WsLayout ws_layout(int M, int N, int K, int rank) {
   WsLayout w{};
   w.gt = cdiv(K, kTSliceRows);
-  w.tparts = std::max(1, tproj_parts(K));
+  w.tparts = std::max(1, tproj_parts(M, K));
   w.tmt = cdiv(M, 32);
   size_t off = align_up(kCtrlBytes);
   w.ctrl = 0;
@@ -46,6 +46,8 @@ WsLayout ws_layout(int M, int N, int K, int rank) {
   if (rank) off += align_up((size_t)kTReplicas * w.gt * kRank * sizeof(unsigned long long));
   w.tproj = off;
   if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
+  w.tfinal = off;
+  if (rank) off += align_up((size_t)M * kRank * sizeof(float));
   w.total = off;
   return w;
 }
@@ -61,7 +63,9 @@ Route route(int M, int lora, const mnb_options *opt) {
   Route r{};
   const int path = opt ? opt->path : MNB_PATH_AUTO;
   const int flags = opt ? opt->flags : 0;
-  r.path = path != MNB_PATH_AUTO ? path : (M == 1 ? MNB_PATH_GEMV : MNB_PATH_GEMM);
+  // automatic rule: the GEMV family for M <= kSmallM (M == 1 decode, the small-M
+  // multi-row variant above it: both stream the weights once), the MFMA GEMM above
+  r.path = path != MNB_PATH_AUTO ? path : (M <= kSmallM ? MNB_PATH_GEMV : MNB_PATH_GEMM);
   r.lora = lora;
   r.tmode = 1;
   r.tproj = false;
@@ -142,7 +146,13 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   const char *ln = r.lora == LORA_NONE ? "none" : (r.lora == LORA_F16 ? "f16" : "q8");
   char tp[96] = "";
   if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tmt * w.tparts, w.tparts);
-  if (r.path == MNB_PATH_GEMV) {
+  if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
+    const int NG = cdiv(N, kGroup);
+    const int q = gemv_rows_split(N, false);
+    const int mr = gemv_rows_mr(M);
+    snprintf(buf, len, "%sgemv_rows_b%d_zp%s_%s grid=%dx%d rows=%d q=%d mr=%d", tp, bits, has_zp ? "x" : "def", ln,
+             NG * q, cdiv(M, mr), kGroup / q, q, mr);
+  } else if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
     const int q = gemv_rows_split(N, extra > 0);
@@ -272,11 +282,23 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     fprintf(stderr, "[mnb] M=%d N=%d K=%d bits=%d: %s\n", M, N, K, bits, b);
   }
 
+  // T projection output: FP32 partials per K-part; consumers read `tparts` parts.  The
+  // projection reduces them itself (per-tile arrival counter, agent-scope fences) where
+  // that pays: for small M, whose consumers would add the parts row by row, and for more
+  // than 4 parts; the GEMM adds up to 4 parts, the M == 1 GEMV up to 8, with their own
+  // loads in flight together.
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
+  int tparts = w.tparts;
   if (r.tproj) {
+    const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && (M <= kRowsMaxM || w.tparts > 4);
     TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), tproj_out,
-                   M, K, w.tmt, w.tparts};
+                   reinterpret_cast<float *>(ws + w.tfinal), reinterpret_cast<int *>(ws + w.ctrl),
+                   M, K, w.tmt, w.tparts, reduce};
     if (launch_tproj(lora, tp, s) != hipSuccess) return MNB_ERR_HIP;
+    if (reduce) {
+      tproj_out = tp.tfinal;
+      tparts = 1;
+    }
   }
 
   if (r.path == MNB_PATH_GEMV) {
@@ -300,11 +322,19 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     p.q = gemv_rows_split(N, p.gt > 0);
     p.kt = kTSliceRows;
     p.nepi = NG * p.q;
-    p.tparts = w.tparts;
+    p.tparts = tparts;
     p.tmpad = M;
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
     p.tin = tproj_out;
     p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
+    if (M > 1 && M <= kRowsMaxM) {
+      // small M: one pass over the weights for all rows (T from the projection launch)
+      p.M = M;
+      p.gt = 0;
+      p.q = gemv_rows_split(N, false);
+      if (launch_gemv_rows(bits, lora, p, NG * p.q, s) != hipSuccess) return MNB_ERR_HIP;
+      return MNB_OK;
+    }
     // rows in chunks that respect the grid's y limit (the in-pass T path has M == 1)
     const int kMaxY = 65535;
     for (int m0 = 0; m0 < M; m0 += kMaxY) {
@@ -330,7 +360,7 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
     g.sB = static_cast<const uint16_t *>(ad->B_scales);
   }
   g.tpart = tproj_out;
-  g.tparts = w.tparts;
+  g.tparts = tparts;
   g.Y = Yh;
   g.M = M;
   g.N = N;

@@ -78,7 +78,10 @@ enum { CTRL_EPOCH = 0, CTRL_TDONE = 1, CTRL_ERROR = 2, CTRL_WORDS = 64 };
 constexpr int kDoneGroups = 16;
 constexpr int kCtrlLineInts = 64;                                        // 256 B
 constexpr int kTReplicas = 16;
-constexpr size_t kCtrlBytes = (size_t)(1 + kDoneGroups) * kCtrlLineInts * sizeof(int);
+// arrival counters of the T projection's K-parts, one per 32-row M tile (M <= 32768 rows)
+constexpr int kTprojCounters = 1024;
+constexpr size_t kCtrlBytes = (size_t)(1 + kDoneGroups) * kCtrlLineInts * sizeof(int) + kTprojCounters * sizeof(int);
+__device__ __forceinline__ int ctrl_tproj_word(int mt) { return (1 + kDoneGroups) * kCtrlLineInts + mt; }
 __device__ __forceinline__ int ctrl_done_word(int group) { return (1 + group) * kCtrlLineInts; }
 
 // Bounded wait for the in-pass T handoff; on expiry the kernel records CTRL_ERROR and
@@ -116,7 +119,9 @@ struct TprojParams {
   const void *A;
   const uint16_t *sA;
   float *tpart;           // [parts, M, 32] FP32 partial sums
-  int M, K, MT, parts;
+  float *tfinal;          // [M, 32] FP32 sum over the parts (when `reduce`)
+  int *ctrl;              // control words (arrival counters per M tile)
+  int M, K, MT, parts, reduce;
 };
 
 struct GemmParams {
@@ -144,6 +149,7 @@ struct PackParams {
 // Host-side launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p,
                        int grid_x, int grid_y, hipStream_t s);
+hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s);
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
 hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
@@ -153,6 +159,11 @@ hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s);
 
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
-int tproj_parts(int K);                        // K parts of the T projection
+int tproj_parts(int M, int K);                 // K parts of the T projection
+int gemv_rows_mr(int M);                       // rows per workgroup of the small-M path
+// largest M of the small-M path: measured crossover against the MFMA GEMM on the workload
+// weights (the small-M path wins up to M = 8 on all of them, the GEMM from M = 12)
+constexpr int kSmallM = 8;
+constexpr int kRowsMaxM = 16;                  // largest M the multi-row GEMV takes (forced path)
 
 }  // namespace mnb

@@ -413,7 +413,7 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       tv = tfin[lane & 31];
     } else {
       // T from the T-projection launch: FP32 partials per K-part, added in part order
-      tv = sum_parts<4>(p.tin + (size_t)m * kRank + (lane & 31), (size_t)p.tmpad * kRank, p.tparts);
+      tv = sum_parts<8>(p.tin + (size_t)m * kRank + (lane & 31), (size_t)p.tmpad * kRank, p.tparts);
     }
 #pragma unroll
     for (int r = 0; r < kRank; ++r) {

@@ -18,13 +18,15 @@
 namespace mnb {
 namespace {
 
-constexpr int kKP = 1024;             // K per part
-constexpr int kStepsPerWave = kKP / 4 / 16;
-constexpr int kLdA = kKP + 8;         // halfs per transposed A row (pad keeps lanes on distinct banks)
-
-template <int KIND>  // 1: F16 A, 2: INT8 A with block-32 fp16 scales
+// KIND 1: F16 A, 2: INT8 A with block-32 fp16 scales; KP: K per part (1024, or 256 when
+// the M tiles alone would leave most CUs idle)
+template <int KIND, int KP>
 __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
-  __shared__ __attribute__((aligned(16))) _Float16 sAT[kRank * kLdA];   // 66 KB
+  constexpr int kKP = KP;
+  constexpr int kStepsPerWave = kKP / 4 / 16;
+  constexpr int kLdA = kKP + 8;       // halfs per transposed A row (pad keeps lanes on distinct banks)
+  static_assert(kRank * kLdA * 2 >= 4 * 1024 * 4, "the cross-wave sum reuses the A buffer");
+  __shared__ __attribute__((aligned(16))) _Float16 sAT[kRank * kLdA];   // 66 KB at KP = 1024
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -136,16 +138,58 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
     const int m = mt * 32 + e / kRank;
     if (m < p.M) p.tpart[((size_t)part * p.M + m) * kRank + (e % kRank)] = sum;
   }
+  if (!p.reduce) return;
+  // The workgroup that counts itself last for this M tile adds the parts in part order
+  // (the order is fixed, so the sum does not depend on which workgroup arrives last) and
+  // writes T once; it resets the counter for the next call.
+  __shared__ int last;
+  fence_release();
+  __syncthreads();
+  if (tid == 0) last = atomic_add_agent(&p.ctrl[ctrl_tproj_word(mt)], 1) == p.parts - 1;
+  __syncthreads();
+  if (!last) return;
+  fence_acquire();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + 256 * q;
+    const int m = mt * 32 + e / kRank;
+    if (m < p.M) {
+      const float *src = p.tpart + (size_t)m * kRank + (e % kRank);
+      float v[4];
+      float t = 0.f;
+      int pp = 0;
+      for (; pp + 4 <= p.parts; pp += 4) {     // four loads in flight, added in order
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = src[(size_t)(pp + u) * p.M * kRank];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t += v[u];
+      }
+      for (; pp < p.parts; ++pp) t += src[(size_t)pp * p.M * kRank];
+      p.tfinal[(size_t)m * kRank + (e % kRank)] = t;
+    }
+  }
+  if (tid == 0) atomic_store_agent(&p.ctrl[ctrl_tproj_word(mt)], 0);
 }
 
 }  // namespace
 
-int tproj_parts(int K) { return (K + kKP - 1) / kKP; }
+// K per part: 1024, or 256 when 1024-k parts would give fewer than 128 workgroups (small M)
+int tproj_kp(int M, int K) { return ((M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024; }
+int tproj_parts(int M, int K) {
+  const int kp = tproj_kp(M, K);
+  return (K + kp - 1) / kp;
+}
 
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s) {
   const int grid = p.MT * p.parts;
-  if (lora == 1) hipLaunchKernelGGL(tproj_kernel<1>, dim3(grid), dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(tproj_kernel<2>, dim3(grid), dim3(256), 0, s, p);
+  const bool small = tproj_kp(p.M, p.K) == 256;
+  if (lora == 1) {
+    if (small) hipLaunchKernelGGL((tproj_kernel<1, 256>), dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((tproj_kernel<1, 1024>), dim3(grid), dim3(256), 0, s, p);
+  } else {
+    if (small) hipLaunchKernelGGL((tproj_kernel<2, 256>), dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((tproj_kernel<2, 1024>), dim3(grid), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

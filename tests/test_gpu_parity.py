@@ -158,7 +158,7 @@ def test_cfg5_batched_prefill_q8():
 # ------------------------------------------------------------------------------------------
 
 SHAPES = [(1, 64, 32), (1, 100, 96), (1, 1, 32), (3, 130, 160), (7, 32, 64), (2, 200, 1024), (129, 257, 320),
-          (256, 384, 512), (1, 4096, 4096)]
+          (256, 384, 512), (1, 4096, 4096), (16, 96, 256), (9, 70, 192), (5, 513, 128), (17, 64, 96)]
 
 
 @pytest.mark.parametrize("bits", [4, 8])
