@@ -57,6 +57,17 @@ __device__ __forceinline__ void atomic_store_agent(int *p, int v) {
 __device__ __forceinline__ h2_t nib_pair(uint32_t w, int i) {
   return as_h2(((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
 }
+// (x & mask) | (c & ~mask) in one v_bfi_b32 (the compiler splits the folded form into two)
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t c) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(x), "v"(c));
+  return d;
+}
+// Shift-free variant for 4-bit words: nibbles 0 and 2 of each half (after a shift by 8 for
+// 2) sit in mantissa bits 0-3, giving 1024 + q; nibbles 1 and 3 are taken in place at
+// bits 4-7, giving 1024 + 16 q, whose difference with 1024 + 16 z is 16 (q - z), exact.
+__device__ __forceinline__ h2_t nib_lo(uint32_t w) { return as_h2(bfi(0x000F000Fu, w, 0x64006400u)); }
+__device__ __forceinline__ h2_t nib_hi16(uint32_t w) { return as_h2(bfi(0x00F000F0u, w, 0x64006400u)); }
 // Same for two 8-bit codes (bytes b0, b1 of w -> halves), via v_perm_b32 with the
 // constant byte 0x64 taken from the first operand.
 __device__ __forceinline__ h2_t byte_pair_lo(uint32_t w) {

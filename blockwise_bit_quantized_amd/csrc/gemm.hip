@@ -71,13 +71,6 @@ __device__ __forceinline__ void dma(const void *src, uint8_t *dst, int size) {
   else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
 }
 
-// (x & mask) | (c & ~mask) in one v_bfi_b32 (the compiler splits the folded form into two)
-__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t c) {
-  uint32_t d;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(mask), "v"(x), "v"(c));
-  return d;
-}
-
 // s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits 3:0 and 15:14), other counters free
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -366,19 +366,22 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
         const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xs[wave][(i * Q + qi) * KPC]);
         uint32_t z = 1u << (BITS - 1);
         if constexpr (HAS_ZP) z = BITS == 4 ? (zraw[i] >> ((row & 1) * 4)) & 0xFu : zraw[i];
-        const _Float16 zz = (_Float16)(float)(1024u + z);   // exact: 1024 + z < 2048
-        const h2_t zz2 = {zz, zz};
+        const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);   // 1024 + z, both halves
         float p0 = 0.f, p1 = 0.f;
         if constexpr (BITS == 4) {
+          // pairs 1 and 3 come out as 16 (q - z) (nib_hi16): p1 holds 16x its terms, which
+          // the power-of-two rescale below undoes exactly
+          const h2_t zz16 = as_h2((z * 0x00100010u) | 0x64006400u);   // 1024 + 16 z
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const u4_t xv = *reinterpret_cast<const u4_t *>(xw + 4 * j);
-            const uint32_t w = cw[i][j];
-            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 0) - zz2, as_h2(xv[0]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 1) - zz2, as_h2(xv[1]), p1, false);
-            p0 = __builtin_amdgcn_fdot2(nib_pair(w, 2) - zz2, as_h2(xv[2]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_pair(w, 3) - zz2, as_h2(xv[3]), p1, false);
+            const uint32_t w = cw[i][j], w8 = w >> 8;
+            p0 = __builtin_amdgcn_fdot2(nib_lo(w) - zz2, as_h2(xv[0]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_hi16(w) - zz16, as_h2(xv[1]), p1, false);
+            p0 = __builtin_amdgcn_fdot2(nib_lo(w8) - zz2, as_h2(xv[2]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_hi16(w8) - zz16, as_h2(xv[3]), p1, false);
           }
+          p1 *= 0.0625f;
         } else {
 #pragma unroll
           for (int j = 0; j < 4; j += 2) {
