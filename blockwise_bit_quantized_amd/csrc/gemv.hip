@@ -23,8 +23,8 @@
 //    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
 //    where the tag identifies this call (a per-call epoch kept in the workspace, never 0),
 //    into kTReplicas copies, so that the readers spread over many lines.  Each row
-//    workgroup has one extra wave that carries no weight loads: it polls the first word of
-//    every slice in its copy (one lane per slice), then reads all the words, accepts them
+//    workgroup has one extra wave that carries no weight loads: it polls one word of its
+//    copy (the last slice's first word), then reads all the words, accepts them
 //    when every tag matches (no fences: the tags make a stale or early read detectable),
 //    adds the slices in slice order and leaves T in LDS for the epilogue.  The slice
 //    workgroups are dispatched first and never wait, so every bounded wait ends.  Row
@@ -256,14 +256,16 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
       const unsigned long long *rep = p.tword + (size_t)(bid % kTReplicas) * p.gt * kRank;
-      // hint: one lane per slice (the first 64) polls the slice's first word
+      // hint: one lane polls the first word of the last slice (dispatched last, so as a
+      // rule done last); the gather below checks every tag anyway.  A single word per
+      // poll keeps the uncached polling traffic of hundreds of workgroups small.
       int spins = 0;
       for (; spins < kSpinLimit; ++spins) {
-        const bool seen = lane >= p.gt ||
-                          (uint32_t)(__hip_atomic_load(rep + (size_t)lane * kRank, __ATOMIC_RELAXED,
+        const bool seen = lane != 0 ||
+                          (uint32_t)(__hip_atomic_load(rep + (size_t)(p.gt - 1) * kRank, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT) >> 32) == tag;
         if (__all(seen)) break;
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(8);
       }
       float tv = 0.f;
       bool ok = false;
