@@ -8,7 +8,8 @@ Importing this package fails if ``libmnb.so`` has not been built (there is no fa
 
 Operation (onnxruntime PR #33370 "[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits";
 PR #33800 "Fuse DQ->MatMulNBits for shared initializers and skip outer-scope weights"):
-    Y[M,N] = X[M,K] . deq(W)^T + (X . A) . B,   deq(W)[n,k] = (q[n,k] - z[n,k/32]) * s[n,k/32]
+    Y[M,N] = X[M,K] . deq(W)^T + (X . A) . B [+ bias[N]],
+    deq(W)[n,k] = (q[n,k] - z[n,k/32]) * s[n,k/32]
 """
 from __future__ import annotations
 
@@ -69,12 +70,14 @@ def _load() -> C.CDLL:
     lib.mnb_matmul.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P]
     lib.mnb_matmul_ex.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P,
                                   C.POINTER(mnb_options)]
+    lib.mnb_matmul_bias.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, P, I, I, I, I, I, P, S, P,
+                                    C.POINTER(mnb_options)]
     lib.mnb_describe_route.argtypes = [I, I, I, I, I, I, C.POINTER(mnb_options), C.c_char_p, S]
     lib.mnb_status_string.argtypes = [I]
     lib.mnb_status_string.restype = C.c_char_p
     lib.mnb_version.argtypes = []
     for f in ("mnb_packed_sizes", "mnb_pack", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
-              "mnb_describe_route", "mnb_version"):
+              "mnb_matmul_bias", "mnb_describe_route", "mnb_version"):
         getattr(lib, f).restype = I
     return lib
 
@@ -120,6 +123,13 @@ def mnb_matmul(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes,
 def mnb_matmul_ex(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream, opt) -> int:
     return lib.mnb_matmul_ex(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, Y, M, N, K, bits,
                              block, workspace, ws_bytes, stream, C.byref(opt) if opt is not None else None)
+
+
+def mnb_matmul_bias(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, workspace, ws_bytes, stream,
+                    opt) -> int:
+    return lib.mnb_matmul_bias(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, bias, Y, M, N, K,
+                               bits, block, workspace, ws_bytes, stream,
+                               C.byref(opt) if opt is not None else None)
 
 
 def mnb_describe_route(M, N, K, bits, has_zp, adapter_kind, opt=None):
@@ -214,8 +224,9 @@ def workspace(dev, nbytes: int):
 
 
 def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
-           flags: int = 0, out=None, ws=None):
-    """Y = X . deq(W)^T (+ (X.A).B) for a device fp16 X [M, K]; returns fp16 Y [M, N]."""
+           flags: int = 0, out=None, ws=None, bias=None):
+    """Y = X . deq(W)^T (+ (X.A).B) (+ bias) for a device fp16 X [M, K] and an optional fp16
+    bias [N]; returns fp16 Y [M, N]."""
     import torch
     M, K = X.shape
     if K != pw.K:
@@ -227,6 +238,6 @@ def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_
         ws = workspace(dev, need)
     ad = adapter.struct() if adapter is not None else None
     opt = mnb_options(path, flags)
-    _check(mnb_matmul_ex(_ptr(X), _ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), ad, _ptr(Y), M, pw.N, K, pw.bits,
-                         32, _ptr(ws), ws.numel(), _stream(dev), opt))
+    _check(mnb_matmul_bias(_ptr(X), _ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), ad, _ptr(bias), _ptr(Y), M,
+                           pw.N, K, pw.bits, 32, _ptr(ws), ws.numel(), _stream(dev), opt))
     return Y

@@ -103,8 +103,8 @@ int check_common(int M, int N, int K, int bits, int block) {
 }
 
 int validate(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad,
-             const void *Y, int M, int N, int K, int bits, int block, const void *ws, size_t ws_bytes,
-             const mnb_options *opt) {
+             const void *bias, const void *Y, int M, int N, int K, int bits, int block, const void *ws,
+             size_t ws_bytes, const mnb_options *opt) {
   int st = check_common(M, N, K, bits, block);
   if (st) return st;
   if (opt) {
@@ -120,7 +120,8 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
   if (M == 0 || N == 0) return MNB_OK;
   if (!Y) return MNB_ERR_INVALID_ARG;
   if (K > 0 && (!X || !wq || !sc)) return MNB_ERR_INVALID_ARG;
-  if (misaligned(X) || misaligned(wq) || misaligned(sc) || misaligned(zpp) || misaligned(Y) || misaligned(ws))
+  if (misaligned(X) || misaligned(wq) || misaligned(sc) || misaligned(zpp) || misaligned(Y) || misaligned(ws) ||
+      misaligned(bias))
     return MNB_ERR_MISALIGNED;
   if (lora && (misaligned(ad->A) || misaligned(ad->B) || misaligned(ad->A_scales) || misaligned(ad->B_scales)))
     return MNB_ERR_MISALIGNED;
@@ -135,7 +136,8 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
                  {lora ? ad->A : nullptr, (size_t)K * kRank * (lora == LORA_F16 ? 2 : 1)},
                  {lora ? ad->B : nullptr, (size_t)kRank * N * (lora == LORA_F16 ? 2 : 1)},
                  {lora == LORA_Q8 ? ad->A_scales : nullptr, (size_t)(K / kBlock) * kRank * 2},
-                 {lora == LORA_Q8 ? ad->B_scales : nullptr, (size_t)N * 2}};
+                 {lora == LORA_Q8 ? ad->B_scales : nullptr, (size_t)N * 2},
+                 {bias, (size_t)N * 2}};
   for (const Range &r : ins)
     if (overlap(Y, ybytes, r)) return MNB_ERR_ALIAS;
   return MNB_OK;
@@ -177,7 +179,7 @@ bool log_enabled() {
 
 extern "C" {
 
-int mnb_version(void) { return 100; }
+int mnb_version(void) { return 101; }
 
 const char *mnb_status_string(int status) {
   switch (status) {
@@ -253,7 +255,7 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
     return MNB_OK;
   }
   if (K == 0) {
-    snprintf(buf, buf_len, "fill_zero");
+    snprintf(buf, buf_len, "fill");
     return MNB_OK;
   }
   describe(buf, buf_len, M, N, K, bits, has_zp, route(M, has_adapter_kind, opt));
@@ -263,12 +265,19 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
 int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad, void *Y,
                   int M, int N, int K, int bits, int block, void *workspace, size_t ws_bytes, void *stream,
                   const mnb_options *opt) {
-  int st = validate(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, opt);
+  return mnb_matmul_bias(X, wq, sc, zpp, ad, nullptr, Y, M, N, K, bits, block, workspace, ws_bytes, stream, opt);
+}
+
+int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad,
+                    const void *bias, void *Y, int M, int N, int K, int bits, int block, void *workspace,
+                    size_t ws_bytes, void *stream, const mnb_options *opt) {
+  int st = validate(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, workspace, ws_bytes, opt);
   if (st) return st;
   if (M == 0 || N == 0) return MNB_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t *Yh = static_cast<uint16_t *>(Y);
-  if (K == 0) return launch_fill_zero(Yh, (long)M * N, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+  const uint16_t *bh = static_cast<const uint16_t *>(bias);
+  if (K == 0) return launch_fill(Yh, bh, M, N, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
 
   const int lora = effective_lora(ad);
   const Route r = route(M, lora, opt);
@@ -314,6 +323,7 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
       p.sB = static_cast<const uint16_t *>(ad->B_scales);
     }
     p.Y = Yh;
+    p.bias = bh;
     p.N = N;
     p.K = K;
     p.NG = NG;
@@ -361,6 +371,7 @@ int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp
   }
   g.tpart = tproj_out;
   g.tparts = tparts;
+  g.bias = bh;
   g.Y = Yh;
   g.M = M;
   g.N = N;

@@ -113,6 +113,7 @@ struct GemvParams {
   const void *B;
   const uint16_t *sB;
   uint16_t *Y;            // [M, N]
+  const uint16_t *bias;   // fp16 [N] broadcast bias or null
   int M, N, K, NG, KB;
   int q;                  // chunk-columns per wave load; a workgroup owns 64/q rows
   int gt;                 // in-pass T: number of T-slice workgroups (first in the grid)
@@ -144,6 +145,7 @@ struct GemmParams {
   const uint16_t *sB;
   const float *tpart;     // T partials [tparts, M, 32]
   uint16_t *Y;
+  const uint16_t *bias;   // fp16 [N] broadcast bias or null
   int M, N, K, NG, KB, MT, NT, tparts;
 };
 
@@ -166,7 +168,7 @@ hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hip
 hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
                          uint8_t *zp, hipStream_t s);
-hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s);
+hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStream_t s);
 
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8

@@ -466,6 +466,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // n = 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per register
   // quad, stored as one 8-byte vector
   const bool vec = (p.N & 3) == 0;
+  // broadcast bias of this lane's columns, added in FP32 before the rounding
+  float bv[2][4][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi + e;
+        bv[nb][j][e] = (p.bias && n < p.N) ? h2f(p.bias[n]) : 0.f;
+      }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int m = m0 + mb * 32 + l32;
@@ -476,8 +487,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi;
-        const h2_t lo = {(_Float16)acc[mb][nb][4 * j], (_Float16)acc[mb][nb][4 * j + 1]};
-        const h2_t hi2 = {(_Float16)acc[mb][nb][4 * j + 2], (_Float16)acc[mb][nb][4 * j + 3]};
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = p.bias ? acc[mb][nb][4 * j + e] + bv[nb][j][e] : acc[mb][nb][4 * j + e];
+        const h2_t lo = {(_Float16)y[0], (_Float16)y[1]};
+        const h2_t hi2 = {(_Float16)y[2], (_Float16)y[3]};
         if (vec && n + 4 <= p.N) {
           *reinterpret_cast<u2_t *>(yrow + n) = u2_t{as_u32(lo), as_u32(hi2)};
         } else {

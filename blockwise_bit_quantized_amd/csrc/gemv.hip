@@ -431,8 +431,9 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
     if constexpr (LORA == LORA_Q8) lora *= bscale;
   }
   if (active) {
-    const _Float16 y = (_Float16)(total + lora);
-    p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, y);
+    float y = total + lora;
+    if (p.bias) y += h2f(p.bias[n]);
+    p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
   }
 }
 

@@ -202,7 +202,9 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
       }
       lsum *= bscale;
     }
-    if (active) p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)(total + lsum));
+    float y = total + lsum;
+    if (p.bias && active) y += h2f(p.bias[n]);
+    if (active) p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
   }
 }
 

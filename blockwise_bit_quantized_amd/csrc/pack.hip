@@ -5,6 +5,8 @@
 // PR #33800 ("Fuse DQ->MatMulNBits for shared initializers and skip outer-scope weights",
 // Description): it reads already-quantized codes, block scales and zero points once and
 // writes the layout the matmul kernels stream.  One thread per (group, block, row).
+#include <algorithm>
+
 #include "common.h"
 
 namespace mnb {
@@ -101,11 +103,16 @@ __global__ __launch_bounds__(256) void unpack_kernel(PackParams p, uint8_t *code
   }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t *Y, long n) {
+// Y[m, n] = bias[n], or 0 without a bias (K == 0: empty packed weights)
+__global__ __launch_bounds__(256) void fill_kernel(uint16_t *Y, const uint16_t *bias, long n, int N) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  const long nv = n / 8;
-  if (i < nv) reinterpret_cast<u4_t *>(Y)[i] = u4_t{0u, 0u, 0u, 0u};
-  if (i < n - nv * 8) Y[nv * 8 + i] = 0;
+  if (!bias) {
+    const long nv = n / 8;
+    if (i < nv) reinterpret_cast<u4_t *>(Y)[i] = u4_t{0u, 0u, 0u, 0u};
+    if (i < n - nv * 8) Y[nv * 8 + i] = 0;
+    return;
+  }
+  for (long e = i; e < n; e += (long)gridDim.x * 256) Y[e] = bias[e % N];
 }
 
 }  // namespace
@@ -129,10 +136,11 @@ hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(uint16_t *Y, long n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const long work = n / 8 > 8 ? n / 8 : 8;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, Y, n);
+hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStream_t s) {
+  const long n = (long)M * N;
+  const long work = bias ? std::min<long>(n, 1L << 22) : std::max<long>(n / 8, n % 8);
+  if (work == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, Y, bias, n, N);
   return hipGetLastError();
 }
 

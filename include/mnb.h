@@ -146,8 +146,10 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank);
  *   bits 4 or 8, block 32, K % 32 == 0
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
- * Path (PR #33370 commit list, auto mode): M == 1 runs the decode GEMV, M > 1 the T
- * projection followed by the MFMA GEMM with the LoRA term in its epilogue.
+ * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV
+ * with T computed in the same launch; 2 <= M <= 8 the T projection, then a GEMV that
+ * streams the weights once for all rows; M > 8 the T projection, then the MFMA GEMM with
+ * the LoRA term in its epilogue.
  */
 int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp,
                const mnb_adapter *ad, void *Y, int M, int N, int K, int bits, int block,
@@ -157,6 +159,19 @@ int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp,
 int mnb_matmul_ex(const void *X, const void *wq, const void *sc, const void *zpp,
                   const mnb_adapter *ad, void *Y, int M, int N, int K, int bits, int block,
                   void *workspace, size_t ws_bytes, void *stream, const mnb_options *opt);
+
+/*
+ * mnb_matmul_ex plus MatMulNBits' optional broadcast bias: Y[m,n] = ... + bias[n], added in
+ * FP32 before the single rounding.  bias: fp16 [N] on the device, 16-byte aligned, or NULL
+ * (then identical to mnb_matmul_ex); it must not overlap Y (MNB_ERR_ALIAS).  With K == 0
+ * (empty packed weights) Y is the broadcast bias, or zeros without one (the PR #33370
+ * page, commit list: empty packed weights keep the logical output shape and give zeros or
+ * the broadcast bias).
+ */
+int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *zpp,
+                    const mnb_adapter *ad, const void *bias, void *Y, int M, int N, int K,
+                    int bits, int block, void *workspace, size_t ws_bytes, void *stream,
+                    const mnb_options *opt);
 
 /*
  * Describe, without any device call, the kernels mnb_matmul_ex would launch for these
@@ -170,7 +185,7 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
 /* Static text for a status code. */
 const char *mnb_status_string(int status);
 
-/* ABI version (major * 100 + minor). */
+/* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias. */
 int mnb_version(void);
 
 #ifdef __cplusplus

@@ -23,10 +23,11 @@ def load(path: str | None = None) -> C.CDLL:
     path = path or _build.LIB
     if path in _libs:
         return _libs[path]
-    if path == _build.LIB and not os.path.exists(path):
-        _build.build()
+    if path == _build.LIB and (not os.path.exists(path) or
+                               os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
+        _build.build()          # absent, or older than its source (a CPU build of seconds)
     lib = C.CDLL(path)
-    lib.mnbo_matmul.argtypes = [C.c_int] * 4 + [_P] * 4 + [C.c_int, C.c_int] + [_P] * 5
+    lib.mnbo_matmul.argtypes = [C.c_int] * 4 + [_P] * 4 + [C.c_int, C.c_int] + [_P] * 6
     lib.mnbo_matmul.restype = C.c_int
     lib.mnbo_pack.argtypes = [C.c_int] * 3 + [_P] * 6
     lib.mnbo_pack.restype = C.c_int
@@ -85,9 +86,10 @@ def matmul(case: dict, lib=None) -> np.ndarray:
             A = None
         if ad.get("B_null"):
             B = None
+    bias = _c(case.get("bias"), np.uint16)
     Y = np.zeros((M, N), np.float64)
     rc = lib.mnbo_matmul(M, N, K, bits, _ptr(X), _ptr(codes), _ptr(scales), _ptr(zp), kind, rank,
-                         _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(Y))
+                         _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(bias), _ptr(Y))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return Y

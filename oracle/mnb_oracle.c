@@ -162,7 +162,8 @@ static double lora_b(int kind, const void *B, const uint16_t *sB, int N, int r, 
  */
 int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t *codes,
                 const uint16_t *scales, const uint8_t *zp, int kind, int rank, const void *A,
-                const uint16_t *A_scales, const void *B, const uint16_t *B_scales, double *Y) {
+                const uint16_t *A_scales, const void *B, const uint16_t *B_scales,
+                const uint16_t *bias, double *Y) {
   if (M < 0 || N < 0 || K < 0 || K % BLK) return -1;
   if (bits != 4 && bits != 8) return -1;
   int has_lora = kind != 0 && rank != 0 && A != NULL && B != NULL;
@@ -226,6 +227,18 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
     free(b);
     free(t);
   }
+
+  /* step 5: Y[m, n] += bias[n], the optional broadcast bias of MatMulNBits (the PR #33370
+     page, commit list: empty packed weights give zeros or the broadcast bias) */
+  if (bias != NULL)
+    for (int m = 0; m < M; ++m)
+      for (int n = 0; n < N; ++n) {
+#if MNBO_MUTATION == 11
+        Y[(long)m * N + n] += h2d(bias[m % N]);       /* planted: bias indexed by the row */
+#else
+        Y[(long)m * N + n] += h2d(bias[n]);
+#endif
+      }
   free(x);
   free(w);
   return 0;

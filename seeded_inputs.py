@@ -142,7 +142,7 @@ def make_config(cfg: int, M: int | None = None, adapter: str | None | bool = Tru
 
 
 def make_random(seed: int, M: int, N: int, K: int, bits: int, with_zp: bool, adapter=None,
-                s_lo=None, s_hi=None, x_std=1.0):
+                s_lo=None, s_hi=None, x_std=1.0, bias=False):
     """Generic seeded case for tests (shapes not tied to a workload).  Scales default to the
     decode/prefill range U[0.001, 0.02] for 4-bit and the lm_head range U[1e-4, 4e-3] for
     8-bit weights; for 8-bit with K > 576 the range shrinks by sqrt(576/K) so that the
@@ -167,4 +167,7 @@ def make_random(seed: int, M: int, N: int, K: int, bits: int, with_zp: bool, ada
         qa, sa = quantize_q8_blocks(a_f, 0)
         qb, sb = quantize_q8_blocks(b_f, 0)
         ad = dict(kind="q8", A=qa, A_scales=sa, B=qb, B_scales=sb)
-    return dict(M=M, N=N, K=K, bits=bits, X=X, codes=codes, scales=scales, zp=zp, adapter=ad)
+    case = dict(M=M, N=N, K=K, bits=bits, X=X, codes=codes, scales=scales, zp=zp, adapter=ad)
+    if bias:   # broadcast bias fp16 [N] ~ N(0, 0.5), drawn after everything else
+        case["bias"] = normal_f16(r, (N,), std=0.5)
+    return case

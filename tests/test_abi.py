@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert mnb.mnb_version() == 100
+    assert mnb.mnb_version() == 101
     for st in range(7):
         assert mnb.mnb_status_string(st).startswith("MNB_")
     assert "unknown" in mnb.mnb_status_string(99)
@@ -105,6 +105,20 @@ def test_validation_status_codes():
     assert call(y=B, ad=mnb.mnb_adapter(1, 32, A, None, B, None)) == E.MNB_ERR_ALIAS
 
 
+BIAS = BASE * 9
+
+
+def call_bias(bias=BIAS, y=Y, M=1, N=64, K=64, ws=WS):
+    return mnb.mnb_matmul_bias(X, WQ, SC, ZP, None, bias, y, M, N, K, 4, 32, ws, 1 << 30, None, None)
+
+
+def test_bias_validation_status_codes():
+    assert call_bias(bias=BIAS + 2) == mnb.MNB_ERR_MISALIGNED
+    assert call_bias(bias=BIAS + 8) == mnb.MNB_ERR_MISALIGNED
+    assert call_bias(y=BIAS) == mnb.MNB_ERR_ALIAS                  # Y over the bias
+    assert call_bias(bias=Y + 64) == mnb.MNB_ERR_ALIAS             # bias inside Y [1, 64]
+
+
 def test_degenerate_sizes_enqueue_nothing():
     # M == 0 or N == 0 returns before any device call, even with NULL tensors
     assert call(M=0, x=None, y=None, wq=None, sc=None, ws=None) == 0
@@ -144,7 +158,7 @@ def test_dispatcher_rule():
     assert route(7, path=1).startswith("tproj_f16") and "gemv_rows_b4_zpx_f16" in route(7, path=1)
     assert route(40, path=1).startswith("tproj_f16") and "gemv_b4_zpx_f16_tprecomp" in route(40, path=1)
     assert "tprecomp" in route(1, flags=1) and route(1, flags=1).startswith("tproj")
-    assert route(0) == "noop" and route(3, K=0) == "fill_zero"
+    assert route(0) == "noop" and route(3, K=0) == "fill"
 
 
 def test_gemv_grid_covers_the_chip():

@@ -55,7 +55,8 @@ def run(case, path=0, flags=0, pw=None, ad="case", X=None):
     pw = pw or dev_weight(case)
     a = dev_adapter(case.get("adapter")) if ad == "case" else ad
     Xd = t16(case["X"]) if X is None else X
-    Y = mnb.matmul(Xd, pw, a, path=path, flags=flags)
+    bias = t16(case["bias"]) if case.get("bias") is not None else None
+    Y = mnb.matmul(Xd, pw, a, path=path, flags=flags, bias=bias)
     torch.cuda.synchronize()
     return Y.cpu().numpy().view(np.uint16)
 
@@ -190,7 +191,7 @@ def test_one_hot_bit_exact(bits, zp):
         assert same_bits(run(c, path, flags, pw=pw), want), name
 
 
-def exact_case(seed, M, N, K, bits, zp, kind):
+def exact_case(seed, M, N, K, bits, zp, kind, bias=False):
     """Inputs whose every product and partial sum is exact in FP32 (P-e)."""
     r = np.random.default_rng(seed)
     X = np.zeros((M, K), np.float16)
@@ -210,8 +211,9 @@ def exact_case(seed, M, N, K, bits, zp, kind):
                   A_scales=np.full((K // 32, 32), 0x3400, np.uint16),       # 2^-2
                   B=r.integers(-3, 4, size=(32, N)).astype(np.int8),
                   B_scales=np.full((1, N), 0x3400, np.uint16))
+    b = si.to_f16_bits(r.integers(-64, 65, size=N) * 0.125) if bias else None
     return dict(M=M, N=N, K=K, bits=bits, X=X.view(np.uint16), codes=codes, scales=scales,
-                zp=z.astype(np.uint8) if zp else None, adapter=ad)
+                zp=z.astype(np.uint8) if zp else None, adapter=ad, bias=b)
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -223,6 +225,55 @@ def test_exact_arithmetic_bit_exact(bits, kind, M):
     pw = dev_weight(case)
     for path, flags, name in PATHS:
         assert same_bits(run(case, path, flags, pw=pw), want), name
+
+
+@pytest.mark.parametrize("kind", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+@pytest.mark.parametrize("M", [1, 6, 16, 130])
+def test_exact_arithmetic_with_bias_bit_exact(kind, M):
+    """Bias multiples of 2^-3 keep every sum exact: each output is the exact value rounded once."""
+    for bits in (4, 8):
+        case = exact_case(170 + M + bits, M, 200, 320, bits, bits == 4, kind, bias=True)
+        want = oracle.f64_to_f16(oracle.matmul(case))
+        pw = dev_weight(case)
+        for path, flags, name in PATHS:
+            assert same_bits(run(case, path, flags, pw=pw), want), "%s bits=%d" % (name, bits)
+
+
+BIAS_SHAPES = [(1, 64, 32), (1, 100, 96), (3, 130, 160), (8, 257, 320), (13, 96, 256), (16, 70, 192),
+               (129, 257, 320), (1, 4096, 2048)]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_bias_small_shapes_all_paths(bits, adapter):
+    for i, (M, N, K) in enumerate(BIAS_SHAPES):
+        case = si.make_random(150 + i, M, N, K, bits, i % 2 == 0, adapter, bias=True)
+        ref = oracle.matmul(case)
+        pw = dev_weight(case)
+        for path, flags, name in PATHS:
+            compare(run(case, path, flags, pw=pw), ref, what="bias %s M=%d N=%d K=%d" % (name, M, N, K))
+
+
+def test_empty_weights_give_broadcast_bias():
+    """K == 0: Y is the bias broadcast over rows, bit for bit, on every path; without a
+    bias it is zeros (empty packed weights keep the output shape)."""
+    for M, N in [(1, 1), (3, 70), (5, 4099), (64, 1000)]:
+        case = si.make_random(160 + M, M, N, 32, 4, False, None, bias=True)
+        bias = t16(case["bias"])
+        X = torch.zeros((M, 0), dtype=torch.float16, device=DEV)
+        pw = mnb.PackedWeight(torch.zeros(16, dtype=torch.uint8, device=DEV),
+                              torch.zeros(8, dtype=torch.float16, device=DEV), None, N, 0, 4)
+        want = np.broadcast_to(case["bias"], (M, N))
+        empty = dict(case, K=0, X=np.zeros((M, 0), np.uint16), codes=np.zeros((N, 0), np.uint8),
+                     scales=np.zeros((N, 0), np.uint16))
+        assert same_bits(oracle.f64_to_f16(oracle.matmul(empty)), want)
+        for path, flags, name in PATHS:
+            Y = mnb.matmul(X, pw, None, path=path, flags=flags, bias=bias)
+            torch.cuda.synchronize()
+            assert same_bits(Y.cpu().numpy().view(np.uint16), want), "%s M=%d N=%d" % (name, M, N)
+            Y = mnb.matmul(X, pw, None, path=path, flags=flags)
+            torch.cuda.synchronize()
+            assert bool((Y == 0).all()), name
 
 
 @pytest.mark.parametrize("M", [1, 64])
@@ -297,3 +348,29 @@ def test_determinism_and_workspace_reuse():
     for c, y0 in zip(cases, first):
         rows = list(range(c["M"])) if c["M"] <= 8 else [0, 5, c["M"] - 1]
         compare(y0[rows], oracle.matmul(rows_case(c, rows)), what="reuse %s" % (c["M"],))
+
+
+def test_workspace_counters_return_to_zero():
+    """The in-pass T handoff and the T projection's part reduction leave every counter of
+    the workspace's control area at zero, never set the error word, and advance the epoch
+    once per in-pass call."""
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    cases = [si.make_random(130, 1, 4096, 2048, 4, False, "f16"),      # in-pass T
+             si.make_random(131, 4, 1000, 4096, 4, True, "q8"),        # small M: T reduced in the projection
+             si.make_random(132, 2, 640, 9216, 8, False, "f16"),       # more than 4 T parts
+             si.make_random(133, 1, 896, 896, 8, True, "q8")]          # in-pass T again
+    inpass = 0
+    for rep in range(3):
+        for c in cases:
+            pw = dev_weight(c)
+            a = dev_adapter(c["adapter"])
+            Y = torch.empty((c["M"], c["N"]), dtype=torch.float16, device=DEV)
+            mnb.matmul(t16(c["X"]), pw, a, out=Y, ws=ws)
+            inpass += c["M"] == 1
+    torch.cuda.synchronize()
+    ctrl = ws[:8448].cpu().numpy().view(np.int32)
+    epoch, tdone, err = int(ctrl[0]), int(ctrl[1]), int(ctrl[2])
+    assert err == 0 and tdone == 0
+    # epoch: the tag of the last in-pass call, i.e. one past the previous tag per call
+    assert epoch == inpass
+    assert not ctrl[3:].any(), np.nonzero(ctrl[3:])[0][:8] + 3

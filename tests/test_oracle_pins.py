@@ -71,6 +71,11 @@ def exact_result(case) -> list:
         for m in range(M):
             for n in range(N):
                 Y[m][n] += sum(T[m][r] * B[r][n] for r in range(32))
+    if case.get("bias") is not None:
+        bias = [Fraction(float(v)) for v in _f16(case["bias"])]
+        for m in range(M):
+            for n in range(N):
+                Y[m][n] += bias[n]
     return Y
 
 
@@ -109,6 +114,8 @@ def numpy_dq_matmul(case) -> np.ndarray:
     if case.get("adapter") is not None:
         A, B = numpy_adapter(case["adapter"], case["K"], case["N"])
         Y = Y + (X @ A) @ B
+    if case.get("bias") is not None:
+        Y = Y + _f16(case["bias"])[None, :]
     return Y
 
 
@@ -116,22 +123,22 @@ def numpy_dq_matmul(case) -> np.ndarray:
 # pins: each takes the oracle library so the mutation test can run them on planted copies
 # ------------------------------------------------------------------------------------------
 
-TINY = [  # (seed, M, N, K, bits, zp, adapter)
-    (1, 1, 5, 32, 4, True, None),
-    (2, 2, 8, 64, 4, False, "f16"),
-    (3, 3, 7, 64, 8, True, "q8"),
-    (4, 2, 6, 32, 8, False, None),
-    (5, 1, 3, 64, 4, True, "q8"),
-    (6, 2, 4, 32, 4, True, "f16"),
+TINY = [  # (seed, M, N, K, bits, zp, adapter, bias)
+    (1, 1, 5, 32, 4, True, None, False),
+    (2, 2, 8, 64, 4, False, "f16", False),
+    (3, 3, 7, 64, 8, True, "q8", True),
+    (4, 2, 6, 32, 8, False, None, True),
+    (5, 1, 3, 64, 4, True, "q8", False),
+    (6, 2, 4, 32, 4, True, "f16", True),
 ]
 
 
 def pin_exact_bruteforce(lib):
-    for seed, M, N, K, bits, zp, ad in TINY:
-        case = si.make_random(seed, M, N, K, bits, zp, ad)
+    for seed, M, N, K, bits, zp, ad, bias in TINY:
+        case = si.make_random(seed, M, N, K, bits, zp, ad, bias=bias)
         ex = exact_result(case)
         got = oracle.matmul(case, lib)
-        bound = 1e-13 * abs_terms(case) + 1e-300
+        bound = 1e-13 * (abs_terms(case) + (np.abs(_f16(case["bias"]))[None, :] if bias else 0)) + 1e-300
         for m in range(M):
             for n in range(N):
                 err = abs(Fraction(float(got[m, n])) - ex[m][n])
@@ -139,12 +146,30 @@ def pin_exact_bruteforce(lib):
 
 
 def pin_numpy_dq_matmul(lib):
-    for seed, (M, N, K, bits, zp, ad) in enumerate([(3, 70, 96, 4, True, "f16"), (2, 65, 160, 8, True, "q8"),
-                                                    (4, 33, 64, 4, False, "q8"), (1, 130, 128, 8, False, None)]):
-        case = si.make_random(100 + seed, M, N, K, bits, zp, ad)
+    for seed, (M, N, K, bits, zp, ad, bias) in enumerate([(3, 70, 96, 4, True, "f16", False),
+                                                          (2, 65, 160, 8, True, "q8", True),
+                                                          (4, 33, 64, 4, False, "q8", False),
+                                                          (1, 130, 128, 8, False, None, True)]):
+        case = si.make_random(100 + seed, M, N, K, bits, zp, ad, bias=bias)
         got = oracle.matmul(case, lib)
         ref = numpy_dq_matmul(case)
-        assert np.all(np.abs(got - ref) <= 1e-12 * abs_terms(case) + 1e-300), seed
+        scale = abs_terms(case) + (np.abs(_f16(case["bias"]))[None, :] if bias else 0)
+        assert np.all(np.abs(got - ref) <= 1e-12 * scale + 1e-300), seed
+
+
+def pin_empty_weights_bias(lib):
+    """K == 0 (empty packed weights): Y is the broadcast bias exactly, or zeros (PR #33370
+    page, commit list: the output keeps its logical shape and holds zeros or the bias)."""
+    r = np.random.default_rng(9)
+    for M, N, bits in ((3, 5, 4), (1, 70, 8)):
+        bias = r.standard_normal(N).astype(np.float16).view(np.uint16)
+        case = dict(M=M, N=N, K=0, bits=bits, X=np.zeros((M, 0), np.uint16),
+                    codes=np.zeros((N, 0), np.uint8), scales=np.zeros((N, 0), np.uint16), zp=None,
+                    adapter=None, bias=bias)
+        got = oracle.matmul(case, lib)
+        assert np.array_equal(got, np.broadcast_to(_f16(bias), (M, N)))
+        case["bias"] = None
+        assert not oracle.matmul(case, lib).any()
 
 
 def pin_p5_closed_form(lib):
@@ -297,7 +322,8 @@ def pin_pack_roundtrip(lib):
 
 PINS = [pin_exact_bruteforce, pin_numpy_dq_matmul, pin_p5_closed_form, pin_one_hot,
         pin_code_equals_zero_point, pin_empty_and_zero_adapter, pin_superposition,
-        pin_default_zero_point, pin_q8_equals_f16, pin_pack_layout, pin_pack_roundtrip]
+        pin_default_zero_point, pin_q8_equals_f16, pin_pack_layout, pin_pack_roundtrip,
+        pin_empty_weights_bias]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -340,7 +366,7 @@ def test_f16_round_nearest_even():
 MUTATIONS = {1: "zero-point sign", 2: "LoRA term dropped", 3: "scale index transposed",
              4: "block index off by one", 5: "A transposed", 6: "default zero point 0",
              7: "natural nibble order", 8: "X transposed", 9: "B transposed",
-             10: "INT8 A scale ignores rank column"}
+             10: "INT8 A scale ignores rank column", 11: "bias indexed by the row"}
 
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS), ids=lambda m: MUTATIONS[m])
