@@ -31,8 +31,8 @@ constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 // workspace stays valid for calls of any shape), then data regions that need no
 // initialisation.
 struct WsLayout {
-  size_t ctrl, tinpass, tproj, tfinal, total;
-  int gt, tparts, tmt;
+  size_t ctrl, tinpass, tproj, tfinal, ypart, total;
+  int gt, tparts, tmt, splits;
 };
 
 WsLayout ws_layout(int M, int N, int K, int rank) {
@@ -48,6 +48,10 @@ WsLayout ws_layout(int M, int N, int K, int rank) {
   if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
   w.tfinal = off;
   if (rank) off += align_up((size_t)M * kRank * sizeof(float));
+  // prefill GEMM with K split into ranges: FP32 partial outputs [splits, M, N]
+  w.splits = gemm_splits(M, N, K);
+  w.ypart = off;
+  if (w.splits > 1) off += align_up((size_t)w.splits * M * N * sizeof(float));
   w.total = off;
   return w;
 }
@@ -161,8 +165,8 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
     snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
-    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64", tp, bits, has_zp ? "x" : "def", ln,
-             cdiv(M, 128) * cdiv(N, 128));
+    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64 splits=%d", tp, bits, has_zp ? "x" : "def", ln,
+             cdiv(M, 128) * cdiv(N, 128) * w.splits, w.splits);
   }
 }
 
@@ -299,7 +303,11 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   int tparts = w.tparts;
   if (r.tproj) {
+#ifndef MNB_EXP_OLDREDUCE
+    const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && M <= kRowsMaxM;
+#else
     const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && (M <= kRowsMaxM || w.tparts > 4);
+#endif
     TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), tproj_out,
                    reinterpret_cast<float *>(ws + w.tfinal), reinterpret_cast<int *>(ws + w.ctrl),
                    M, K, w.tmt, w.tparts, reduce};
@@ -380,6 +388,8 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   g.KB = KB;
   g.MT = cdiv(M, 128);
   g.NT = cdiv(N, 128);
+  g.splits = w.splits;
+  g.ypart = reinterpret_cast<float *>(ws + w.ypart);
   return launch_gemm(bits, has_zp, lora, g, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
 }
 

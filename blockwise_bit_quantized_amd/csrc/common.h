@@ -146,7 +146,9 @@ struct GemmParams {
   const float *tpart;     // T partials [tparts, M, 32]
   uint16_t *Y;
   const uint16_t *bias;   // fp16 [N] broadcast bias or null
+  float *ypart;           // splits > 1: FP32 partial outputs [splits, M, N]
   int M, N, K, NG, KB, MT, NT, tparts;
+  int splits;             // K ranges per output tile (1: the workgroup stores Y itself)
 };
 
 struct PackParams {
@@ -165,6 +167,8 @@ hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvPar
 hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s);
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
+int gemm_splits(int M, int N, int K);         // K ranges per output tile of the prefill GEMM
+constexpr int kMaxSplits = 16;
 hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
                          uint8_t *zp, hipStream_t s);

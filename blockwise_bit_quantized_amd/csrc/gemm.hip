@@ -99,14 +99,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int kh = wave >> 1;                  // block of the K-step
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // XCD-aware tile order: consecutive workgroup ids go to different XCDs, so give each XCD
-  // a contiguous range of tiles (M fastest) that shares weight columns in its L2.
+  // XCD-aware order: consecutive workgroup ids go to different XCDs, so give each XCD a
+  // contiguous range of (K range, tile) items (M fastest) that shares weight columns in
+  // its L2.
   const int ntiles = p.MT * p.NT;
-  int tile = blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int nwg = ntiles * p.splits;
+  int item = blockIdx.x;
+  if ((nwg & 7) == 0) item = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  const int ks = item / ntiles;              // K range of this workgroup
+  const int tile = item - ks * ntiles;
   const int mt = tile % p.MT, nt = tile / p.MT;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int nsteps = (p.KB + 1) / 2;
+  // K-steps [sbase, sbase + nsteps) of the (KB + 1) / 2; the host picks `splits` so that
+  // every range is non-empty
+  const int tsteps = (p.KB + 1) / 2;
+  const int sps = (tsteps + p.splits - 1) / p.splits;
+  const int sbase = ks * sps;
+  const int nsteps = min(tsteps, sbase + sps) - sbase;
+  // the LoRA term is added once, by the first K range
+  const bool lora_here = LORA != 0 && ks == 0;
 
   const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
   const int wg = (n0 >> 6) + nh;             // packed row group of this wave
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     xhigh[q] = c >= 4;
   }
   auto issue_x = [&](int step, int slot, int half) {
-    const int sv = step < nsteps ? step : nsteps - 1;     // past the end: a valid address
+    const int sv = sbase + (step < nsteps ? step : nsteps - 1);   // past the end: a valid address
     // with an odd block count the last step's second block lies past K: those chunks
     // re-read the first block (any valid address; the block's scales are masked to 0)
     const bool ragged = 2 * sv + 1 >= p.KB;
@@ -138,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     }
   };
   auto issue_w = [&](int step, int slot) {
-    const int sv = step < nsteps ? step : nsteps - 1;
+    const int sv = sbase + (step < nsteps ? step : nsteps - 1);
     uint8_t *base = smem + slot * SL::kBytes;
     const int kb = 2 * sv + kh;
     const bool ok = wrow_ok && kb < p.KB;
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     }
   };
   auto dq_compute = [&](int step, const Raw &rw, int nb, u4_t (&bo)[2][2]) {
-    const bool wok = wrow_ok && 2 * step + kh < p.KB;
+    const bool wok = wrow_ok && 2 * (sbase + step) + kh < p.KB;
     const int r = 32 * nb + l32;
     uint32_t z = 1u << (BITS - 1);
     if constexpr (HAS_ZP) z = BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int trow = tid >> 1, thh = (tid & 1) * 16;
   const int br = tid >> 3, bnc = (tid & 7) * 16;
   float4 tv[4][4];
-  if constexpr (LORA != 0) {
+  if (lora_here) {
     const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // ---- prologue: steps 0..2 in flight, step 0 dequantized ----
 #pragma unroll
   for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
-  if constexpr (LORA != 0) {
+  if (lora_here) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
 #pragma unroll
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
   _Float16 *sB = sT + BM * LDT;
-  if constexpr (LORA != 0) {
+  if (lora_here) {
     // epilogue operands: T tile [128 m][32 r] (fp16, rounded once from the FP32 sum) and
     // the B tile transposed to [128 n][32 r]
     u4_t o[2];
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         acc[mb][nb][4 * v4 + 3] += o.w;
       }
 
-  if constexpr (LORA != 0) {
+  if (lora_here) {
     const int akof = 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < kRank / 16; ++kk) {
@@ -464,8 +475,33 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // store: the MFMAs computed Y^T blocks (weights as the row operand), so accumulator
   // register v of block [mb][nb] holds output row m = 32 mb + lane % 32 and column
   // n = 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per register
-  // quad, stored as one 8-byte vector
+  // quad, stored as one 8-byte vector (16 bytes for an FP32 partial)
   const bool vec = (p.N & 3) == 0;
+  if (p.splits > 1) {
+    // this K range's FP32 partial; the reduction launch adds the ranges in order
+    float *part = p.ypart + (size_t)ks * p.M * p.N;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + mb * 32 + l32;
+      if (m >= p.M) continue;
+      float *prow = part + (size_t)m * p.N;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi;
+          if (vec && n + 4 <= p.N) {
+            *reinterpret_cast<float4 *>(prow + n) =
+                float4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < p.N) prow[n + e] = acc[mb][nb][4 * j + e];
+          }
+        }
+    }
+    return;
+  }
   // broadcast bias of this lane's columns, added in FP32 before the rounding
   float bv[2][4][4];
 #pragma unroll
@@ -503,9 +539,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
 }
 
+// Y = fp16(sum over the K ranges of the FP32 partials, in range order, + bias): four
+// consecutive outputs per thread when N % 4 == 0, else one
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, int splits, const uint16_t *bias,
+                                                            uint16_t *Y, int M, int N) {
+  const long MN = (long)M * N;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if ((N & 3) == 0) {
+    const long e = 4 * i;
+    if (e >= MN) return;
+    float4 v[kMaxSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxSplits; ++k)
+      if (k < splits) v[k] = *reinterpret_cast<const float4 *>(part + k * MN + e);
+    float4 y = v[0];
+#pragma unroll
+    for (int k = 1; k < kMaxSplits; ++k)
+      if (k < splits) {
+        y.x += v[k].x;
+        y.y += v[k].y;
+        y.z += v[k].z;
+        y.w += v[k].w;
+      }
+    if (bias) {
+      const int n = (int)(e % N);
+      y.x += h2f(bias[n]);
+      y.y += h2f(bias[n + 1]);
+      y.z += h2f(bias[n + 2]);
+      y.w += h2f(bias[n + 3]);
+    }
+    const h2_t lo = {(_Float16)y.x, (_Float16)y.y};
+    const h2_t hi = {(_Float16)y.z, (_Float16)y.w};
+    *reinterpret_cast<u2_t *>(Y + e) = u2_t{as_u32(lo), as_u32(hi)};
+  } else {
+    if (i >= MN) return;
+    float y = part[i];
+    for (int k = 1; k < splits; ++k) y += part[k * MN + i];
+    if (bias) y += h2f(bias[i % N]);
+    Y[i] = __builtin_bit_cast(uint16_t, (_Float16)y);
+  }
+}
+
 template <int BITS, bool HAS_ZP>
 hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
-  const dim3 grid(p.MT * p.NT), block(kThreads);
+  const dim3 grid(p.MT * p.NT * p.splits), block(kThreads);
   switch (lora) {
     case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0>), grid, block, 0, s, p); break;
     case 1: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 1>), grid, block, 0, s, p); break;
@@ -517,8 +594,45 @@ hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s) {
-  if (bits == 4) return has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s);
-  return has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s);
+  if (p.splits < 1 || p.splits > kMaxSplits) return hipErrorInvalidValue;
+  const hipError_t e = bits == 4 ? (has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s))
+                                 : (has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s));
+  if (e != hipSuccess || p.splits == 1) return e;
+  const long MN = (long)p.M * p.N;
+  const long work = (p.N & 3) == 0 ? MN / 4 : MN;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, p.ypart, p.splits,
+                     p.bias, p.Y, p.M, p.N);
+  return hipGetLastError();
+}
+
+// K ranges per output tile.  The grid holds one 128 x 128 tile per CU at a time, so a
+// shape with fewer tiles than CUs (small M) leaves CUs idle for the whole K loop, and a
+// tile count just above a multiple of the CU count leaves a short last round.  Splitting
+// K into S ranges multiplies the workgroups by S at the price of S FP32 partial outputs
+// written and read once more by a reduction launch.  S minimises the estimate
+//   rounds(tiles * S) * steps(S) * t_step  +  [S > 1] (t_launch + partial bytes / bandwidth)
+// with t_step ~0.8 us per 64-k step of a tile, t_launch ~2 us and ~6 TB/s for the
+// partials (they stay in the Infinity Cache at these sizes); at least 2 K-steps per range.
+int gemm_splits(int M, int N, int K) {
+  constexpr int kCUs = 256;
+  const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int tsteps = (K / kBlock + 1) / 2;
+  if (tiles <= 0 || tsteps <= 0) return 1;
+  int best = 1;
+  double best_us = 1e30;
+  for (int S = 1; S <= kMaxSplits; ++S) {
+    const int sps = (tsteps + S - 1) / S;
+    if (S > 1 && sps < 2) break;
+    if ((tsteps + sps - 1) / sps != S) continue;     // some range would be empty
+    const double rounds = (double)((tiles * S + kCUs - 1) / kCUs);
+    double us = rounds * sps * 0.8;
+    if (S > 1) us += 2.0 + (2.0 * S + 0.5) * 4.0 * (double)M * N / 6e6;
+    if (us < best_us * 0.97) {
+      best_us = us;
+      best = S;
+    }
+  }
+  return best;
 }
 
 }  // namespace mnb

@@ -127,8 +127,9 @@ int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, in
 
 /*
  * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path and
- * any adapter kind (host only).  The workspace holds partial sums, the LoRA down-projection
- * T and a few counters.  It must be ZERO-FILLED before its first use; every call that
+ * any adapter kind (host only).  The workspace holds partial sums (among them the prefill
+ * GEMM's FP32 partial outputs when it splits K over several workgroups per output tile),
+ * the LoRA down-projection T and a few counters.  It must be ZERO-FILLED before its first use; every call that
  * completes leaves its counters at zero again, so one workspace can be reused by
  * consecutive calls on one stream.  Calls that overlap in time must not share a workspace.
  */
