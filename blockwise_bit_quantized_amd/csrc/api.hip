@@ -295,19 +295,16 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     fprintf(stderr, "[mnb] M=%d N=%d K=%d bits=%d: %s\n", M, N, K, bits, b);
   }
 
-  // T projection output: FP32 partials per K-part; consumers read `tparts` parts.  The
-  // projection reduces them itself (per-tile arrival counter, agent-scope fences) where
-  // that pays: for small M, whose consumers would add the parts row by row, and for more
-  // than 4 parts; the GEMM adds up to 4 parts, the M == 1 GEMV up to 8, with their own
-  // loads in flight together.
+  // T projection output: FP32 partials per K-part; consumers read `tparts` parts.  For
+  // 2 <= M <= 16, whose consumers would add the parts row by row, the projection reduces
+  // them itself (per-tile arrival counter, agent-scope fences).  Above that the fences
+  // cost more than they save (each writes back and invalidates an L2), so the projection
+  // uses 1024-k parts and the GEMM adds them (four loads in flight, then one at a time);
+  // the M == 1 GEMV adds up to 8 with its loads in flight together.
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   int tparts = w.tparts;
   if (r.tproj) {
-#ifndef MNB_EXP_OLDREDUCE
     const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && M <= kRowsMaxM;
-#else
-    const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && (M <= kRowsMaxM || w.tparts > 4);
-#endif
     TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), tproj_out,
                    reinterpret_cast<float *>(ws + w.tfinal), reinterpret_cast<int *>(ws + w.ctrl),
                    M, K, w.tmt, w.tparts, reduce};

@@ -173,11 +173,10 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
 
 }  // namespace
 
-// K per part: 1024, or 256 when 1024-k parts would give fewer than 128 workgroups (small M)
+// K per part: 1024; for M <= 16 (whose parts the projection adds itself) 256 when 1024-k
+// parts would give fewer than 128 workgroups
 int tproj_kp(int M, int K) {
-#ifndef MNB_EXP_KP256
   if (M > kRowsMaxM) return 1024;
-#endif
   return ((M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024;
 }
 int tproj_parts(int M, int K) {

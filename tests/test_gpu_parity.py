@@ -174,6 +174,22 @@ def test_small_shapes_all_paths(bits, zp, adapter):
             compare(run(case, path, flags, pw=pw), ref, what="%s M=%d N=%d K=%d" % (name, M, N, K))
 
 
+SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
+
+
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_gemm_split_k_ranges(adapter):
+    """Shapes with fewer 128x128 tiles than CUs: the GEMM splits K into ranges (odd block
+    counts, ragged M and N, N % 4 != 0 for the scalar reduction) and must still match."""
+    for i, (M, N, K) in enumerate(SPLIT_SHAPES):
+        _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, {None: 0, "f16": 1, "q8": 2}[adapter],
+                                         mnb.mnb_options(2, 0))
+        assert not desc.endswith(" splits=1"), desc
+        case = si.make_random(190 + i, M, N, K, 4, i % 2 == 0, adapter, bias=i >= 2)
+        rows = list(range(M)) if M <= 64 else [0, 1, 127, 128, M - 1]
+        compare(run(case, 2, 0)[rows], oracle.matmul(rows_case(case, rows)), what="split M=%d N=%d K=%d" % (M, N, K))
+
+
 # ------------------------------------------------------------------------------------------
 # bit-exact pins on the GPU
 # ------------------------------------------------------------------------------------------
