@@ -64,6 +64,7 @@ def _load() -> C.CDLL:
     P, I, S = C.c_void_p, C.c_int, C.c_size_t
     lib.mnb_packed_sizes.argtypes = [I, I, I, I, I, C.POINTER(S), C.POINTER(S), C.POINTER(S)]
     lib.mnb_pack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+    lib.mnb_pack_kn.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
     lib.mnb_unpack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
     lib.mnb_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.mnb_workspace_bytes.restype = S
@@ -76,7 +77,7 @@ def _load() -> C.CDLL:
     lib.mnb_status_string.argtypes = [I]
     lib.mnb_status_string.restype = C.c_char_p
     lib.mnb_version.argtypes = []
-    for f in ("mnb_packed_sizes", "mnb_pack", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
+    for f in ("mnb_packed_sizes", "mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
               "mnb_matmul_bias", "mnb_describe_route", "mnb_version"):
         getattr(lib, f).restype = I
     return lib
@@ -105,6 +106,10 @@ def mnb_packed_sizes(N, K, bits, block, has_zp):
 
 def mnb_pack(codes, scales, zp, N, K, bits, block, wq, sc, zpp, stream) -> int:
     return lib.mnb_pack(codes, scales, zp, N, K, bits, block, wq, sc, zpp, stream)
+
+
+def mnb_pack_kn(codes_kn, scales_kn, zp_kn, N, K, bits, block, wq, sc, zpp, stream) -> int:
+    return lib.mnb_pack_kn(codes_kn, scales_kn, zp_kn, N, K, bits, block, wq, sc, zpp, stream)
 
 
 def mnb_unpack(wq, sc, zpp, N, K, bits, block, codes, scales, zp, stream) -> int:
@@ -194,6 +199,22 @@ def pack(codes, scales, zp, bits: int) -> PackedWeight:
     zpp = torch.empty(zpb, dtype=torch.uint8, device=dev) if zp is not None else None
     _check(mnb_pack(_ptr(codes), _ptr(scales), _ptr(zp), N, K, bits, 32, _ptr(wq), _ptr(sc), _ptr(zpp),
                     _stream(dev)))
+    return PackedWeight(wq, sc, zpp, N, K, bits)
+
+
+def pack_kn(codes_kn, scales_kn, zp_kn, bits: int) -> PackedWeight:
+    """Pack from the DequantizeLinear layout: codes uint8 [K,N], scales fp16 [K/32,N],
+    zp uint8 [K/32,N] | None (device tensors)."""
+    import torch
+    K, N = codes_kn.shape
+    st, wqb, scb, zpb = mnb_packed_sizes(N, K, bits, 32, zp_kn is not None)
+    _check(st)
+    dev = codes_kn.device
+    wq = torch.empty(wqb, dtype=torch.uint8, device=dev)
+    sc = torch.empty(scb // 2, dtype=torch.float16, device=dev)
+    zpp = torch.empty(zpb, dtype=torch.uint8, device=dev) if zp_kn is not None else None
+    _check(mnb_pack_kn(_ptr(codes_kn), _ptr(scales_kn), _ptr(zp_kn), N, K, bits, 32, _ptr(wq), _ptr(sc),
+                       _ptr(zpp), _stream(dev)))
     return PackedWeight(wq, sc, zpp, N, K, bits)
 
 

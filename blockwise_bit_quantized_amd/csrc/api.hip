@@ -170,6 +170,22 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   }
 }
 
+// both packers: kn selects the [K, N] (DequantizeLinear) source layout
+int pack_any(const uint8_t *codes, const void *scales, const uint8_t *zp, int N, int K, int bits, int block,
+             void *wq, void *sc, void *zpp, void *stream, bool kn) {
+  int st = check_common(0, N, K, bits, block);
+  if (st) return st;
+  if (N == 0 || K == 0) return MNB_OK;
+  if (!codes || !scales || !wq || !sc || (zp && !zpp)) return MNB_ERR_INVALID_ARG;
+  if (misaligned(codes) || misaligned(scales) || misaligned(zp) || misaligned(wq) || misaligned(sc) ||
+      (zp && misaligned(zpp)))
+    return MNB_ERR_MISALIGNED;
+  PackParams p{codes, static_cast<const uint16_t *>(scales), zp, static_cast<uint8_t *>(wq),
+               static_cast<uint16_t *>(sc), static_cast<uint8_t *>(zpp), N, K, cdiv(N, kGroup), K / kBlock};
+  if (!zp) p.zpp = nullptr;
+  return launch_pack(bits, kn, p, static_cast<hipStream_t>(stream)) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+}
+
 bool log_enabled() {
   static int v = -1;
   if (v < 0) {
@@ -183,7 +199,7 @@ bool log_enabled() {
 
 extern "C" {
 
-int mnb_version(void) { return 101; }
+int mnb_version(void) { return 102; }
 
 const char *mnb_status_string(int status) {
   switch (status) {
@@ -217,18 +233,14 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank) {
 
 int mnb_pack(const uint8_t *codes, const void *scales, const uint8_t *zp, int N, int K, int bits, int block,
              void *wq, void *sc, void *zpp, void *stream) {
-  int st = check_common(0, N, K, bits, block);
-  if (st) return st;
-  if (N == 0 || K == 0) return MNB_OK;
-  if (!codes || !scales || !wq || !sc || (zp && !zpp)) return MNB_ERR_INVALID_ARG;
-  if (misaligned(codes) || misaligned(scales) || misaligned(zp) || misaligned(wq) || misaligned(sc) ||
-      (zp && misaligned(zpp)))
-    return MNB_ERR_MISALIGNED;
-  PackParams p{codes, static_cast<const uint16_t *>(scales), zp, static_cast<uint8_t *>(wq),
-               static_cast<uint16_t *>(sc), static_cast<uint8_t *>(zpp), N, K, cdiv(N, kGroup), K / kBlock};
-  if (!zp) p.zpp = nullptr;
-  return launch_pack(bits, p, static_cast<hipStream_t>(stream)) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
+  return pack_any(codes, scales, zp, N, K, bits, block, wq, sc, zpp, stream, false);
 }
+
+int mnb_pack_kn(const uint8_t *codes_kn, const void *scales_kn, const uint8_t *zp_kn, int N, int K, int bits,
+                int block, void *wq, void *sc, void *zpp, void *stream) {
+  return pack_any(codes_kn, scales_kn, zp_kn, N, K, bits, block, wq, sc, zpp, stream, true);
+}
+
 
 int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, int bits, int block,
                uint8_t *codes, void *scales, uint8_t *zp, void *stream) {

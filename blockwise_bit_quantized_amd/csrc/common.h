@@ -169,7 +169,7 @@ hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
 int gemm_splits(int M, int N, int K);         // K ranges per output tile of the prefill GEMM
 constexpr int kMaxSplits = 16;
-hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s);
+hipError_t launch_pack(int bits, bool kn, const PackParams &p, hipStream_t s);  // kn: [K, N] source
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
                          uint8_t *zp, hipStream_t s);
 hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStream_t s);

@@ -12,7 +12,9 @@
 namespace mnb {
 namespace {
 
-template <int BITS>
+// KN: codes [K, N] and scales / zero points [K/32, N] (the DequantizeLinear layout, blocks
+// along the first axis) instead of [N, K] and [N, K/32]
+template <int BITS, bool KN>
 __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const long total = (long)p.NG * p.KB * kGroup;
@@ -24,11 +26,21 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
   const int n = g * kGroup + r;
   const bool ok = n < p.N;
   u4_t c0 = {0u, 0u, 0u, 0u}, c1 = {0u, 0u, 0u, 0u};
-  if (ok) {
+  if (ok && !KN) {
     const uint8_t *src = p.codes + (size_t)n * p.K + (size_t)kb * kBlock;
     c0 = *reinterpret_cast<const u4_t *>(src);
     c1 = *reinterpret_cast<const u4_t *>(src + 16);
+  } else if (ok) {
+    // column n of the block's 32 rows: consecutive threads read consecutive bytes
+    const uint8_t *src = p.codes + (size_t)kb * kBlock * p.N + n;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      c0[k >> 2] |= (uint32_t)src[(size_t)k * p.N] << (8 * (k & 3));
+      c1[k >> 2] |= (uint32_t)src[(size_t)(k + 16) * p.N] << (8 * (k & 3));
+    }
   }
+  // block-parameter index of row n (scales, zero points)
+  auto bidx = [&](int nn) -> size_t { return KN ? (size_t)kb * p.N + nn : (size_t)nn * p.KB + kb; };
   auto code = [&](int k) -> uint32_t {  // code k (0..31) of this row-block
     const u4_t &v = k < 16 ? c0 : c1;
     const int kk = k & 15;
@@ -51,16 +63,16 @@ __global__ __launch_bounds__(256) void pack_kernel(PackParams p) {
     *reinterpret_cast<u4_t *>(p.wq + (((size_t)tile * 2 + 0) * kGroup + r) * 16) = c0;
     *reinterpret_cast<u4_t *>(p.wq + (((size_t)tile * 2 + 1) * kGroup + r) * 16) = c1;
   }
-  p.sc[(size_t)tile * kGroup + r] = ok ? p.scales[(size_t)n * p.KB + kb] : (uint16_t)0;
+  p.sc[(size_t)tile * kGroup + r] = ok ? p.scales[bidx(n)] : (uint16_t)0;
   if (p.zp) {
     if constexpr (BITS == 4) {
       if ((r & 1) == 0) {
-        const uint32_t z0 = ok ? (p.zp[(size_t)n * p.KB + kb] & 0xFu) : 0u;
-        const uint32_t z1 = (n + 1 < p.N) ? (p.zp[(size_t)(n + 1) * p.KB + kb] & 0xFu) : 0u;
+        const uint32_t z0 = ok ? (p.zp[bidx(n)] & 0xFu) : 0u;
+        const uint32_t z1 = (n + 1 < p.N) ? (p.zp[bidx(n + 1)] & 0xFu) : 0u;
         p.zpp[(size_t)tile * 32 + (r >> 1)] = (uint8_t)(z0 | (z1 << 4));
       }
     } else {
-      p.zpp[(size_t)tile * kGroup + r] = ok ? p.zp[(size_t)n * p.KB + kb] : (uint8_t)0;
+      p.zpp[(size_t)tile * kGroup + r] = ok ? p.zp[bidx(n)] : (uint8_t)0;
     }
   }
 }
@@ -117,12 +129,14 @@ __global__ __launch_bounds__(256) void fill_kernel(uint16_t *Y, const uint16_t *
 
 }  // namespace
 
-hipError_t launch_pack(int bits, const PackParams &p, hipStream_t s) {
+hipError_t launch_pack(int bits, bool kn, const PackParams &p, hipStream_t s) {
   const long total = (long)p.NG * p.KB * kGroup;
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 255) / 256));
-  if (bits == 4) hipLaunchKernelGGL(pack_kernel<4>, grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL(pack_kernel<8>, grid, dim3(256), 0, s, p);
+  if (bits == 4 && !kn) hipLaunchKernelGGL((pack_kernel<4, false>), grid, dim3(256), 0, s, p);
+  else if (bits == 4) hipLaunchKernelGGL((pack_kernel<4, true>), grid, dim3(256), 0, s, p);
+  else if (!kn) hipLaunchKernelGGL((pack_kernel<8, false>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((pack_kernel<8, true>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -121,6 +121,21 @@ int mnb_packed_sizes(int N, int K, int bits, int block, int has_zp,
 int mnb_pack(const uint8_t *codes, const void *scales, const uint8_t *zp, int N, int K,
              int bits, int block, void *wq, void *sc, void *zpp, void *stream);
 
+/*
+ * mnb_pack from the DequantizeLinear layout that a DequantizeLinear -> MatMul pair holds:
+ * the weight's first axis is K and the blocks of 32 run along it.  This is the offline
+ * transposition of PR #33800's TransposeDQWeightsForMatMulNBits ("Fuse DQ->MatMulNBits for
+ * shared initializers and skip outer-scope weights", Description: the fusion reads the
+ * original initializers and adds transposed ones), done on the device.
+ *   codes_kn   uint8 [K, N], one code per byte, value < 2^bits
+ *   scales_kn  fp16  [K/32, N]
+ *   zp_kn      uint8 [K/32, N] or NULL (default zero point 2^(bits-1))
+ *   wq, sc, zpp, stream, status codes: as mnb_pack; the output bytes are identical to
+ *   mnb_pack of the transposed tensors.  All pointers 16-byte aligned.
+ */
+int mnb_pack_kn(const uint8_t *codes_kn, const void *scales_kn, const uint8_t *zp_kn, int N,
+                int K, int bits, int block, void *wq, void *sc, void *zpp, void *stream);
+
 /* Inverse of mnb_pack (for round-trip checks).  zp may be NULL iff zpp is NULL. */
 int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, int bits,
                int block, uint8_t *codes, void *scales, uint8_t *zp, void *stream);
@@ -186,7 +201,7 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
 /* Static text for a status code. */
 const char *mnb_status_string(int status);
 
-/* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias. */
+/* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias, 102 mnb_pack_kn. */
 int mnb_version(void);
 
 #ifdef __cplusplus

@@ -31,6 +31,8 @@ def load(path: str | None = None) -> C.CDLL:
     lib.mnbo_matmul.restype = C.c_int
     lib.mnbo_pack.argtypes = [C.c_int] * 3 + [_P] * 6
     lib.mnbo_pack.restype = C.c_int
+    lib.mnbo_pack_kn.argtypes = [C.c_int] * 3 + [_P] * 6
+    lib.mnbo_pack_kn.restype = C.c_int
     lib.mnbo_unpack.argtypes = [C.c_int] * 3 + [_P] * 6
     lib.mnbo_unpack.restype = C.c_int
     lib.mnbo_packed_sizes.argtypes = [C.c_int] * 4 + [C.POINTER(C.c_long)] * 3
@@ -114,6 +116,20 @@ def pack(codes, scales, zp, N, K, bits, lib=None):
                        _ptr(_c(zp, np.uint8)), _ptr(wq), _ptr(sc), _ptr(zpp))
     if rc:
         raise ValueError("pack failed")
+    return wq, sc, zpp
+
+
+def pack_kn(codes_kn, scales_kn, zp_kn, N, K, bits, lib=None):
+    """Pack from the DequantizeLinear layout: codes [K, N], scales / zero points [K/32, N]."""
+    lib = lib or load()
+    wqb, scb, zpb = packed_sizes(N, K, bits, zp_kn is not None, lib)
+    wq = np.zeros(wqb, np.uint8)
+    sc = np.zeros(scb // 2, np.uint16)
+    zpp = np.zeros(zpb, np.uint8) if zp_kn is not None else None
+    rc = lib.mnbo_pack_kn(N, K, bits, _ptr(_c(codes_kn, np.uint8)), _ptr(_c(scales_kn, np.uint16)),
+                          _ptr(_c(zp_kn, np.uint8)), _ptr(wq), _ptr(sc), _ptr(zpp))
+    if rc:
+        raise ValueError("pack_kn failed")
     return wq, sc, zpp
 
 

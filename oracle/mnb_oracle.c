@@ -304,6 +304,44 @@ int mnbo_pack(int N, int K, int bits, const uint8_t *codes, const uint16_t *scal
   return 0;
 }
 
+/*
+ * Packing from the DequantizeLinear layout: codes [K, N], scales and zero points [K/32, N]
+ * (blocks along K, the weight's first axis), as DequantizeLinear -> MatMul holds them.
+ * The PR #33800 page ("Fuse DQ->MatMulNBits ...", Description) fuses that pair into
+ * MatMulNBits by writing new, transposed initializers; here: transpose to [N, K] and
+ * [N, K/32], then pack as above.
+ */
+int mnbo_pack_kn(int N, int K, int bits, const uint8_t *codes_kn, const uint16_t *scales_kn,
+                 const uint8_t *zp_kn, uint8_t *wq, uint16_t *sc, uint8_t *zpp) {
+  if (N < 0 || K < 0 || K % BLK || (bits != 4 && bits != 8)) return -1;
+  int KB = K / BLK;
+  uint8_t *codes = malloc((size_t)N * K + 1);
+  uint16_t *scales = malloc(((size_t)N * KB + 1) * sizeof(uint16_t));
+  uint8_t *zp = zp_kn ? malloc((size_t)N * KB + 1) : NULL;
+  if (!codes || !scales || (zp_kn && !zp)) {
+    free(codes);
+    free(scales);
+    free(zp);
+    return -1;
+  }
+  for (int k = 0; k < K; ++k)
+    for (int n = 0; n < N; ++n) codes[(long)n * K + k] = codes_kn[(long)k * N + n];
+  for (int kb = 0; kb < KB; ++kb)
+    for (int n = 0; n < N; ++n) {
+#if MNBO_MUTATION == 12
+      scales[(long)n * KB + kb] = scales_kn[(long)n * KB + kb];   /* planted: scales not transposed */
+#else
+      scales[(long)n * KB + kb] = scales_kn[(long)kb * N + n];
+#endif
+      if (zp) zp[(long)n * KB + kb] = zp_kn[(long)kb * N + n];
+    }
+  int rc = mnbo_pack(N, K, bits, codes, scales, zp, wq, sc, zpp);
+  free(codes);
+  free(scales);
+  free(zp);
+  return rc;
+}
+
 int mnbo_unpack(int N, int K, int bits, const uint8_t *wq, const uint16_t *sc, const uint8_t *zpp,
                 uint8_t *codes, uint16_t *scales, uint8_t *zp) {
   if (N < 0 || K < 0 || K % BLK || (bits != 4 && bits != 8)) return -1;

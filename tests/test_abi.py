@@ -28,8 +28,9 @@ def header_functions():
 
 def test_header_declares_the_abi():
     names = header_functions()
-    for n in ("mnb_pack", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex", "mnb_workspace_bytes",
-              "mnb_packed_sizes", "mnb_status_string", "mnb_describe_route", "mnb_version"):
+    for n in ("mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex", "mnb_matmul_bias",
+              "mnb_workspace_bytes", "mnb_packed_sizes", "mnb_status_string", "mnb_describe_route",
+              "mnb_version"):
         assert n in names
 
 
@@ -40,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert mnb.mnb_version() == 101
+    assert mnb.mnb_version() == 102
     for st in range(7):
         assert mnb.mnb_status_string(st).startswith("MNB_")
     assert "unknown" in mnb.mnb_status_string(99)
@@ -133,6 +134,12 @@ def test_pack_validation():
     assert mnb.mnb_pack(P, P * 2, P * 5, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_INVALID_ARG
     assert mnb.mnb_pack(None, None, None, 0, 64, 4, 32, None, None, None, None) == 0
     assert mnb.mnb_unpack(P, P, P, 64, 64, 8, 32, P, P, None, None) == mnb.MNB_ERR_INVALID_ARG
+    for f in (mnb.mnb_pack, mnb.mnb_pack_kn):     # the DQ-layout packer validates the same way
+        assert f(P, P * 2, None, 64, 33, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_UNSUPPORTED
+        assert f(P, P * 2 + 2, None, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_MISALIGNED
+        assert f(P, P * 2, None, 64, 64, 3, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_UNSUPPORTED
+        assert f(P, None, None, 64, 64, 4, 32, P * 3, P * 4, None, None) == mnb.MNB_ERR_INVALID_ARG
+        assert f(None, None, None, 64, 0, 4, 32, None, None, None, None) == 0
 
 
 def route(M, N=4096, K=4096, bits=4, zp=1, kind=1, path=0, flags=0):

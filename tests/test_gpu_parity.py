@@ -92,6 +92,28 @@ def test_pack_matches_oracle_bytes(N, K, bits, zp):
         assert np.array_equal(z2.cpu().numpy(), case["zp"])
 
 
+@pytest.mark.parametrize("N,K,bits,zp", [(1, 32, 4, True), (70, 96, 4, False), (100, 96, 8, True),
+                                          (130, 160, 4, True), (49152, 576, 8, True), (4096, 4096, 4, True),
+                                          (257, 1024, 8, False)])
+def test_pack_from_dq_layout_matches_oracle_bytes(N, K, bits, zp):
+    """mnb_pack_kn ([K, N] codes, [K/32, N] scales and zero points, as DequantizeLinear
+    holds them; the 576 x 49152 int8 case is the tied lm_head's own layout) against the
+    oracle, byte for byte, and against mnb_pack of the transposed tensors."""
+    case = si.make_random(21, 1, N, K, bits, zp, None)
+    ckn = np.ascontiguousarray(case["codes"].T)
+    skn = np.ascontiguousarray(case["scales"].T)
+    zkn = np.ascontiguousarray(case["zp"].T) if zp else None
+    pw = mnb.pack_kn(tu8(ckn), t16(skn), tu8(zkn) if zp else None, bits)
+    ref = dev_weight(case)
+    torch.cuda.synchronize()
+    want = oracle.pack_kn(ckn, skn, zkn, N, K, bits)
+    assert same_bits(pw.wq.cpu().numpy(), want[0])
+    assert same_bits(pw.sc.cpu().numpy().view(np.uint16), want[1])
+    if zp:
+        assert same_bits(pw.zp.cpu().numpy(), want[2])
+    assert torch.equal(pw.wq, ref.wq) and torch.equal(pw.sc.view(torch.int16), ref.sc.view(torch.int16))
+
+
 def test_pack_is_deterministic():
     case = si.make_random(12, 1, 300, 256, 4, True, None)
     a, b = dev_weight(case), dev_weight(case)

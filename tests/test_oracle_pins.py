@@ -12,12 +12,14 @@
    and adapter, the default zero point, INT8 adapters equal to F16 adapters holding the
    same values;
  - binary16 conversion against numpy for every bit pattern and for rounding ties;
- - hand-derived bytes of the packed layout, and pack/unpack round trips.
+ - hand-derived bytes of the packed layout, and pack/unpack round trips;
+ - packing from the DequantizeLinear layout ([K, N]) against numpy's transpose, and the
+   same page's repro packed from its own layout.
 
 ``test_planted_mistakes_are_caught`` rebuilds the oracle with each deliberate mistake of
 mnb_oracle.c (zero-point sign, dropped LoRA term, transposed operands, wrong block or
-scale index, wrong default zero point, wrong nibble order) and checks that at least one
-pin fails for each.
+scale index, wrong default zero point, wrong nibble order, bias by row, untransposed
+DQ-layout scales) and checks that at least one pin fails for each.
 """
 from __future__ import annotations
 
@@ -320,10 +322,53 @@ def pin_pack_roundtrip(lib):
                 assert np.array_equal(z2, case["zp"])
 
 
+def pin_pack_from_dq_layout(lib):
+    """Packing from the DequantizeLinear layout (codes [K, N], scales / zero points
+    [K/32, N]; PR #33800 page, Description: the fusion writes transposed initializers)
+    equals packing numpy's transpose of the same tensors, byte for byte."""
+    r = np.random.default_rng(12)
+    for N, K, bits, zp in ((70, 96, 4, True), (33, 64, 8, True), (5, 160, 4, False), (130, 32, 8, False)):
+        codes_kn = r.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
+        scales_kn = r.integers(0x1000, 0x3C00, size=(K // 32, N)).astype(np.uint16)
+        zp_kn = r.integers(0, 1 << bits, size=(K // 32, N)).astype(np.uint8) if zp else None
+        got = oracle.pack_kn(codes_kn, scales_kn, zp_kn, N, K, bits, lib)
+        want = oracle.pack(np.transpose(codes_kn), np.transpose(scales_kn),
+                           None if zp_kn is None else np.transpose(zp_kn), N, K, bits, lib)
+        for g, w in zip(got, want):
+            assert (g is None and w is None) or np.array_equal(g, w)
+
+
+def pin_p5_closed_form_dq_layout(lib):
+    """The PR #33800 repro in its own DequantizeLinear layout (w_q [K, N] = 0, scalar scale
+    0.02 and zero point 3, broadcast to every block): packed from [K, N], every output is
+    -3 * s * sum_k x[k], the same in every column."""
+    kv = {}
+    for line in open(os.path.join(GOLD, "p5_constant_codes.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            kv[k] = int(v, 0)
+    K, N, bits = kv["K"], kv["N"], kv["bits"]
+    s = Fraction(kv["scale_exact_numerator"], kv["scale_exact_denominator"])
+    wq, sc, zpp = oracle.pack_kn(np.full((K, N), kv["code"], np.uint8),
+                                 np.full((K // 32, N), kv["scale_f16"], np.uint16),
+                                 np.full((K // 32, N), kv["zero_point"], np.uint8), N, K, bits, lib)
+    codes, scales, zp = oracle.unpack(wq, sc, zpp, N, K, bits, lib)
+    M = 2
+    X = si.to_f16_bits(np.random.default_rng(8).standard_normal((M, K)))
+    got = oracle.matmul(dict(M=M, N=N, K=K, bits=bits, X=X, codes=codes, scales=scales, zp=zp,
+                             adapter=None), lib)
+    Xf = _frac_matrix(_f16(X))
+    for m in range(M):
+        want = -3 * s * sum(Xf[m])
+        assert np.all(got[m] == got[m, 0])
+        bound = 1e-13 * float(3 * s * sum(abs(v) for v in Xf[m]))
+        assert abs(Fraction(float(got[m, 0])) - want) <= Fraction(bound)
+
+
 PINS = [pin_exact_bruteforce, pin_numpy_dq_matmul, pin_p5_closed_form, pin_one_hot,
         pin_code_equals_zero_point, pin_empty_and_zero_adapter, pin_superposition,
         pin_default_zero_point, pin_q8_equals_f16, pin_pack_layout, pin_pack_roundtrip,
-        pin_empty_weights_bias]
+        pin_empty_weights_bias, pin_pack_from_dq_layout, pin_p5_closed_form_dq_layout]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -366,7 +411,8 @@ def test_f16_round_nearest_even():
 MUTATIONS = {1: "zero-point sign", 2: "LoRA term dropped", 3: "scale index transposed",
              4: "block index off by one", 5: "A transposed", 6: "default zero point 0",
              7: "natural nibble order", 8: "X transposed", 9: "B transposed",
-             10: "INT8 A scale ignores rank column", 11: "bias indexed by the row"}
+             10: "INT8 A scale ignores rank column", 11: "bias indexed by the row",
+             12: "DQ-layout scales not transposed"}
 
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS), ids=lambda m: MUTATIONS[m])
