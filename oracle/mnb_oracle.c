@@ -33,15 +33,22 @@
  * The packed device layout (mnbo_pack / mnbo_unpack) is this project's own layout; it is
  * implemented here independently from its prose description:
  *  - rows are grouped by 64 (NG = ceil(N/64)), padded rows hold code 0, scale 0, zp 0;
- *  - KB = K/32 blocks; each block of one row is C = bits/4 chunks of 16 bytes;
- *  - wq chunk (g, kb, c, r) sits at byte ((((g*KB + kb)*C + c)*64 + r) * 16);
+ *  - KB = K/32 blocks; for 4 and 8 bits each block of one row is C = bits/4 chunks of
+ *    16 bytes, and wq chunk (g, kb, c, r) sits at byte ((((g*KB + kb)*C + c)*64 + r) * 16);
+ *  - 2-bit: one 16-byte chunk holds two consecutive blocks of one row: chunk (g, kb2, r),
+ *    kb2 < KB2 = ceil(KB/2), sits at byte (((g*KB2 + kb2)*64 + r) * 16); its bytes 8h..8h+7
+ *    hold block 2*kb2 + h (all zero when that block is past KB).  Within a block's 8 bytes,
+ *    bytes 4j..4j+3 form a little-endian word (j = 0, 1) whose 2-bit field i (bits
+ *    2i..2i+1, i = 0..7) holds k = 16j + 2i and whose field 8+i (bits 16+2i..) holds
+ *    k = 16j + 2i + 1;
  *  - 4-bit chunk: 32 codes k = 0..31 of the block; bytes 4j..4j+3 form a little-endian
  *    32-bit word whose nibble i (bits 4i..4i+3, i = 0..3) holds k = 8j + 2i and whose
  *    nibble 4+i (bits 16+4i..) holds k = 8j + 2i + 1;
  *  - 8-bit chunk c: byte b holds k = 16c + b;
  *  - scales: fp16 element ((g*KB + kb)*64 + r);
  *  - zero points: 4-bit byte ((g*KB + kb)*32 + r/2), low nibble for even r, high for odd r;
- *    8-bit byte ((g*KB + kb)*64 + r).
+ *    8-bit byte ((g*KB + kb)*64 + r); 2-bit byte ((g*KB + kb)*16 + r/4), bits
+ *    2*(r%4)..2*(r%4)+1.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC.  MNBO_MUTATION=<n> plants one
  * deliberate mistake (see the switch in each function); it exists so that the pin tests
@@ -165,7 +172,7 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
                 const uint16_t *A_scales, const void *B, const uint16_t *B_scales,
                 const uint16_t *bias, double *Y) {
   if (M < 0 || N < 0 || K < 0 || K % BLK) return -1;
-  if (bits != 4 && bits != 8) return -1;
+  if (bits != 2 && bits != 4 && bits != 8) return -1;
   int has_lora = kind != 0 && rank != 0 && A != NULL && B != NULL;
   if (has_lora && (rank != 32 || (kind != 1 && kind != 2))) return -1;
   if (has_lora && kind == 2 && (A_scales == NULL || B_scales == NULL)) return -1;
@@ -248,10 +255,12 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
 /* Packed device layout                                                                  */
 /* ------------------------------------------------------------------------------------ */
 
+static int bits_ok(int bits) { return bits == 2 || bits == 4 || bits == 8; }
+
 int mnbo_packed_sizes(int N, int K, int bits, int has_zp, long *wq, long *sc, long *zpb) {
-  if (N < 0 || K < 0 || K % BLK || (bits != 4 && bits != 8)) return -1;
+  if (N < 0 || K < 0 || K % BLK || !bits_ok(bits)) return -1;
   long NG = (N + GROUP - 1) / GROUP, KB = K / BLK;
-  *wq = NG * KB * GROUP * 16 * (bits / 4);
+  *wq = bits == 2 ? NG * ((KB + 1) / 2) * GROUP * 16 : NG * KB * GROUP * 16 * (bits / 4);
   *sc = NG * KB * GROUP * 2;
   *zpb = has_zp ? NG * KB * GROUP * bits / 8 : 0;
   return 0;
@@ -269,11 +278,21 @@ static void nib_pos(int k, int *byte, int *shift) {
   *shift = bit % 8;
 }
 
+/* byte offset of the 2-bit code k (0..31) of block kb inside its 16-byte chunk, and its
+   shift; the chunk is (kb / 2) */
+static void crumb_pos(int kb, int k, int *byte, int *shift) {
+  int j = k / 16, within = k % 16;
+  int i = within / 2, odd = within % 2;
+  int bit = (odd ? 16 : 0) + 2 * i;
+  *byte = 8 * (kb % 2) + 4 * j + bit / 8;
+  *shift = bit % 8;
+}
+
 int mnbo_pack(int N, int K, int bits, const uint8_t *codes, const uint16_t *scales,
               const uint8_t *zp, uint8_t *wq, uint16_t *sc, uint8_t *zpp) {
   long wqb, scb, zpb;
   if (mnbo_packed_sizes(N, K, bits, zp != NULL, &wqb, &scb, &zpb)) return -1;
-  int NG = (N + GROUP - 1) / GROUP, KB = K / BLK, C = bits / 4;
+  int NG = (N + GROUP - 1) / GROUP, KB = K / BLK, C = bits / 4, KB2 = (KB + 1) / 2;
   memset(wq, 0, (size_t)wqb);
   memset(sc, 0, (size_t)scb);
   if (zp && zpp) memset(zpp, 0, (size_t)zpb);
@@ -285,7 +304,11 @@ int mnbo_pack(int N, int K, int bits, const uint8_t *codes, const uint16_t *scal
         long tile = (long)g * KB + kb;
         for (int kk = 0; kk < BLK; ++kk) {
           uint8_t q = codes[(long)n * K + kb * BLK + kk];
-          if (bits == 4) {
+          if (bits == 2) {
+            int byte, shift;
+            crumb_pos(kb, kk, &byte, &shift);
+            wq[(((long)g * KB2 + kb / 2) * GROUP + r) * 16 + byte] |= (uint8_t)((q & 3) << shift);
+          } else if (bits == 4) {
             int byte, shift;
             nib_pos(kk, &byte, &shift);
             wq[((tile * C + 0) * GROUP + r) * 16 + byte] |= (uint8_t)((q & 0xf) << shift);
@@ -297,7 +320,8 @@ int mnbo_pack(int N, int K, int bits, const uint8_t *codes, const uint16_t *scal
         sc[tile * GROUP + r] = scales[(long)n * KB + kb];
         if (zp && zpp) {
           uint8_t z = zp[(long)n * KB + kb];
-          if (bits == 4) zpp[tile * 32 + r / 2] |= (uint8_t)((z & 0xf) << (4 * (r % 2)));
+          if (bits == 2) zpp[tile * 16 + r / 4] |= (uint8_t)((z & 3) << (2 * (r % 4)));
+          else if (bits == 4) zpp[tile * 32 + r / 2] |= (uint8_t)((z & 0xf) << (4 * (r % 2)));
           else zpp[tile * 64 + r] = z;
         }
       }
@@ -313,7 +337,7 @@ int mnbo_pack(int N, int K, int bits, const uint8_t *codes, const uint16_t *scal
  */
 int mnbo_pack_kn(int N, int K, int bits, const uint8_t *codes_kn, const uint16_t *scales_kn,
                  const uint8_t *zp_kn, uint8_t *wq, uint16_t *sc, uint8_t *zpp) {
-  if (N < 0 || K < 0 || K % BLK || (bits != 4 && bits != 8)) return -1;
+  if (N < 0 || K < 0 || K % BLK || !bits_ok(bits)) return -1;
   int KB = K / BLK;
   uint8_t *codes = malloc((size_t)N * K + 1);
   uint16_t *scales = malloc(((size_t)N * KB + 1) * sizeof(uint16_t));
@@ -344,15 +368,19 @@ int mnbo_pack_kn(int N, int K, int bits, const uint8_t *codes_kn, const uint16_t
 
 int mnbo_unpack(int N, int K, int bits, const uint8_t *wq, const uint16_t *sc, const uint8_t *zpp,
                 uint8_t *codes, uint16_t *scales, uint8_t *zp) {
-  if (N < 0 || K < 0 || K % BLK || (bits != 4 && bits != 8)) return -1;
-  int KB = K / BLK, C = bits / 4;
+  if (N < 0 || K < 0 || K % BLK || !bits_ok(bits)) return -1;
+  int KB = K / BLK, C = bits / 4, KB2 = (KB + 1) / 2;
   for (int n = 0; n < N; ++n) {
     int g = n / GROUP, r = n % GROUP;
     for (int kb = 0; kb < KB; ++kb) {
       long tile = (long)g * KB + kb;
       for (int kk = 0; kk < BLK; ++kk) {
         uint8_t q;
-        if (bits == 4) {
+        if (bits == 2) {
+          int byte, shift;
+          crumb_pos(kb, kk, &byte, &shift);
+          q = (wq[(((long)g * KB2 + kb / 2) * GROUP + r) * 16 + byte] >> shift) & 3;
+        } else if (bits == 4) {
           int byte, shift;
           nib_pos(kk, &byte, &shift);
           q = (wq[((tile * C + 0) * GROUP + r) * 16 + byte] >> shift) & 0xf;
@@ -363,7 +391,8 @@ int mnbo_unpack(int N, int K, int bits, const uint8_t *wq, const uint16_t *sc, c
       }
       scales[(long)n * KB + kb] = sc[tile * GROUP + r];
       if (zp && zpp) {
-        if (bits == 4) zp[(long)n * KB + kb] = (zpp[tile * 32 + r / 2] >> (4 * (r % 2))) & 0xf;
+        if (bits == 2) zp[(long)n * KB + kb] = (zpp[tile * 16 + r / 4] >> (2 * (r % 4))) & 3;
+        else if (bits == 4) zp[(long)n * KB + kb] = (zpp[tile * 32 + r / 2] >> (4 * (r % 2))) & 0xf;
         else zp[(long)n * KB + kb] = zpp[tile * 64 + r];
       }
     }

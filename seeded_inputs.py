@@ -144,12 +144,12 @@ def make_config(cfg: int, M: int | None = None, adapter: str | None | bool = Tru
 def make_random(seed: int, M: int, N: int, K: int, bits: int, with_zp: bool, adapter=None,
                 s_lo=None, s_hi=None, x_std=1.0, bias=False):
     """Generic seeded case for tests (shapes not tied to a workload).  Scales default to the
-    decode/prefill range U[0.001, 0.02] for 4-bit and the lm_head range U[1e-4, 4e-3] for
-    8-bit weights; for 8-bit with K > 576 the range shrinks by sqrt(576/K) so that the
+    decode/prefill range U[0.001, 0.02] for 4-bit (and 2-bit) and the lm_head range
+    U[1e-4, 4e-3] for 8-bit weights; for 8-bit with K > 576 the range shrinks by sqrt(576/K) so that the
     output spread stays at the lm_head's (sigma(Y) ~ 4), inside the range where the fp16
     output rounding (half an ulp) stays well below the 2e-2 max-abs tolerance."""
     if s_lo is None:
-        s_lo, s_hi = (0.001, 0.02) if bits == 4 else (1e-4, 4e-3)
+        s_lo, s_hi = (0.001, 0.02) if bits in (2, 4) else (1e-4, 4e-3)
         if bits == 8 and K > 576:
             f = float(np.sqrt(576.0 / K))
             s_lo, s_hi = s_lo * f, s_hi * f

@@ -132,6 +132,8 @@ TINY = [  # (seed, M, N, K, bits, zp, adapter, bias)
     (4, 2, 6, 32, 8, False, None, True),
     (5, 1, 3, 64, 4, True, "q8", False),
     (6, 2, 4, 32, 4, True, "f16", True),
+    (7, 2, 5, 64, 2, True, "f16", False),
+    (8, 1, 6, 96, 2, False, "q8", True),
 ]
 
 
@@ -151,7 +153,9 @@ def pin_numpy_dq_matmul(lib):
     for seed, (M, N, K, bits, zp, ad, bias) in enumerate([(3, 70, 96, 4, True, "f16", False),
                                                           (2, 65, 160, 8, True, "q8", True),
                                                           (4, 33, 64, 4, False, "q8", False),
-                                                          (1, 130, 128, 8, False, None, True)]):
+                                                          (1, 130, 128, 8, False, None, True),
+                                                          (2, 67, 224, 2, True, "f16", True),
+                                                          (3, 40, 96, 2, False, None, False)]):
         case = si.make_random(100 + seed, M, N, K, bits, zp, ad, bias=bias)
         got = oracle.matmul(case, lib)
         ref = numpy_dq_matmul(case)
@@ -163,7 +167,7 @@ def pin_empty_weights_bias(lib):
     """K == 0 (empty packed weights): Y is the broadcast bias exactly, or zeros (PR #33370
     page, commit list: the output keeps its logical shape and holds zeros or the bias)."""
     r = np.random.default_rng(9)
-    for M, N, bits in ((3, 5, 4), (1, 70, 8)):
+    for M, N, bits in ((3, 5, 4), (1, 70, 8), (2, 9, 2)):
         bias = r.standard_normal(N).astype(np.float16).view(np.uint16)
         case = dict(M=M, N=N, K=0, bits=bits, X=np.zeros((M, 0), np.uint16),
                     codes=np.zeros((N, 0), np.uint8), scales=np.zeros((N, 0), np.uint16), zp=None,
@@ -200,7 +204,7 @@ def pin_p5_closed_form(lib):
 
 
 def pin_one_hot(lib):
-    for bits, zp in ((4, True), (4, False), (8, True), (8, False)):
+    for bits, zp in ((4, True), (4, False), (8, True), (8, False), (2, True), (2, False)):
         N, K = 67, 96
         case = si.make_random(200 + bits, 1, N, K, bits, zp, None)
         for k in (0, 1, 2, 7, 8, 15, 16, 31, 32, 33, 63, 64, K - 1):
@@ -215,7 +219,7 @@ def pin_one_hot(lib):
 
 
 def pin_code_equals_zero_point(lib):
-    for bits, zp in ((4, True), (8, True), (4, False), (8, False)):
+    for bits, zp in ((4, True), (8, True), (4, False), (8, False), (2, True), (2, False)):
         case = si.make_random(300 + bits, 3, 40, 96, bits, zp, "f16")
         z = case["zp"] if zp else np.full(case["scales"].shape, 2 ** (bits - 1), np.uint8)
         codes = np.repeat(z, 32, axis=1).astype(np.uint8)
@@ -251,7 +255,7 @@ def pin_superposition(lib):
 
 
 def pin_default_zero_point(lib):
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         case = si.make_random(600 + bits, 2, 30, 64, bits, False, None)
         explicit = dict(case, zp=np.full(case["scales"].shape, 2 ** (bits - 1), np.uint8))
         assert np.array_equal(oracle.matmul(case, lib), oracle.matmul(explicit, lib))
@@ -294,6 +298,12 @@ def pack_example_inputs(name):
         k = np.arange(32)
         codes = np.stack([k % 16, 15 - k % 16]).astype(np.uint8)
         return codes, np.array([[0x3C00], [0x4000]], np.uint16), np.array([[3], [12]], np.uint8)
+    if name == "C":
+        n, k = np.arange(5)[:, None], np.arange(96)[None, :]
+        codes = ((k + n) % 4).astype(np.uint8)
+        scales = np.repeat((0x3C00 + np.arange(5))[:, None], 3, axis=1).astype(np.uint16)
+        zp = np.repeat((np.arange(5) % 4)[:, None], 3, axis=1).astype(np.uint8)
+        return codes, scales, zp
     codes = (100 + np.arange(32)).astype(np.uint8)[None, :]
     return codes, np.array([[0x2E66]], np.uint16), np.array([[128]], np.uint8)
 
@@ -312,7 +322,7 @@ def pin_pack_layout(lib):
 
 
 def pin_pack_roundtrip(lib):
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         for N, K, zp in ((1, 32, True), (64, 64, False), (130, 96, True), (200, 32, True)):
             case = si.make_random(800 + N, 1, N, K, bits, zp, None)
             wq, sc, zpp = oracle.pack(case["codes"], case["scales"], case["zp"], N, K, bits, lib)
@@ -327,7 +337,8 @@ def pin_pack_from_dq_layout(lib):
     [K/32, N]; PR #33800 page, Description: the fusion writes transposed initializers)
     equals packing numpy's transpose of the same tensors, byte for byte."""
     r = np.random.default_rng(12)
-    for N, K, bits, zp in ((70, 96, 4, True), (33, 64, 8, True), (5, 160, 4, False), (130, 32, 8, False)):
+    for N, K, bits, zp in ((70, 96, 4, True), (33, 64, 8, True), (5, 160, 4, False), (130, 32, 8, False),
+                           (66, 96, 2, True), (3, 32, 2, False)):
         codes_kn = r.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
         scales_kn = r.integers(0x1000, 0x3C00, size=(K // 32, N)).astype(np.uint16)
         zp_kn = r.integers(0, 1 << bits, size=(K // 32, N)).astype(np.uint8) if zp else None
