@@ -235,6 +235,17 @@ def main():
                    "t_separate_us": round(tsep_s * 1e6, 3),
                    "empty_adapter_us": round(base_s * 1e6, 3),
                    "empty_adapter_GBps": round(dbytes_base / base_s / 1e9, 1)}
+        # the same decode shape with 2-bit codes (default zero point 2) and the F16 adapter,
+        # cold copies of the weights
+        dec2 = si.make_random(2002, dM, dN, dK, 2, False, None)
+        pw2 = weight(dec2)
+        dbytes2 = algorithmic_bytes(dM, dN, dK, 2, False, 32)
+        copies2 = max(1, math.ceil(args.cold_mib * 2**20 / dbytes2))
+        w2 = [mnb.PackedWeight(pw2.wq.clone(), pw2.sc.clone(), None, dN, dK, 2) for _ in range(copies2)]
+        two_s = graph_time(lambda j: mnb.matmul(X0, w2[j % copies2], dcopies[0][2], out=Yd, ws=ws), n_ctx)
+        context["decode_2bit_us"] = round(two_s * 1e6, 3)
+        context["decode_2bit_GBps"] = round(dbytes2 / two_s / 1e9, 1)
+        del w2
     dec_route = mnb.mnb_describe_route(dM, dN, dK, 4, False, mnb.MNB_ADAPTER_F16)[1]
     pre_route = mnb.mnb_describe_route(pM, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
     traffic = recorded_traffic("gemv")

@@ -101,7 +101,7 @@ int effective_lora(const mnb_adapter *ad) {
 
 int check_common(int M, int N, int K, int bits, int block) {
   if (M < 0 || N < 0 || K < 0) return MNB_ERR_INVALID_ARG;
-  if (bits != 4 && bits != 8) return MNB_ERR_UNSUPPORTED;
+  if (bits != 2 && bits != 4 && bits != 8) return MNB_ERR_UNSUPPORTED;
   if (block != kBlock || K % kBlock) return MNB_ERR_UNSUPPORTED;
   return MNB_OK;
 }
@@ -155,7 +155,7 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
     const int NG = cdiv(N, kGroup);
     const int q = gemv_rows_split(N, false);
-    const int mr = gemv_rows_mr(M);
+    const int mr = gemv_rows_mr(M, bits);
     snprintf(buf, len, "%sgemv_rows_b%d_zp%s_%s grid=%dx%d rows=%d q=%d mr=%d", tp, bits, has_zp ? "x" : "def", ln,
              NG * q, cdiv(M, mr), kGroup / q, q, mr);
   } else if (r.path == MNB_PATH_GEMV) {
@@ -205,7 +205,7 @@ const char *mnb_status_string(int status) {
   switch (status) {
     case MNB_OK: return "MNB_OK";
     case MNB_ERR_INVALID_ARG: return "MNB_ERR_INVALID_ARG: invalid argument";
-    case MNB_ERR_UNSUPPORTED: return "MNB_ERR_UNSUPPORTED: unsupported setting (bits 4/8, block 32, K%32==0, rank 0/32)";
+    case MNB_ERR_UNSUPPORTED: return "MNB_ERR_UNSUPPORTED: unsupported setting (bits 2/4/8, block 32, K%32==0, rank 0/32)";
     case MNB_ERR_MISALIGNED: return "MNB_ERR_MISALIGNED: tensor pointer not 16-byte aligned";
     case MNB_ERR_WORKSPACE: return "MNB_ERR_WORKSPACE: workspace missing or too small";
     case MNB_ERR_ALIAS: return "MNB_ERR_ALIAS: output overlaps an input or the workspace";
@@ -219,7 +219,7 @@ int mnb_packed_sizes(int N, int K, int bits, int block, int has_zp, size_t *wq_b
   const int st = check_common(0, N, K, bits, block);
   if (st) return st;
   const size_t tiles = (size_t)cdiv(N, kGroup) * (K / kBlock);
-  if (wq_bytes) *wq_bytes = tiles * kGroup * 16 * (bits / 4);
+  if (wq_bytes) *wq_bytes = (size_t)cdiv(N, kGroup) * chunk_cols(bits, K / kBlock) * kGroup * 16;
   if (sc_bytes) *sc_bytes = tiles * kGroup * 2;
   if (zp_bytes) *zp_bytes = has_zp ? tiles * kGroup * bits / 8 : 0;
   return MNB_OK;

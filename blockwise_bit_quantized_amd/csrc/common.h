@@ -1,20 +1,26 @@
 // common.h -- types, packed-layout geometry and launch parameters shared by the libmnb
 // kernels (gfx950 / CDNA4, wave64).
 //
-// Packed layout (this library's own; the pages fix only "INT4/INT8 codes in blocks of 32
+// Packed layout (this library's own; the pages fix only "2/4/8-bit codes in blocks of 32
 // along K with an FP16 scale and an optional zero point per block"):
 //   * weight rows are grouped by 64 (NG = ceil(N/64) groups, padded rows are zero);
-//   * K is split in KB = K/32 blocks; one block of one row is C = bits/4 chunks of 16 B;
-//   * chunk (g, kb, c, r) lives at byte ((((g*KB + kb)*C + c)*64 + r) * 16), so one
-//     wave64 load instruction of 16 B per lane reads 1 KiB of contiguous codes: 64 rows of
-//     one block (4-bit) or 64 rows of half a block (8-bit);
+//   * K is split in KB = K/32 blocks; a row holds CC 16-byte chunk-columns: CC = 2*KB
+//     (8-bit, half a block each), KB (4-bit, one block), ceil(KB/2) (2-bit, two blocks);
+//   * chunk (g, cc, r) lives at byte (((g*CC + cc)*64 + r) * 16), so one wave64 load
+//     instruction of 16 B per lane reads 1 KiB of contiguous codes (64 rows of one
+//     chunk-column);
 //   * 4-bit chunk: 32-bit word j (bytes 4j..4j+3, little-endian) holds k = 8j..8j+7 with
 //     nibble i = k 8j+2i (bits 4i..4i+3) and nibble 4+i = k 8j+2i+1 (bits 16+4i..).  The
 //     mask 0x000F000F applied to (word >> 4i) then yields the pair (k, k+1) in the two
 //     16-bit halves, which is exactly the packed-fp16 pair order of natural X;
 //   * 8-bit chunk c: byte b holds k = 16c + b;
+//   * 2-bit chunk cc: bytes 8h..8h+7 hold block 2cc + h (zero past KB); in it, word j
+//     (bytes 4j..4j+3) holds k = 16j..16j+15 with 2-bit field i (bits 2i..2i+1) = k
+//     16j+2i and field 8+i (bits 16+2i..) = k 16j+2i+1, so (word >> 2i) & 0x00030003 is
+//     the natural pair (k, k+1) again;
 //   * scales fp16 at ((g*KB + kb)*64 + r); zero points (4-bit) two per byte at
-//     ((g*KB + kb)*32 + r/2), low nibble for even r; (8-bit) one byte at ((g*KB+kb)*64 + r).
+//     ((g*KB + kb)*32 + r/2), low nibble for even r; (8-bit) one byte at ((g*KB+kb)*64 + r);
+//     (2-bit) four per byte at ((g*KB + kb)*16 + r/4), bits 2*(r%4).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,6 +32,11 @@ constexpr int kGroup = 64;   // weight rows per interleaved group (= wave64 lane
 constexpr int kBlock = 32;   // quantization block along K
 constexpr int kRank = 32;    // LoRA rank supported by the kernels
 constexpr int kCUs = 256;    // MI355X compute units (planning constant)
+
+// 16-byte chunk-columns per row of KB blocks
+__host__ __device__ __forceinline__ int chunk_cols(int bits, int KB) {
+  return bits == 2 ? (KB + 1) / 2 : KB * (bits / 4);
+}
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
@@ -68,6 +79,10 @@ __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t c) {
 // bits 4-7, giving 1024 + 16 q, whose difference with 1024 + 16 z is 16 (q - z), exact.
 __device__ __forceinline__ h2_t nib_lo(uint32_t w) { return as_h2(bfi(0x000F000Fu, w, 0x64006400u)); }
 __device__ __forceinline__ h2_t nib_hi16(uint32_t w) { return as_h2(bfi(0x00F000F0u, w, 0x64006400u)); }
+// 2-bit codes: field pair e (bits 2e.. of each half) as 1024 + q, both halves
+__device__ __forceinline__ h2_t crumb_pair(uint32_t w, int e) {
+  return as_h2(((w >> (2 * e)) & 0x00030003u) | 0x64006400u);
+}
 // Same for two 8-bit codes (bytes b0, b1 of w -> halves), via v_perm_b32 with the
 // constant byte 0x64 taken from the first operand.
 __device__ __forceinline__ h2_t byte_pair_lo(uint32_t w) {
@@ -177,7 +192,7 @@ hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStrea
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
 int tproj_parts(int M, int K);                 // K parts of the T projection
-int gemv_rows_mr(int M);                       // rows per workgroup of the small-M path
+int gemv_rows_mr(int M, int bits);                       // rows per workgroup of the small-M path
 // largest M of the small-M path: measured crossover against the MFMA GEMM on the workload
 // weights (the small-M path wins up to M = 8 on all of them, the GEMM from M = 12)
 constexpr int kSmallM = 8;

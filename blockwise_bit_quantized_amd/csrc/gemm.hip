@@ -1,6 +1,7 @@
-// gemm.hip -- prefill path of MatMulNBits (M > 1): FP16 MFMA GEMM whose weight operand is
-// dequantized straight into MFMA operand registers, with the rank-32 LoRA up-projection
-// T.B run as two extra MFMA k-steps on the same accumulators before the fp16 store.
+// gemm.hip -- prefill path of MatMulNBits (M > 1): FP16 MFMA GEMM whose 2-, 4- or 8-bit
+// weight operand is dequantized straight into MFMA operand registers, with the rank-32
+// LoRA up-projection T.B run as two extra MFMA k-steps on the same accumulators before the
+// fp16 store.
 //
 // onnxruntime PR #33370 ("[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits"), commit
 // list: prefill (fuse_up) computes T first, then the base GEMM "with an integrated
@@ -86,7 +87,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int BITS, bool HAS_ZP, int LORA>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  constexpr int C = BITS / 4;
+  constexpr int C = BITS == 8 ? 2 : 1;       // 16-byte code chunks per wave and step
   using SL = Slot<C>;
   // direct loads per wave per step: 4 X, C codes, 1 scale, 1 zero point
   constexpr int kLoadsPerStep = 4 + C + 1 + (HAS_ZP ? 1 : 0);
@@ -163,12 +164,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     const int kb = 2 * sv + kh;
     const bool ok = wrow_ok && kb < p.KB;
     const size_t t = ok ? (size_t)wg * p.KB + kb : 0;
+    if constexpr (BITS == 2) {
+      // one chunk holds both blocks of the step (each wave uses its half)
+      const size_t ch = wrow_ok ? (size_t)wg * tsteps + sv : 0;
+      dma(p.wq + (ch * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave, 16);
+    } else {
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      dma(p.wq + ((t * C + c) * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+      for (int c = 0; c < C; ++c)
+        dma(p.wq + ((t * C + c) * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+    }
     dma(p.sc + t * kGroup + 2 * l32, base + SL::kScale + wave * 256, 4);
     if constexpr (HAS_ZP) {
-      const uint8_t *zsrc = BITS == 4 ? p.zp + t * 32 + 4 * (lane & 7) : p.zp + t * kGroup + 4 * (lane & 15);
+      const uint8_t *zsrc = BITS == 2   ? p.zp + t * 16 + 4 * (lane & 3)
+                            : BITS == 4 ? p.zp + t * 32 + 4 * (lane & 7)
+                                        : p.zp + t * kGroup + 4 * (lane & 15);
       dma(zsrc, base + SL::kZp + wave * 256, 4);
     }
   };
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // piece and needs no selects.  B operand: lane holds 8 consecutive k of column l32;
   // column = weight row 32 * nb + l32.
   struct Raw {
-    u4_t cw[2];          // 4-bit: words (2hi, 2hi+1) in [0], [1]; 8-bit: chunk hi
+    u4_t cw[2];          // 4-bit: words (2hi, 2hi+1) in [0], [1]; 8-bit: chunk hi; 2-bit: word hi in [0]
     uint32_t sraw[2], zb[2];
   };
   auto dq_read = [&](int slot, Raw &rw) {
@@ -195,7 +204,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int r = 32 * nb + l32;
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 2) {
+        // word hi of this wave's block kh: k 16 hi .. 16 hi + 15 of the block
+        rw.cw[nb][0] = *reinterpret_cast<const uint32_t *>(base + SL::kCodes + wave * SL::kCodesWave + r * 16 + 8 * kh +
+                                                            4 * hi);
+      } else if constexpr (BITS == 4) {
         const u2_t w2 = *reinterpret_cast<const u2_t *>(base + SL::kCodes + wave * SL::kCodesWave + r * 16 + hi * 8);
         rw.cw[nb][0] = w2[0];
         rw.cw[nb][1] = w2[1];
@@ -204,20 +217,30 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
       }
       rw.sraw[nb] = *reinterpret_cast<const uint16_t *>(base + SL::kScale + wave * 256 + r * 2);
       rw.zb[nb] = 0;
-      if constexpr (HAS_ZP) rw.zb[nb] = BITS == 4 ? base[SL::kZp + wave * 256 + (r >> 1)] : base[SL::kZp + wave * 256 + r];
+      if constexpr (HAS_ZP)
+        rw.zb[nb] = BITS == 2   ? base[SL::kZp + wave * 256 + (r >> 2)]
+                    : BITS == 4 ? base[SL::kZp + wave * 256 + (r >> 1)]
+                                : base[SL::kZp + wave * 256 + r];
     }
   };
   auto dq_compute = [&](int step, const Raw &rw, int nb, u4_t (&bo)[2][2]) {
     const bool wok = wrow_ok && 2 * (sbase + step) + kh < p.KB;
     const int r = 32 * nb + l32;
     uint32_t z = 1u << (BITS - 1);
-    if constexpr (HAS_ZP) z = BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
+    if constexpr (HAS_ZP)
+      z = BITS == 2 ? (rw.zb[nb] >> ((r & 3) * 2)) & 3u : BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
     // binary16 of 1024 + z is 0x6400 | z (z < 1024): both halves at once
     const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);
     const h2_t s2 = as_h2((wok ? rw.sraw[nb] : 0u) * 0x00010001u);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      if constexpr (BITS == 4) {
+      if constexpr (BITS == 2) {
+        // byte kk of each half of the word: fields (2e, 2e+1) -> the pair k = 8 kk + 2e,
+        // + 1 of this wave's 16; (q - z) exact, times s rounded once
+        const uint32_t v = rw.cw[nb][0] >> (8 * kk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bo[nb][kk][e] = as_u32((crumb_pair(v, e) - zz2) * s2);
+      } else if constexpr (BITS == 4) {
         // Nibbles 0 and 2 of each half sit in mantissa bits 0-3 (after a shift by 8 for
         // 2): OR-ing 0x6400 gives 1024 + q.  Nibbles 1 and 3 are taken in place, at bits
         // 4-7: 1024 + 16 q; minus (1024 + 16 z) that is 16 (q - z), exact, and the scale
@@ -604,8 +627,9 @@ hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
 
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s) {
   if (p.splits < 1 || p.splits > kMaxSplits) return hipErrorInvalidValue;
-  const hipError_t e = bits == 4 ? (has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s))
-                                 : (has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s));
+  const hipError_t e = bits == 2   ? (has_zp ? launch2<2, true>(lora, p, s) : launch2<2, false>(lora, p, s))
+                       : bits == 4 ? (has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s))
+                                   : (has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s));
   if (e != hipSuccess || p.splits == 1) return e;
   const long MN = (long)p.M * p.N;
   const long work = (p.N & 3) == 0 ? MN / 4 : MN;
@@ -623,7 +647,6 @@ hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hip
 // with t_step ~0.8 us per 64-k step of a tile, t_launch ~2 us and ~6 TB/s for the
 // partials (they stay in the Infinity Cache at these sizes); at least 2 K-steps per range.
 int gemm_splits(int M, int N, int K) {
-  constexpr int kCUs = 256;
   const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int tsteps = (K / kBlock + 1) / 2;
   if (tiles <= 0 || tsteps <= 0) return 1;

@@ -1,6 +1,6 @@
 // gemv.hip -- decode path of MatMulNBits (M == 1; any M when forced): one HBM pass over
-// the packed weights with dequantization in registers, FP32 accumulation, and the rank-32
-// LoRA term fused into the same launch.
+// the packed 2-, 4- or 8-bit weights with dequantization in registers, FP32 accumulation,
+// and the rank-32 LoRA term fused into the same launch.
 //
 // Operation (onnxruntime PR #33370 "[WebGPU] Fuse rank-32 quantized LoRA with
 // MatMulNBits", commit list: decode computes base + T and then base + T*Bt^T, sharing the
@@ -210,9 +210,8 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
 
 template <int BITS, bool HAS_ZP, int LORA, int TMODE, int Q, int LPW>
 __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
-  constexpr int C = BITS / 4;       // 16-byte chunks per block and row
   constexpr int R = kGroup / Q;     // rows per workgroup
-  constexpr int KPC = 32 / C;       // k values per chunk (32 for 4-bit, 16 for 8-bit)
+  constexpr int KPC = BITS == 2 ? 64 : 32 / (BITS / 4);   // k per chunk: 64, 32 or 16
   constexpr int XW = LPW * Q * KPC; // halfs of X one wave needs per round
   constexpr bool kTWave = LORA != LORA_NONE && TMODE == T_INPASS;
   __shared__ float red[kWaves][kGroup];
@@ -299,7 +298,7 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
     }
   }
 
-  const int ncc = p.KB * C;             // chunk-columns per row
+  const int ncc = chunk_cols(BITS, p.KB); // chunk-columns per row
   const int nloads = (ncc + Q - 1) / Q; // wave loads per workgroup
   const _Float16 *xrow = reinterpret_cast<const _Float16 *>(p.X) + (size_t)m * p.K;
   const size_t tile0 = (size_t)g * p.KB;
@@ -337,15 +336,25 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       const int l = l0 + wave + kWaves * i;
       const int cc = l * Q + qi;
       const bool ok = l < lend && cc < ncc;
-      const int kb = ok ? cc / C : 0;
-      const int c = ok ? cc - kb * C : 0;
-      const size_t tile = tile0 + kb;
-      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + ((tile * C + c) * kGroup + row) * 16);
-      sraw[i] = p.sc[tile * kGroup + row];
-      zraw[i] = 0;
-      if constexpr (HAS_ZP) {
-        if constexpr (BITS == 4) zraw[i] = p.zp[tile * 32 + (row >> 1)];
-        else zraw[i] = p.zp[tile * kGroup + row];
+      const int ccl = ok ? cc : 0;
+      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + (((size_t)g * ncc + ccl) * kGroup + row) * 16);
+      if constexpr (BITS == 2) {
+        // two blocks per chunk: both scales in one word (0 for a block past K), both
+        // zero-point bytes in the low two bytes
+        const int kb0 = 2 * ccl, kb1 = min(2 * ccl + 1, p.KB - 1);
+        const uint32_t s1 = 2 * ccl + 1 < p.KB ? p.sc[(tile0 + kb1) * kGroup + row] : 0u;
+        sraw[i] = p.sc[(tile0 + kb0) * kGroup + row] | (s1 << 16);
+        zraw[i] = 0;
+        if constexpr (HAS_ZP)
+          zraw[i] = p.zp[(tile0 + kb0) * 16 + (row >> 2)] | ((uint32_t)p.zp[(tile0 + kb1) * 16 + (row >> 2)] << 8);
+      } else {
+        const size_t tile = tile0 + ccl / (BITS / 4);
+        sraw[i] = p.sc[tile * kGroup + row];
+        zraw[i] = 0;
+        if constexpr (HAS_ZP) {
+          if constexpr (BITS == 4) zraw[i] = p.zp[tile * 32 + (row >> 1)];
+          else zraw[i] = p.zp[tile * kGroup + row];
+        }
       }
     }
     // 2. this wave's X: slot j = i*Q + qi holds the KPC values of chunk-column
@@ -356,8 +365,13 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       const int j = pc / (KPC / 8), sub = pc % (KPC / 8);
       const int i = j / Q, q = j % Q;
       const int cc = (l0 + wave + kWaves * i) * Q + q;
-      const int k = cc < ncc ? cc * KPC + sub * 8 : 0;
-      *reinterpret_cast<u4_t *>(&xs[wave][pc * 8]) = *reinterpret_cast<const u4_t *>(xrow + k);
+      // (2-bit: the second block of the last chunk of an odd block count lies past K; its
+      // X is staged as zeros, its scale is 0)
+      const int k = cc * KPC + sub * 8;
+      const bool kin = cc < ncc && k < p.K;
+      u4_t xv = *reinterpret_cast<const u4_t *>(xrow + (kin ? k : 0));
+      if (!kin) xv = u4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u4_t *>(&xs[wave][pc * 8]) = xv;
     }
     // 3. arithmetic (xs[wave] is written and read by this wave only: LDS order suffices)
 #pragma unroll
@@ -366,6 +380,33 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       const int cc = l * Q + qi;
       if (l < lend && cc < ncc) {
         const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xs[wave][(i * Q + qi) * KPC]);
+        if constexpr (BITS == 2) {
+          // two blocks; in each 32-bit word the four 2-bit field pairs of a byte are taken
+          // in place (v_bfi_b32): pair e comes out as 4^e (q - z), exact, into its own
+          // accumulator pe, which a power-of-two FP32 rescale puts back exactly
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            uint32_t z = 2u;
+            if constexpr (HAS_ZP) z = ((zraw[i] >> (8 * h)) >> ((row & 3) * 2)) & 3u;
+            float pe[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const u4_t xa = *reinterpret_cast<const u4_t *>(xw + 16 * h + 8 * j);
+              const u4_t xb = *reinterpret_cast<const u4_t *>(xw + 16 * h + 8 * j + 4);
+              const uint32_t w = cw[i][2 * h + j], w8 = w >> 8;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t mask = 0x00030003u << (2 * e);
+                const h2_t zz = as_h2(((z << (2 * e)) * 0x00010001u) | 0x64006400u);   // 1024 + 4^e z
+                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w, 0x64006400u)) - zz, as_h2(xa[e]), pe[e], false);
+                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w8, 0x64006400u)) - zz, as_h2(xb[e]), pe[e], false);
+              }
+            }
+            const float blk = pe[0] + pe[1] * 0.25f + pe[2] * 0.0625f + pe[3] * 0.015625f;
+            acc = fmaf(blk, h2f((uint16_t)(sraw[i] >> (16 * h))), acc);
+          }
+          continue;
+        }
         uint32_t z = 1u << (BITS - 1);
         if constexpr (HAS_ZP) z = BITS == 4 ? (zraw[i] >> ((row & 1) * 4)) & 0xFu : zraw[i];
         const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);   // 1024 + z, both halves
@@ -474,7 +515,7 @@ hipError_t launch3(int lora, int tmode, const GemvParams &p, int lpw, int gx, in
 }
 
 int loads_per_wave(int K, int bits, int q) {
-  const int ncc = (K / kBlock) * (bits / 4);
+  const int ncc = chunk_cols(bits, K / kBlock);
   const int nloads = (ncc + q - 1) / q;
   const int lpw = (nloads + kWaves - 1) / kWaves;
   return lpw <= 2 ? 2 : (lpw <= 4 ? 4 : 8);
@@ -497,10 +538,10 @@ int gemv_rows_split(int N, bool inpass_t) {
 
 size_t gemv_lds_bytes(int K, int bits, int q) {
   const int lpw = loads_per_wave(K, bits, q);
-  const int ncc = (K / kBlock) * (bits / 4);
+  const int ncc = chunk_cols(bits, K / kBlock);
   const int nloads = (ncc + q - 1) / q;
   const int per_round = std::min(nloads, kWaves * lpw);
-  const int kpc = 32 / (bits / 4);
+  const int kpc = bits == 2 ? 64 : 32 / (bits / 4);
   return (size_t)per_round * q * kpc * sizeof(uint16_t);
 }
 
@@ -508,6 +549,9 @@ hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvPar
                        hipStream_t s) {
   const int lpw = loads_per_wave(p.K, bits, p.q);
   const size_t lds = gemv_lds_bytes(p.K, bits, p.q);
+  if (bits == 2)
+    return has_zp ? launch3<2, true>(lora, tmode, p, lpw, grid_x, grid_y, lds, s)
+                  : launch3<2, false>(lora, tmode, p, lpw, grid_x, grid_y, lds, s);
   if (bits == 4)
     return has_zp ? launch3<4, true>(lora, tmode, p, lpw, grid_x, grid_y, lds, s)
                   : launch3<4, false>(lora, tmode, p, lpw, grid_x, grid_y, lds, s);

@@ -28,9 +28,8 @@ constexpr int kXHalfs = 4096;    // MR x (X halfs per wave per round) <= this: 8
 
 template <int BITS, int MR, int Q, int LPW>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int lora) {
-  constexpr int C = BITS / 4;       // 16-byte chunks per block and row
   constexpr int R = kGroup / Q;     // rows per workgroup
-  constexpr int KPC = 32 / C;       // k values per chunk (32 for 4-bit, 16 for 8-bit)
+  constexpr int KPC = BITS == 2 ? 64 : 32 / (BITS / 4);   // k per chunk: 64, 32 or 16
   constexpr int XW = LPW * Q * KPC; // halfs of X one wave needs per round and row
   static_assert(MR * XW <= kXHalfs, "X staging size");
   __shared__ float red[MR][kWaves][kGroup];
@@ -54,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
   const int n = g * kGroup + row;       // this lane's output column
   const bool has_zp = p.zp != nullptr;
 
-  const int ncc = p.KB * C;             // chunk-columns per row
+  const int ncc = chunk_cols(BITS, p.KB); // chunk-columns per row
   const int nloads = (ncc + Q - 1) / Q; // wave loads per workgroup
   const size_t tile0 = (size_t)g * p.KB;
   const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
@@ -73,15 +72,27 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
       const int l = l0 + wave + kWaves * i;
       const int cc = l * Q + qi;
       const bool ok = l < lend && cc < ncc;
-      const int kb = ok ? cc / C : 0;
-      const int c = ok ? cc - kb * C : 0;
-      const size_t tile = tile0 + kb;
-      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + ((tile * C + c) * kGroup + row) * 16);
-      sraw[i] = p.sc[tile * kGroup + row];
-      zraw[i] = 1u << (BITS - 1);
-      if (has_zp) {
-        if constexpr (BITS == 4) zraw[i] = (p.zp[tile * 32 + (row >> 1)] >> ((row & 1) * 4)) & 0xFu;
-        else zraw[i] = p.zp[tile * kGroup + row];
+      const int ccl = ok ? cc : 0;
+      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + (((size_t)g * ncc + ccl) * kGroup + row) * 16);
+      if constexpr (BITS == 2) {
+        // two blocks per chunk: scales (0 for a block past K) and zero points of both
+        const int kb0 = 2 * ccl, kb1 = min(2 * ccl + 1, p.KB - 1);
+        const uint32_t s1 = 2 * ccl + 1 < p.KB ? p.sc[(tile0 + kb1) * kGroup + row] : 0u;
+        sraw[i] = p.sc[(tile0 + kb0) * kGroup + row] | (s1 << 16);
+        zraw[i] = 2u | (2u << 8);
+        if (has_zp) {
+          const int sh = (row & 3) * 2;
+          zraw[i] = ((p.zp[(tile0 + kb0) * 16 + (row >> 2)] >> sh) & 3u) |
+                    (((uint32_t)(p.zp[(tile0 + kb1) * 16 + (row >> 2)] >> sh) & 3u) << 8);
+        }
+      } else {
+        const size_t tile = tile0 + ccl / (BITS / 4);
+        sraw[i] = p.sc[tile * kGroup + row];
+        zraw[i] = 1u << (BITS - 1);
+        if (has_zp) {
+          if constexpr (BITS == 4) zraw[i] = (p.zp[tile * 32 + (row >> 1)] >> ((row & 1) * 4)) & 0xFu;
+          else zraw[i] = p.zp[tile * kGroup + row];
+        }
       }
     }
     // 2. this wave's X for MR rows: slot j = i*Q + qi holds the KPC values of
@@ -93,9 +104,12 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
       const int j = pp / (KPC / 8), sub = pp % (KPC / 8);
       const int i = j / Q, q = j % Q;
       const int cc = (l0 + wave + kWaves * i) * Q + q;
-      const int k = cc < ncc ? cc * KPC + sub * 8 : 0;
+      const int k = cc * KPC + sub * 8;
+      const bool kin = cc < ncc && k < p.K;     // (2-bit: past K in the last chunk -> zeros)
       const _Float16 *xrow = X + (size_t)min(m0 + r, p.M - 1) * p.K;
-      *reinterpret_cast<u4_t *>(&xs[wave][r][pp * 8]) = *reinterpret_cast<const u4_t *>(xrow + k);
+      u4_t xv = *reinterpret_cast<const u4_t *>(xrow + (kin ? k : 0));
+      if (!kin) xv = u4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u4_t *>(&xs[wave][r][pp * 8]) = xv;
     }
     // 3. arithmetic: exact (q - z) pairs once per word, dotted with MR rows of X
 #pragma unroll
@@ -103,6 +117,34 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
       const int l = l0 + wave + kWaves * i;
       const int cc = l * Q + qi;
       if (l < lend && cc < ncc) {
+        if constexpr (BITS == 2) {
+          // two blocks of 32 k = 16 pairs each
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const h2_t zzh = as_h2((((zraw[i] >> (8 * h)) & 3u) * 0x00010001u) | 0x64006400u);
+            h2_t d[16];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) d[8 * j + e] = crumb_pair(cw[i][2 * h + j], e) - zzh;
+            const float sh = h2f((uint16_t)(sraw[i] >> (16 * h)));
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+              const u4_t *xv = reinterpret_cast<const u4_t *>(&xs[wave][r][(i * Q + qi) * KPC + 32 * h]);
+              float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u4_t x4 = xv[j];
+                q0 = __builtin_amdgcn_fdot2(d[4 * j], as_h2(x4[0]), q0, false);
+                q1 = __builtin_amdgcn_fdot2(d[4 * j + 1], as_h2(x4[1]), q1, false);
+                q0 = __builtin_amdgcn_fdot2(d[4 * j + 2], as_h2(x4[2]), q0, false);
+                q1 = __builtin_amdgcn_fdot2(d[4 * j + 3], as_h2(x4[3]), q1, false);
+              }
+              acc[r] = fmaf(q0 + q1, sh, acc[r]);
+            }
+          }
+          continue;
+        }
         const h2_t zz2 = as_h2((zraw[i] * 0x00010001u) | 0x64006400u);   // 1024 + z, both halves
         if constexpr (BITS == 4) {
           // 4-bit: one chunk = one block = 32 k = 16 pairs
@@ -210,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvParams p, int l
 
 template <int BITS, int MR, int Q>
 hipError_t launch_q(const GemvParams &p, int lora, int lpw, int gx, int gy, hipStream_t s) {
-  constexpr int KPC = 32 / (BITS / 4);
+  constexpr int KPC = BITS == 2 ? 64 : 32 / (BITS / 4);
   constexpr int kCap = kXHalfs / (MR * Q * KPC);   // largest LPW whose X staging fits
   constexpr int kCapP2 = kCap >= 8 ? 8 : kCap >= 4 ? 4 : kCap >= 2 ? 2 : 1;
   const int want = lpw <= 1 ? 1 : lpw <= 2 ? 2 : lpw <= 4 ? 4 : 8;   // one round if it fits
@@ -238,20 +280,23 @@ hipError_t launch_mr(const GemvParams &p, int lora, int lpw, int gx, int gy, hip
 template <int BITS>
 hipError_t launch_bits(const GemvParams &p, int lora, int mr, int lpw, int gx, int gy, hipStream_t s) {
   if (mr <= 4) return launch_mr<BITS, 4>(p, lora, lpw, gx, gy, s);
-  if (mr <= 8) return launch_mr<BITS, 8>(p, lora, lpw, gx, gy, s);
-  return launch_mr<BITS, 16>(p, lora, lpw, gx, gy, s);
+  if (mr <= 8 || BITS == 2) return launch_mr<BITS, 8>(p, lora, lpw, gx, gy, s);
+  if constexpr (BITS != 2) return launch_mr<BITS, 16>(p, lora, lpw, gx, gy, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int gemv_rows_mr(int M) { return M <= 4 ? 4 : (M <= 8 ? 8 : 16); }
+// rows per workgroup; 2-bit stops at 8 (its 64-k chunks would not fit 16 rows of X in LDS)
+int gemv_rows_mr(int M, int bits) { return M <= 4 ? 4 : (M <= 8 || bits == 2 ? 8 : 16); }
 
 hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s) {
-  const int mr = gemv_rows_mr(p.M);
-  const int ncc = p.KB * (bits / 4);
+  const int mr = gemv_rows_mr(p.M, bits);
+  const int ncc = chunk_cols(bits, p.KB);
   const int nloads = (ncc + p.q - 1) / p.q;
   const int lpw = (nloads + kWaves - 1) / kWaves;
   const int gy = (p.M + mr - 1) / mr;
+  if (bits == 2) return launch_bits<2>(p, lora, mr, lpw, grid_x, gy, s);
   return bits == 4 ? launch_bits<4>(p, lora, mr, lpw, grid_x, gy, s) : launch_bits<8>(p, lora, mr, lpw, grid_x, gy, s);
 }
 

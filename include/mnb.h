@@ -11,7 +11,9 @@
  * adapters, base + (X.A).B, empty adapters run the base projection only) and
  * "Fuse DQ->MatMulNBits for shared initializers and skip outer-scope weights" (PR #33800:
  * Description -- MatMulNBits equals DequantizeLinear followed by MatMul; 8-bit weights with
- * block scales and uint8 zero points for a tied lm_head).
+ * block scales and uint8 zero points for a tied lm_head).  Both pages run MatMulNBits with
+ * 2-, 4- and 8-bit weights (PR #33370's file list and its split-out empty-weights change test
+ * 2/4/8-bit cases); all three widths are supported here.
  *
  * Conventions for every call:
  *  - fp16 tensors are IEEE binary16 bit patterns, passed as (const) void *.
@@ -43,7 +45,7 @@ extern "C" {
 enum {
   MNB_OK = 0,
   MNB_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
-  MNB_ERR_UNSUPPORTED = 2,  /* bits not 4/8, block not 32, K % 32 != 0, rank not 0/32 */
+  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, rank not 0/32 */
   MNB_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned */
   MNB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than mnb_workspace_bytes() */
   MNB_ERR_ALIAS = 5,        /* Y overlaps an input or the workspace */
@@ -97,9 +99,10 @@ typedef struct mnb_options {
 
 /*
  * Sizes in bytes of the packed weight buffers for an N x K weight (host only, no device
- * call).  block must be 32; bits 4 or 8; has_zp selects whether a zero-point buffer exists.
- * Layout (this library's own): rows grouped by 64 (padded), K in blocks of 32:
- *   wq: ceil(N/64) * (K/32) * 64 * 16 * (bits/4) bytes
+ * call).  block must be 32; bits 2, 4 or 8; has_zp selects whether a zero-point buffer
+ * exists.  Layout (this library's own): rows grouped by 64 (padded), K in blocks of 32:
+ *   wq: ceil(N/64) * CC * 64 * 16 bytes, CC = 16-byte chunks per row = (K/32) * bits/4
+ *       for 4 and 8 bits, ceil((K/32) / 2) for 2 bits (two blocks per chunk)
  *   sc: ceil(N/64) * (K/32) * 64 * 2 bytes
  *   zp: ceil(N/64) * (K/32) * 64 * bits/8 bytes, or 0 without zero points
  */
@@ -154,12 +157,12 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank);
  * Y[M,N] = X . deq(W)^T (+ (X.A).B), fp16 output rounded to nearest even once, from FP32
  * accumulation.
  *   X      fp16 [M, K] row-major
- *   wq, sc, zpp   packed by mnb_pack (zpp NULL: default zero point 2^(bits-1), i.e. 8 for
- *                 4-bit, 128 for 8-bit)
+ *   wq, sc, zpp   packed by mnb_pack (zpp NULL: default zero point 2^(bits-1), i.e. 2 for
+ *                 2-bit, 8 for 4-bit, 128 for 8-bit)
  *   ad     adapter or NULL (see mnb_adapter for when it counts as empty)
  *   Y      fp16 [M, N] row-major; must not overlap X, wq, sc, zpp, the adapter or the
  *          workspace (MNB_ERR_ALIAS)
- *   bits 4 or 8, block 32, K % 32 == 0
+ *   bits 2, 4 or 8, block 32, K % 32 == 0
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
  * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV

@@ -74,7 +74,8 @@ PATHS = [(0, 0, "auto"), (1, 0, "gemv"), (1, 1, "gemv_tsep"), (2, 0, "gemm")]
 
 @pytest.mark.parametrize("N,K,bits,zp", [(1, 32, 4, True), (64, 64, 4, False), (100, 96, 8, True),
                                           (130, 160, 4, True), (896, 896, 4, True), (8192, 2048, 4, False),
-                                          (49152, 576, 8, True), (257, 1024, 8, False)])
+                                          (49152, 576, 8, True), (257, 1024, 8, False), (70, 96, 2, True),
+                                          (130, 160, 2, False), (8192, 2048, 2, True), (5, 32, 2, True)])
 def test_pack_matches_oracle_bytes(N, K, bits, zp):
     case = si.make_random(11, 1, N, K, bits, zp, None)
     pw = dev_weight(case)
@@ -94,7 +95,7 @@ def test_pack_matches_oracle_bytes(N, K, bits, zp):
 
 @pytest.mark.parametrize("N,K,bits,zp", [(1, 32, 4, True), (70, 96, 4, False), (100, 96, 8, True),
                                           (130, 160, 4, True), (49152, 576, 8, True), (4096, 4096, 4, True),
-                                          (257, 1024, 8, False)])
+                                          (257, 1024, 8, False), (66, 96, 2, True), (4096, 4096, 2, False)])
 def test_pack_from_dq_layout_matches_oracle_bytes(N, K, bits, zp):
     """mnb_pack_kn ([K, N] codes, [K/32, N] scales and zero points, as DequantizeLinear
     holds them; the 576 x 49152 int8 case is the tied lm_head's own layout) against the
@@ -184,7 +185,7 @@ SHAPES = [(1, 64, 32), (1, 100, 96), (1, 1, 32), (3, 130, 160), (7, 32, 64), (2,
           (256, 384, 512), (1, 4096, 4096), (16, 96, 256), (9, 70, 192), (5, 513, 128), (17, 64, 96)]
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("zp", [True, False], ids=["zp", "zpdef"])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
 def test_small_shapes_all_paths(bits, zp, adapter):
@@ -199,15 +200,16 @@ def test_small_shapes_all_paths(bits, zp, adapter):
 SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
 
 
+@pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
-def test_gemm_split_k_ranges(adapter):
+def test_gemm_split_k_ranges(bits, adapter):
     """Shapes with fewer 128x128 tiles than CUs: the GEMM splits K into ranges (odd block
     counts, ragged M and N, N % 4 != 0 for the scalar reduction) and must still match."""
     for i, (M, N, K) in enumerate(SPLIT_SHAPES):
-        _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, {None: 0, "f16": 1, "q8": 2}[adapter],
+        _, desc = mnb.mnb_describe_route(M, N, K, bits, 1, {None: 0, "f16": 1, "q8": 2}[adapter],
                                          mnb.mnb_options(2, 0))
         assert not desc.endswith(" splits=1"), desc
-        case = si.make_random(190 + i, M, N, K, 4, i % 2 == 0, adapter, bias=i >= 2)
+        case = si.make_random(190 + i, M, N, K, bits, i % 2 == 0, adapter, bias=i >= 2)
         rows = list(range(M)) if M <= 64 else [0, 1, 127, 128, M - 1]
         compare(run(case, 2, 0)[rows], oracle.matmul(rows_case(case, rows)), what="split M=%d N=%d K=%d" % (M, N, K))
 
@@ -216,7 +218,7 @@ def test_gemm_split_k_ranges(adapter):
 # bit-exact pins on the GPU
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits,zp", [(4, True), (4, False), (8, True), (8, False)])
+@pytest.mark.parametrize("bits,zp", [(4, True), (4, False), (8, True), (8, False), (2, True), (2, False)])
 def test_one_hot_bit_exact(bits, zp):
     """X = rows of the identity: each output is one dequantized weight rounded once."""
     N, K = 200, 256
@@ -236,7 +238,8 @@ def exact_case(seed, M, N, K, bits, zp, kind, bias=False):
     for m in range(M):
         ks = r.choice(K, size=min(8, K), replace=False)
         X[m, ks] = r.choice([-2.0, -1.0, 1.0, 2.0], size=len(ks))
-    z = r.integers(0, 16, size=(N, K // 32)) if bits == 4 else r.integers(100, 157, size=(N, K // 32))
+    z = {2: r.integers(0, 4, size=(N, K // 32)), 4: r.integers(0, 16, size=(N, K // 32)),
+         8: r.integers(100, 157, size=(N, K // 32))}[bits]
     zfull = np.repeat(z if zp else np.full_like(z, 2 ** (bits - 1)), 32, axis=1)
     codes = (np.clip(zfull + r.integers(-15, 16, size=(N, K)), 0, 2 ** bits - 1)).astype(np.uint8)
     scales = np.full((N, K // 32), 0x3000, np.uint16)                  # 2^-3
@@ -254,7 +257,7 @@ def exact_case(seed, M, N, K, bits, zp, kind, bias=False):
                 zp=z.astype(np.uint8) if zp else None, adapter=ad, bias=b)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("kind", [None, "f16", "q8"], ids=["base", "f16", "q8"])
 @pytest.mark.parametrize("M", [1, 5, 130])
 def test_exact_arithmetic_bit_exact(bits, kind, M):
@@ -269,8 +272,8 @@ def test_exact_arithmetic_bit_exact(bits, kind, M):
 @pytest.mark.parametrize("M", [1, 6, 16, 130])
 def test_exact_arithmetic_with_bias_bit_exact(kind, M):
     """Bias multiples of 2^-3 keep every sum exact: each output is the exact value rounded once."""
-    for bits in (4, 8):
-        case = exact_case(170 + M + bits, M, 200, 320, bits, bits == 4, kind, bias=True)
+    for bits in (2, 4, 8):
+        case = exact_case(170 + M + bits, M, 200, 320, bits, bits != 8, kind, bias=True)
         want = oracle.f64_to_f16(oracle.matmul(case))
         pw = dev_weight(case)
         for path, flags, name in PATHS:
@@ -281,7 +284,7 @@ BIAS_SHAPES = [(1, 64, 32), (1, 100, 96), (3, 130, 160), (8, 257, 320), (13, 96,
                (129, 257, 320), (1, 4096, 2048)]
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
 def test_bias_small_shapes_all_paths(bits, adapter):
     for i, (M, N, K) in enumerate(BIAS_SHAPES):
@@ -334,7 +337,7 @@ def test_empty_and_zero_adapter_equal_base_bitwise(M):
 
 
 def test_code_equal_zero_point_gives_zero():
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         case = si.make_random(90 + bits, 3, 130, 256, bits, True, "f16")
         codes = np.repeat(case["zp"], 32, axis=1).astype(np.uint8)
         c = dict(case, codes=codes)
@@ -346,7 +349,7 @@ def test_code_equal_zero_point_gives_zero():
 
 
 def test_default_zero_point_equals_explicit():
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         case = si.make_random(95 + bits, 3, 130, 256, bits, False, "q8")
         explicit = dict(case, zp=np.full(case["scales"].shape, 2 ** (bits - 1), np.uint8))
         for path, flags, name in PATHS:
