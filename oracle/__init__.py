@@ -27,7 +27,7 @@ def load(path: str | None = None) -> C.CDLL:
                                os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
         _build.build()          # absent, or older than its source (a CPU build of seconds)
     lib = C.CDLL(path)
-    lib.mnbo_matmul.argtypes = [C.c_int] * 4 + [_P] * 4 + [C.c_int, C.c_int] + [_P] * 6
+    lib.mnbo_matmul.argtypes = [C.c_int] * 4 + [_P] * 4 + [C.c_int, C.c_int] + [_P] * 6 + [C.c_int]
     lib.mnbo_matmul.restype = C.c_int
     lib.mnbo_pack.argtypes = [C.c_int] * 3 + [_P] * 6
     lib.mnbo_pack.restype = C.c_int
@@ -67,7 +67,8 @@ def f64_to_f16(vals, lib=None) -> np.ndarray:
 
 
 def matmul(case: dict, lib=None) -> np.ndarray:
-    """FP64 Y[M,N] for a case dict (see ``seeded_inputs``)."""
+    """FP64 Y[M,N] for a case dict (see ``seeded_inputs``); ``acc_level`` 4 selects int8
+    block-quantized activations for the base product."""
     lib = lib or load()
     M, N, K, bits = case["M"], case["N"], case["K"], case["bits"]
     X = _c(case["X"], np.uint16)
@@ -91,7 +92,7 @@ def matmul(case: dict, lib=None) -> np.ndarray:
     bias = _c(case.get("bias"), np.uint16)
     Y = np.zeros((M, N), np.float64)
     rc = lib.mnbo_matmul(M, N, K, bits, _ptr(X), _ptr(codes), _ptr(scales), _ptr(zp), kind, rank,
-                         _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(bias), _ptr(Y))
+                         _ptr(A), _ptr(sA), _ptr(B), _ptr(sB), _ptr(bias), _ptr(Y), int(case.get("acc_level", 0)))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return Y

@@ -163,14 +163,51 @@ static double lora_b(int kind, const void *B, const uint16_t *sB, int N, int r, 
 }
 
 /*
+ * Accuracy level 4 (int8 activations for the base product; the PR #33370 page's commit
+ * list keeps "DP4A activation quantization for the base, with original FP16 X for T", and
+ * the PR #33800 page runs its lm_head at the default accuracy level 4).  The pages give no
+ * quantization rule; the reading taken here, per row and per block of 32 along K:
+ *   amax = max |x|  (FP32; every binary16 is exact in it)
+ *   amax == 0: every code 0;  else inv = 127 / amax, q = rint(x * inv) clamped to
+ *   [-127, 127] (FP32 division and multiplication, round to nearest even), sx = amax / 127
+ *   x' = q * sx  (exact in FP64), and the base product uses x' in place of x.
+ */
+static void quantize_block_acc4(const uint16_t *xh, double *xq) {
+  float amax = 0.0f;
+  for (int j = 0; j < BLK; ++j) {
+    float a = fabsf((float)h2d(xh[j]));
+    if (a > amax) amax = a;
+  }
+  if (amax == 0.0f) {
+    for (int j = 0; j < BLK; ++j) xq[j] = 0.0;
+    return;
+  }
+#if MNBO_MUTATION == 13
+  volatile float inv = 128.0f / amax;                /* planted: 128 levels instead of 127 */
+#else
+  volatile float inv = 127.0f / amax;
+#endif
+  volatile float sx = amax / 127.0f;
+  for (int j = 0; j < BLK; ++j) {
+    volatile float prod = (float)h2d(xh[j]) * inv;
+    float q = rintf(prod);
+    if (q > 127.0f) q = 127.0f;
+    if (q < -127.0f) q = -127.0f;
+    xq[j] = (double)q * (double)sx;
+  }
+}
+
+/*
  * Y[m,n] (FP64, row-major [M,N]).  X [M,K] binary16; codes [N,K] one per byte; scales
- * [N,K/32] binary16; zp [N,K/32] or NULL; kind 0 none / 1 F16 / 2 INT8; rank 0 or 32.
+ * [N,K/32] binary16; zp [N,K/32] or NULL; kind 0 none / 1 F16 / 2 INT8; rank 0 or 32;
+ * acc_level 0 (exact FP16 activations) or 4 (int8 activations for the base, above).
  * Returns 0, or -1 on unsupported arguments.
  */
 int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t *codes,
                 const uint16_t *scales, const uint8_t *zp, int kind, int rank, const void *A,
                 const uint16_t *A_scales, const void *B, const uint16_t *B_scales,
-                const uint16_t *bias, double *Y) {
+                const uint16_t *bias, double *Y, int acc_level) {
+  if (acc_level != 0 && acc_level != 4) return -1;
   if (M < 0 || N < 0 || K < 0 || K % BLK) return -1;
   if (bits != 2 && bits != 4 && bits != 8) return -1;
   int has_lora = kind != 0 && rank != 0 && A != NULL && B != NULL;
@@ -192,6 +229,15 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
 #endif
   }
 
+  /* step 1b (accuracy level 4): the base product's activations are quantized per block */
+  double *xb = x;
+  if (acc_level == 4) {
+    xb = (double *)malloc(sizeof(double) * ((size_t)M * K + 1));
+    for (int m = 0; m < M; ++m)
+      for (int b = 0; b < K / BLK; ++b)
+        quantize_block_acc4(X + (long)m * K + (long)b * BLK, xb + (long)m * K + (long)b * BLK);
+  }
+
   /* step 2: dequantize W to FP64 */
   double *w = (double *)malloc(sizeof(double) * ((size_t)N * K + 1));
 #pragma omp parallel for schedule(static)
@@ -202,7 +248,7 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
 #pragma omp parallel for collapse(2) schedule(static)
   for (int m = 0; m < M; ++m)
     for (int n = 0; n < N; ++n) {
-      const double *xr = x + (long)m * K, *wr = w + (long)n * K;
+      const double *xr = xb + (long)m * K, *wr = w + (long)n * K;
       double acc = 0.0;
       for (int k = 0; k < K; ++k) acc += xr[k] * wr[k];
       Y[(long)m * N + n] = acc;
@@ -220,7 +266,11 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
     for (int m = 0; m < M; ++m)
       for (int r = 0; r < 32; ++r) {
         double acc = 0.0;
+#if MNBO_MUTATION == 14
+        for (int k = 0; k < K; ++k) acc += xb[(long)m * K + k] * a[k * 32 + r];   /* planted: T from quantized X */
+#else
         for (int k = 0; k < K; ++k) acc += x[(long)m * K + k] * a[k * 32 + r];
+#endif
         t[m * 32 + r] = acc;
       }
 #pragma omp parallel for collapse(2) schedule(static)
@@ -246,6 +296,7 @@ int mnbo_matmul(int M, int N, int K, int bits, const uint16_t *X, const uint8_t 
         Y[(long)m * N + n] += h2d(bias[n]);
 #endif
       }
+  if (xb != x) free(xb);
   free(x);
   free(w);
   return 0;

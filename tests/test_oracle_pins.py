@@ -376,10 +376,63 @@ def pin_p5_closed_form_dq_layout(lib):
         assert abs(Fraction(float(got[m, 0])) - want) <= Fraction(bound)
 
 
+def _acc4_representable_x(r, M, K):
+    """X whose every block is c * 2^-e with integer |c| <= 127, max |c| = 127 (or all zero):
+    then 127 / amax = 2^e and amax / 127 = 2^-e exactly, so block quantization is lossless."""
+    X = np.zeros((M, K), np.float64)
+    for m in range(M):
+        for b in range(K // 32):
+            if (m + b) % 7 == 3:
+                continue                                   # an all-zero block
+            c = r.integers(-127, 128, size=32)
+            c[r.integers(0, 32)] = 127 * (1 if r.integers(0, 2) else -1)
+            X[m, 32 * b:32 * b + 32] = c * 2.0 ** -int(r.integers(7, 13))
+    return si.to_f16_bits(X)
+
+
+def pin_acc4_lossless_when_representable(lib):
+    """Accuracy level 4 on activations that block quantization represents exactly equals
+    the FP16-activation result bit for bit (same products, same order)."""
+    r = np.random.default_rng(44)
+    for bits, zp, ad in ((4, True, "f16"), (8, True, None), (2, False, "q8"), (4, False, None)):
+        case = si.make_random(440 + bits, 3, 37, 160, bits, zp, ad)
+        case["X"] = _acc4_representable_x(r, 3, 160)
+        assert np.array_equal(oracle.matmul(dict(case, acc_level=4), lib), oracle.matmul(case, lib))
+
+
+def pin_acc4_error_bound(lib):
+    """Round-to-nearest block quantization moves each activation by at most half a step
+    (sx / 2, sx = amax / 127 in FP32): |Y4 - Y| <= sum_k |w[n,k]| sx(k) / 2, and it does move
+    random activations."""
+    for bits, zp in ((4, True), (8, True), (2, False)):
+        case = si.make_random(450 + bits, 3, 41, 192, bits, zp, None)
+        y0 = oracle.matmul(case, lib)
+        y4 = oracle.matmul(dict(case, acc_level=4), lib)
+        x = _f16(case["X"])
+        amax = np.abs(x.reshape(3, -1, 32)).max(axis=2).astype(np.float32)
+        step = np.repeat((amax / np.float32(127.0)).astype(np.float64), 32, axis=1)        # [M, K]
+        z = case["zp"].astype(np.float64) if zp else np.full(case["scales"].shape, 2.0 ** (bits - 1))
+        W = np.abs((case["codes"] - np.repeat(z, 32, axis=1)) * np.repeat(_f16(case["scales"]), 32, axis=1))
+        bound = (step / 2) @ W.T
+        assert np.all(np.abs(y4 - y0) <= bound * (1 + 1e-9) + 1e-12)
+        assert np.any(y4 != y0)
+
+
+def pin_acc4_lora_uses_fp16_x(lib):
+    """With all codes equal to their zero points the base is exactly 0 at any accuracy
+    level, so accuracy level 4 leaves exactly the LoRA term, which takes the original FP16
+    X (PR #33370 page, commit list)."""
+    for kind in ("f16", "q8"):
+        case = si.make_random(460, 2, 30, 96, 4, True, kind)
+        case["codes"] = np.repeat(case["zp"], 32, axis=1).astype(np.uint8)
+        assert np.array_equal(oracle.matmul(dict(case, acc_level=4), lib), oracle.matmul(case, lib))
+
+
 PINS = [pin_exact_bruteforce, pin_numpy_dq_matmul, pin_p5_closed_form, pin_one_hot,
         pin_code_equals_zero_point, pin_empty_and_zero_adapter, pin_superposition,
         pin_default_zero_point, pin_q8_equals_f16, pin_pack_layout, pin_pack_roundtrip,
-        pin_empty_weights_bias, pin_pack_from_dq_layout, pin_p5_closed_form_dq_layout]
+        pin_empty_weights_bias, pin_pack_from_dq_layout, pin_p5_closed_form_dq_layout,
+        pin_acc4_lossless_when_representable, pin_acc4_error_bound, pin_acc4_lora_uses_fp16_x]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -423,7 +476,8 @@ MUTATIONS = {1: "zero-point sign", 2: "LoRA term dropped", 3: "scale index trans
              4: "block index off by one", 5: "A transposed", 6: "default zero point 0",
              7: "natural nibble order", 8: "X transposed", 9: "B transposed",
              10: "INT8 A scale ignores rank column", 11: "bias indexed by the row",
-             12: "DQ-layout scales not transposed"}
+             12: "DQ-layout scales not transposed", 13: "acc4 with 128 levels",
+             14: "acc4 T from quantized X"}
 
 
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS), ids=lambda m: MUTATIONS[m])
