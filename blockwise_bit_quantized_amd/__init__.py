@@ -24,7 +24,7 @@ MNB_OK, MNB_ERR_INVALID_ARG, MNB_ERR_UNSUPPORTED, MNB_ERR_MISALIGNED = 0, 1, 2, 
 MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP = 4, 5, 6
 MNB_ADAPTER_NONE, MNB_ADAPTER_F16, MNB_ADAPTER_Q8 = 0, 1, 2
 MNB_PATH_AUTO, MNB_PATH_GEMV, MNB_PATH_GEMM = 0, 1, 2
-MNB_FLAG_T_SEPARATE = 1
+MNB_FLAG_T_SEPARATE, MNB_FLAG_ACC4 = 1, 2
 
 
 class mnb_adapter(C.Structure):

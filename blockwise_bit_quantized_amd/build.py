@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmnb.so")
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "gemv.hip", "gemv_rows.hip", "tproj.hip", "gemm.hip", "pack.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemv_rows.hip", "gemv_acc4.hip", "tproj.hip", "gemm.hip", "pack.hip"]
 ARCH = os.environ.get("MNB_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

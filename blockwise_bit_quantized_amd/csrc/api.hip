@@ -61,6 +61,7 @@ struct Route {
   int lora;      // LORA_*
   int tmode;     // 0 in-pass, 1 precomputed by the T projection launch
   bool tproj;
+  bool acc4;     // int8 activations for the base product (GEMV family, every M)
 };
 
 Route route(int M, int lora, const mnb_options *opt) {
@@ -73,6 +74,12 @@ Route route(int M, int lora, const mnb_options *opt) {
   r.lora = lora;
   r.tmode = 1;
   r.tproj = false;
+  r.acc4 = (flags & MNB_FLAG_ACC4) != 0;
+  if (r.acc4) {
+    r.path = MNB_PATH_GEMV;
+    r.tproj = lora != 0;
+    return r;
+  }
   if (lora) {
     if (r.path == MNB_PATH_GEMV && M == 1 && !(flags & MNB_FLAG_T_SEPARATE)) r.tmode = 0;
     else r.tproj = true;
@@ -113,7 +120,8 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
   if (st) return st;
   if (opt) {
     if (opt->path < MNB_PATH_AUTO || opt->path > MNB_PATH_GEMM) return MNB_ERR_INVALID_ARG;
-    if (opt->flags & ~MNB_FLAG_T_SEPARATE) return MNB_ERR_INVALID_ARG;
+    if (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4)) return MNB_ERR_INVALID_ARG;
+    if ((opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
   }
   if (ad) {
     if (ad->kind < MNB_ADAPTER_NONE || ad->kind > MNB_ADAPTER_Q8 || ad->rank < 0) return MNB_ERR_INVALID_ARG;
@@ -152,7 +160,12 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   const char *ln = r.lora == LORA_NONE ? "none" : (r.lora == LORA_F16 ? "f16" : "q8");
   char tp[96] = "";
   if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tmt * w.tparts, w.tparts);
-  if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
+  if (r.acc4) {
+    const int NG = cdiv(N, kGroup);
+    const int q = gemv_rows_split(N, false);
+    snprintf(buf, len, "%sgemv_acc4_b%d_zp%s_%s grid=%dx%d rows=%d q=%d", tp, bits, has_zp ? "x" : "def", ln, NG * q, M,
+             kGroup / q, q);
+  } else if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
     const int NG = cdiv(N, kGroup);
     const int q = gemv_rows_split(N, false);
     const int mr = gemv_rows_mr(M, bits);
@@ -265,7 +278,9 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
   int st = check_common(M, N, K, bits, kBlock);
   if (st) return st;
   if (has_adapter_kind < 0 || has_adapter_kind > 2 || !buf || buf_len == 0) return MNB_ERR_INVALID_ARG;
-  if (opt && (opt->path < 0 || opt->path > 2 || (opt->flags & ~MNB_FLAG_T_SEPARATE))) return MNB_ERR_INVALID_ARG;
+  if (opt && (opt->path < 0 || opt->path > 2 || (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4))))
+    return MNB_ERR_INVALID_ARG;
+  if (opt && (opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) {
     snprintf(buf, buf_len, "noop");
     return MNB_OK;
@@ -354,6 +369,21 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);
     p.tin = tproj_out;
     p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
+    if (r.acc4) {
+      // accuracy level 4: one X row per workgroup row (T from the projection launch)
+      p.gt = 0;
+      p.q = gemv_rows_split(N, false);
+      for (int m0 = 0; m0 < M; m0 += 65535) {
+        const int mc = std::min(65535, M - m0);
+        GemvParams q = p;
+        q.X = p.X + (size_t)m0 * K;
+        q.Y = p.Y + (size_t)m0 * N;
+        if (tproj_out) q.tin = tproj_out + (size_t)m0 * kRank;
+        q.M = mc;
+        if (launch_gemv_acc4(bits, has_zp, lora, q, NG * p.q, mc, s) != hipSuccess) return MNB_ERR_HIP;
+      }
+      return MNB_OK;
+    }
     if (M > 1 && M <= kRowsMaxM) {
       // small M: one pass over the weights for all rows (T from the projection launch)
       p.M = M;

@@ -180,6 +180,10 @@ struct PackParams {
 hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p,
                        int grid_x, int grid_y, hipStream_t s);
 hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s);
+// accuracy level 4 (int8 block-quantized activations for the base product), any M
+constexpr int kAcc4MaxK = 16384;
+hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
+                            hipStream_t s);
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
 int gemm_splits(int M, int N, int K);         // K ranges per output tile of the prefill GEMM

@@ -1,0 +1,291 @@
+// gemv_acc4.hip -- MatMulNBits at accuracy level 4: the base product takes int8
+// block-quantized activations and integer dot products (v_dot4_i32_i8), the rank-32 LoRA
+// term keeps the original FP16 X (T from the T projection launch).
+//
+// onnxruntime PR #33370 ("[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits"), commit
+// list: DP4A activation quantization for the base, original FP16 X for T; PR #33800
+// ("Fuse DQ->MatMulNBits ...", Description): the lm_head runs at the default accuracy level
+// 4.  The pages give no quantization rule; the one used (per row, per block of 32 along
+// K): amax = max |x| in FP32, inv = 127 / amax, q = rint(x * inv) clamped to [-127, 127],
+// sx = amax / 127, all FP32 with round to nearest even; an all-zero block has q = 0.
+//
+// Per workgroup (8 waves, one X row, 64/Q weight rows of one 64-row group, as the decode
+// GEMV):
+//  * each thread loads its 16-byte pieces of the X row first, then the weight stream;
+//  * the X row is quantized into LDS: four threads share a block (max and sum by lane
+//    exchange); the int8 codes are stored in the byte order the weight codes unpack to
+//    (4-bit: (w & 0x0F0F0F0F) holds k 0, 4, 1, 5 of a word, (w >> 4) & .. k 2, 6, 3, 7;
+//    2-bit: (w >> 2e) & 0x03030303 holds k 2e, 8+2e, 2e+1, 9+2e; 8-bit: natural order),
+//    with sx per block and the code sum per 16 k;
+//  * per 16-byte chunk: exact int32 sums of q_w * q_x by v_dot4_i32_i8 (8-bit codes as
+//    q - 128), minus z_eff * sum(q_x) (z_eff = z, or z - 128 for 8-bit), so the partial
+//    is the exact integer sum of (q - z) * q_x; it is scaled once by sx * s in FP32.
+#include "common.h"
+
+namespace mnb {
+namespace {
+
+enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+
+// byte position of k within its 32-k block in the quantized-X layout of each code width
+template <int BITS>
+__device__ __forceinline__ int xq_pos(int t) {
+  if constexpr (BITS == 4) {          // word j = t / 8: bytes x0 x4 x1 x5 | x2 x6 x3 x7
+    const int j = t >> 3, u = t & 7;
+    return 8 * j + 2 * (u & 3) + (u >> 2);
+  } else if constexpr (BITS == 2) {   // word j = t / 16: groups e of x 2e, 8+2e, 2e+1, 9+2e
+    const int j = t >> 4, u = t & 15;
+    return 16 * j + 4 * ((u & 7) >> 1) + (u >= 8 ? 1 : 0) + ((u & 1) ? 2 : 0);
+  } else {
+    return t;
+  }
+}
+
+template <int BITS, bool HAS_ZP, int LORA, int Q, int LPW>
+__global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
+  constexpr int R = kGroup / Q;                                   // rows per workgroup
+  constexpr int KPC = BITS == 2 ? 64 : 32 / (BITS / 4);           // k per chunk
+  __shared__ float red[kWaves][kGroup];
+  __shared__ __attribute__((aligned(16))) int8_t xq[kAcc4MaxK];   // quantized X row
+  __shared__ float sxs[kAcc4MaxK / 32];                           // sx per block
+  __shared__ int sqs[kAcc4MaxK / 16];                             // sum of codes per 16 k
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = blockIdx.y;
+  int wgi = blockIdx.x;
+  if (Q > 1 && (p.NG & 7) == 0) {
+    const int x = wgi & 7, u = wgi >> 3;
+    wgi = (x + 8 * (u / Q)) * Q + (u % Q);
+  }
+  const int g = wgi / Q;
+  const int rowoff = (wgi - g * Q) * R;
+  const int rl = lane % R, qi = lane / R;
+  const int row = rowoff + rl;
+  const int n = g * kGroup + row;
+  const int ncc = chunk_cols(BITS, p.KB);
+  const int nloads = (ncc + Q - 1) / Q;
+  const size_t tile0 = (size_t)g * p.KB;
+  const _Float16 *xrow = reinterpret_cast<const _Float16 *>(p.X) + (size_t)m * p.K;
+
+  // 1. this thread's X pieces (8 halfs each) first: their wait then does not wait for the
+  //    weight stream issued after them
+  constexpr int kMaxPieces = kAcc4MaxK / 8 / kThreads;
+  const int npieces = p.K / 8;
+  u4_t xv[kMaxPieces];
+#pragma unroll
+  for (int i = 0; i < kMaxPieces; ++i) {
+    const int pc = tid + i * kThreads;
+    xv[i] = *reinterpret_cast<const u4_t *>(xrow + 8 * (pc < npieces ? pc : 0));
+  }
+
+  float acc = 0.f;
+  for (int l0 = 0; l0 < nloads; l0 += kWaves * LPW) {
+    const int lend = min(nloads, l0 + kWaves * LPW);
+    // 2. weight stream of the round
+    u4_t cw[LPW];
+    uint32_t sraw[LPW], zraw[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int l = l0 + wave + kWaves * i;
+      const int cc = l * Q + qi;
+      const bool ok = l < lend && cc < ncc;
+      const int ccl = ok ? cc : 0;
+      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + (((size_t)g * ncc + ccl) * kGroup + row) * 16);
+      if constexpr (BITS == 2) {
+        const int kb0 = 2 * ccl, kb1 = min(2 * ccl + 1, p.KB - 1);
+        const uint32_t s1 = 2 * ccl + 1 < p.KB ? p.sc[(tile0 + kb1) * kGroup + row] : 0u;
+        sraw[i] = p.sc[(tile0 + kb0) * kGroup + row] | (s1 << 16);
+        zraw[i] = 2u | (2u << 8);
+        if constexpr (HAS_ZP) {
+          const int sh = (row & 3) * 2;
+          zraw[i] = ((p.zp[(tile0 + kb0) * 16 + (row >> 2)] >> sh) & 3u) |
+                    (((uint32_t)(p.zp[(tile0 + kb1) * 16 + (row >> 2)] >> sh) & 3u) << 8);
+        }
+      } else {
+        const size_t tile = tile0 + ccl / (BITS / 4);
+        sraw[i] = p.sc[tile * kGroup + row];
+        zraw[i] = 1u << (BITS - 1);
+        if constexpr (HAS_ZP) {
+          if constexpr (BITS == 4) zraw[i] = (p.zp[tile * 32 + (row >> 1)] >> ((row & 1) * 4)) & 0xFu;
+          else zraw[i] = p.zp[tile * kGroup + row];
+        }
+      }
+    }
+
+    // 3. quantize the X row into LDS (first round only); four consecutive threads hold
+    //    the four pieces of a block
+    if (l0 == 0) {
+#pragma unroll
+      for (int i = 0; i < kMaxPieces; ++i) {
+        const int pc = tid + i * kThreads;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const h2_t h = as_h2(xv[i][e]);
+          v[2 * e] = (float)h[0];
+          v[2 * e + 1] = (float)h[1];
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        const float inv = amax > 0.f ? 127.f / amax : 0.f;
+        int sum = 0;
+        int q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          q[e] = (int)fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
+          sum += q[e];
+        }
+        sum += __shfl_xor(sum, 1);     // the 16 k of this piece and its neighbour
+        if (pc < npieces) {
+          const int kb = pc >> 2, t0 = 8 * (pc & 3);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xq[32 * kb + xq_pos<BITS>(t0 + e)] = (int8_t)q[e];
+          if ((pc & 1) == 0) sqs[pc >> 1] = sum;
+          if ((pc & 3) == 0) sxs[kb] = amax / 127.f;
+        }
+      }
+      __syncthreads();
+    }
+
+    // 4. integer dot products per chunk, one FP32 scaling per block
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int l = l0 + wave + kWaves * i;
+      const int cc = l * Q + qi;
+      if (l < lend && cc < ncc) {
+        const int k0 = cc * KPC;                      // first k of the chunk
+        const int *xw = reinterpret_cast<const int *>(xq + k0);
+        if constexpr (BITS == 4) {
+          const int kb = cc;
+          int isum = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w = cw[i][j];
+            isum = __builtin_amdgcn_sdot4((int)(w & 0x0F0F0F0Fu), xw[2 * j], isum, false);
+            isum = __builtin_amdgcn_sdot4((int)((w >> 4) & 0x0F0F0F0Fu), xw[2 * j + 1], isum, false);
+          }
+          const int part = isum - (int)zraw[i] * (sqs[2 * kb] + sqs[2 * kb + 1]);
+          acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)sraw[i]), acc);
+        } else if constexpr (BITS == 2) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int kb = 2 * cc + h;
+            if (kb < p.KB) {
+              int isum = 0;
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const uint32_t w = cw[i][2 * h + j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  isum = __builtin_amdgcn_sdot4((int)((w >> (2 * e)) & 0x03030303u), xw[8 * h + 4 * j + e], isum, false);
+              }
+              const int z = (int)((zraw[i] >> (8 * h)) & 0xFFu);
+              const int part = isum - z * (sqs[2 * kb] + sqs[2 * kb + 1]);
+              acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)(sraw[i] >> (16 * h))), acc);
+            }
+          }
+        } else {
+          const int kb = cc >> 1;
+          int isum = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) isum = __builtin_amdgcn_sdot4((int)(cw[i][j] ^ 0x80808080u), xw[j], isum, false);
+          const int part = isum - ((int)zraw[i] - 128) * sqs[cc];
+          acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)sraw[i]), acc);
+        }
+      }
+    }
+  }
+
+  // lanes sharing a row, then waves, in fixed order
+  if constexpr (Q >= 8) acc += __shfl_xor(acc, 8);
+  if constexpr (Q >= 4) acc += __shfl_xor(acc, 16);
+  if constexpr (Q >= 2) acc += __shfl_xor(acc, 32);
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += red[w][rl];
+
+  const bool active = lane < R && n < p.N;
+  float lora = 0.f;
+  if constexpr (LORA != LORA_NONE) {
+    // T (FP32 partials per K-part of the projection launch, added in part order) from the
+    // original FP16 X; this lane's column of B
+    const float *src = p.tin + (size_t)m * kRank + (lane & 31);
+    float tv = 0.f;
+    for (int pp = 0; pp < p.tparts; ++pp) tv += src[(size_t)pp * p.tmpad * kRank];
+    const size_t nb = active ? n : 0;
+    float bscale = 1.f;
+    if constexpr (LORA == LORA_Q8) bscale = h2f(p.sB[nb]);
+#pragma unroll
+    for (int r = 0; r < kRank; ++r) {
+      const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
+      float b;
+      if constexpr (LORA == LORA_F16) b = h2f(static_cast<const uint16_t *>(p.B)[(size_t)r * p.N + nb]);
+      else b = (float)static_cast<const int8_t *>(p.B)[(size_t)r * p.N + nb];
+      lora = fmaf(tr, b, lora);
+    }
+    lora *= bscale;
+  }
+  if (active) {
+    float y = total + lora;
+    if (p.bias) y += h2f(p.bias[n]);
+    p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+  }
+}
+
+template <int BITS, bool HAS_ZP, int LORA, int Q>
+hipError_t launch_q4(const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
+  const dim3 grid(gx, gy), block(kThreads);
+  if (lpw <= 2) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 2>), grid, block, 0, s, p);
+  else if (lpw <= 4) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 4>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 8>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+template <int BITS, bool HAS_ZP, int LORA>
+hipError_t launch_l4(const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
+  switch (p.q) {
+    case 1: return launch_q4<BITS, HAS_ZP, LORA, 1>(p, lpw, gx, gy, s);
+    case 2: return launch_q4<BITS, HAS_ZP, LORA, 2>(p, lpw, gx, gy, s);
+    case 4: return launch_q4<BITS, HAS_ZP, LORA, 4>(p, lpw, gx, gy, s);
+    default: return launch_q4<BITS, HAS_ZP, LORA, 8>(p, lpw, gx, gy, s);
+  }
+}
+
+template <int BITS, bool HAS_ZP>
+hipError_t launch_z4(int lora, const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
+  switch (lora) {
+    case LORA_NONE: return launch_l4<BITS, HAS_ZP, LORA_NONE>(p, lpw, gx, gy, s);
+    case LORA_F16: return launch_l4<BITS, HAS_ZP, LORA_F16>(p, lpw, gx, gy, s);
+    default: return launch_l4<BITS, HAS_ZP, LORA_Q8>(p, lpw, gx, gy, s);
+  }
+}
+
+template <int BITS>
+hipError_t launch_b4(bool has_zp, int lora, const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
+  return has_zp ? launch_z4<BITS, true>(lora, p, lpw, gx, gy, s) : launch_z4<BITS, false>(lora, p, lpw, gx, gy, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
+                            hipStream_t s) {
+  if (p.K > kAcc4MaxK || p.K % kBlock) return hipErrorInvalidValue;
+  const int ncc = chunk_cols(bits, p.KB);
+  const int nloads = (ncc + p.q - 1) / p.q;
+  const int lpw = (nloads + kWaves - 1) / kWaves;
+  if (bits == 2) return launch_b4<2>(has_zp, lora, p, lpw, grid_x, grid_y, s);
+  if (bits == 4) return launch_b4<4>(has_zp, lora, p, lpw, grid_x, grid_y, s);
+  return launch_b4<8>(has_zp, lora, p, lpw, grid_x, grid_y, s);
+}
+
+}  // namespace mnb

@@ -64,7 +64,15 @@ enum {
   /* Decode (GEMV, M == 1) with an adapter normally computes T = X.A inside the same launch
    * as the base product.  This flag computes T in a separate launch first (two launches,
    * the structure of the pages' fuse_down), for comparison. */
-  MNB_FLAG_T_SEPARATE = 1
+  MNB_FLAG_T_SEPARATE = 1,
+  /* Accuracy level 4: the base product takes int8 activations, quantized per row and per
+   * block of 32 along K (amax = max |x|, q = rint(x * (127 / amax)) clamped to +-127,
+   * scale amax / 127, FP32), with integer dot products; the LoRA term keeps the FP16 X
+   * (PR #33370 commit list: DP4A activation quantization for the base, original FP16 X
+   * for T; PR #33800 Description: the lm_head at the default accuracy level 4).  Runs the
+   * GEMV family for every M (T from the projection launch when there is an adapter).
+   * Requires K <= 16384 and a path of AUTO or GEMV (MNB_ERR_UNSUPPORTED otherwise). */
+  MNB_FLAG_ACC4 = 2
 };
 
 /*

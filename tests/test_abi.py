@@ -148,6 +148,21 @@ def route(M, N=4096, K=4096, bits=4, zp=1, kind=1, path=0, flags=0):
     return text
 
 
+def test_accuracy_level4_route_and_validation():
+    A4 = mnb.MNB_FLAG_ACC4
+    assert route(1, flags=A4).startswith("tproj_f16") and "gemv_acc4_b4_zpx_f16" in route(1, flags=A4)
+    assert route(1, kind=0, flags=A4).startswith("gemv_acc4_b4_zpx_none")
+    assert "gemv_acc4" in route(1024, flags=A4) and "gemv_acc4" in route(5, bits=8, kind=0, flags=A4)
+    assert "gemv_acc4_b2" in route(3, bits=2, flags=A4, path=1)
+    st, _ = mnb.mnb_describe_route(4, 4096, 4096, 4, 1, 1, mnb.mnb_options(2, A4))
+    assert st == mnb.MNB_ERR_UNSUPPORTED                                    # forced GEMM
+    st, _ = mnb.mnb_describe_route(1, 64, 16416, 4, 1, 1, mnb.mnb_options(0, A4))
+    assert st == mnb.MNB_ERR_UNSUPPORTED                                    # K above 16384
+    assert call(opt=mnb.mnb_options(2, A4)) == mnb.MNB_ERR_UNSUPPORTED
+    assert call(K=16416, opt=mnb.mnb_options(0, A4)) == mnb.MNB_ERR_UNSUPPORTED
+    assert call(opt=mnb.mnb_options(0, 4)) == mnb.MNB_ERR_INVALID_ARG      # unknown flag
+
+
 def test_dispatcher_rule():
     # M == 1: decode GEMV with in-pass T; 2 <= M <= 8: the small-M weight-streaming GEMV
     # after the T projection; M > 8: T projection + MFMA GEMM

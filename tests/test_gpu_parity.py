@@ -357,6 +357,68 @@ def test_default_zero_point_equals_explicit():
 
 
 # ------------------------------------------------------------------------------------------
+# accuracy level 4 (int8 block-quantized activations for the base product)
+# ------------------------------------------------------------------------------------------
+
+ACC4_SHAPES = [(1, 64, 32), (1, 100, 96), (3, 130, 160), (1, 8192, 2048), (2, 200, 1024), (130, 257, 320),
+               (9, 70, 192), (1, 49152, 576), (1, 64, 16384)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_acc4_against_oracle(bits, adapter):
+    for i, (M, N, K) in enumerate(ACC4_SHAPES):
+        if bits != 8 and N == 49152:
+            continue
+        case = si.make_random(300 + i, M, N, K, bits, i % 2 == 1, adapter, bias=i % 3 == 2)
+        rows = list(range(M)) if M <= 16 else [0, 1, 63, 64, M - 1]
+        ref4 = oracle.matmul(dict(rows_case(case, rows), acc_level=4))
+        pw = dev_weight(case)
+        for path in (0, 1):
+            y = run(case, path, mnb.MNB_FLAG_ACC4, pw=pw)
+            compare(y[rows], ref4, what="acc4 path=%d M=%d N=%d K=%d" % (path, M, N, K))
+
+
+def acc4_exact_case(seed, M, N, K, bits, zp, kind):
+    """Activations that block quantization represents exactly (c * 2^-e, max |c| = 127)
+    and weights, adapters and scales that keep every sum exact: the result is unique."""
+    case = exact_case(seed, M, N, K, bits, zp, kind)
+    r = np.random.default_rng(seed + 1)
+    X = np.zeros((M, K))
+    for m in range(M):
+        for b in range(K // 32):
+            if (m + b) % 5 == 2:
+                continue
+            c = r.integers(-127, 128, size=32)
+            c[r.integers(0, 32)] = 127
+            X[m, 32 * b:32 * b + 32] = c * 2.0 ** -int(r.integers(8, 11))
+    return dict(case, X=si.to_f16_bits(X))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("kind", [None, "f16"], ids=["base", "f16"])
+@pytest.mark.parametrize("M", [1, 6])
+def test_acc4_exact_bit_exact(bits, kind, M):
+    """On exactly representable activations accuracy level 4 is lossless: GPU == oracle at
+    level 4 == oracle at level 0, bit for bit."""
+    case = acc4_exact_case(500 + 10 * bits + M, M, 192, 320, bits, bits != 8, kind)
+    want = oracle.f64_to_f16(oracle.matmul(dict(case, acc_level=4)))
+    assert same_bits(want, oracle.f64_to_f16(oracle.matmul(case)))
+    assert same_bits(run(case, 0, mnb.MNB_FLAG_ACC4), want)
+
+
+def test_acc4_differs_from_fp16_activations():
+    """On random activations the quantization is visible (and within its tolerance of the
+    FP16-activation result), so the flag really selects the int8 path."""
+    case = si.make_random(333, 1, 4096, 2048, 4, True, None)
+    pw = dev_weight(case)
+    y4 = run(case, 0, mnb.MNB_FLAG_ACC4, pw=pw)
+    y0 = run(case, 0, 0, pw=pw)
+    assert not same_bits(y4, y0)
+    compare(y4, oracle.matmul(case), max_abs=0.1, max_rel=0.02, what="acc4 vs fp16 activations")
+
+
+# ------------------------------------------------------------------------------------------
 # degenerate sizes, determinism, workspace reuse
 # ------------------------------------------------------------------------------------------
 
