@@ -178,8 +178,9 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
     snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
-    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=128x128x64 splits=%d", tp, bits, has_zp ? "x" : "def", ln,
-             cdiv(M, 128) * cdiv(N, 128) * w.splits, w.splits);
+    const int bm = gemm_bm(M, N);
+    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=%dx128x64 splits=%d", tp, bits, has_zp ? "x" : "def", ln,
+             cdiv(M, bm) * cdiv(N, 128) * w.splits, bm, w.splits);
   }
 }
 
@@ -425,7 +426,8 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   g.K = K;
   g.NG = NG;
   g.KB = KB;
-  g.MT = cdiv(M, 128);
+  g.bm = gemm_bm(M, N);
+  g.MT = cdiv(M, g.bm);
   g.NT = cdiv(N, 128);
   g.splits = w.splits;
   g.ypart = reinterpret_cast<float *>(ws + w.ypart);

@@ -164,6 +164,7 @@ struct GemmParams {
   float *ypart;           // splits > 1: FP32 partial outputs [splits, M, N]
   int M, N, K, NG, KB, MT, NT, tparts;
   int splits;             // K ranges per output tile (1: the workgroup stores Y itself)
+  int bm;                 // tile rows: 128 or 64
 };
 
 struct PackParams {
@@ -187,6 +188,7 @@ hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
 int gemm_splits(int M, int N, int K);         // K ranges per output tile of the prefill GEMM
+int gemm_bm(int M, int N);                    // tile rows of the prefill GEMM (64 or 128)
 constexpr int kMaxSplits = 16;
 hipError_t launch_pack(int bits, bool kn, const PackParams &p, hipStream_t s);  // kn: [K, N] source
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,

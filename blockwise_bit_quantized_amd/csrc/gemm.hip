@@ -41,27 +41,28 @@
 namespace mnb {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BN = 128, BK = 64;   // tile columns and K-step; the tile rows BMT are 128 or 64
 constexpr int kThreads = 256;
 constexpr int LDT = kRank + 8; // halfs per LDS row of the epilogue operands
 constexpr int kSlots = 4;      // ring depth: loads run kSlots - 1 steps ahead
 
-
-constexpr int kXBytes = BM * BK * 2;               // X tile of one step
-template <int C>
+template <int BMT, int C>
 struct Slot {
   static constexpr int kX = 0;
   static constexpr int kCodesWave = C * 1024;         // 64 rows x 16 B x C chunks
-  static constexpr int kCodes = kXBytes;
+  static constexpr int kCodes = BMT * BK * 2;         // after the X tile of one step
   static constexpr int kScale = kCodes + 4 * kCodesWave;   // per wave 256 B: 64 scales, twice
   static constexpr int kZp = kScale + 4 * 256;             // per wave 256 B: 32 or 64 B, repeated
   static constexpr int kBytes = kZp + 4 * 256;
 };
-constexpr int kLdsBytes = kSlots * Slot<2>::kBytes;  // sized for 8-bit codes
-constexpr int kRedBytes = 2 * 128 * 64 * 4;          // the kh = 1 partials
-constexpr int kEpiOff = kRedBytes;                   // epilogue operands after them
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-static_assert(kEpiOff + 2 * BM * LDT * 2 <= kSlots * Slot<1>::kBytes, "epilogue buffers fit the ring");
+template <int BMT>
+struct Lds {
+  static constexpr int kBytes = kSlots * Slot<BMT, 2>::kBytes;   // sized for 8-bit codes
+  static constexpr int kRed = 2 * BMT * 64 * 4;                  // the kh = 1 partials
+  static constexpr int kEpiOff = kRed;                           // epilogue operands after them
+  static_assert(kBytes <= (BMT == 128 ? 160 : 80) * 1024, "LDS budget (two workgroups per CU at 64 rows)");
+  static_assert(kEpiOff + (BMT + BN) * LDT * 2 <= kSlots * Slot<BMT, 1>::kBytes, "epilogue buffers fit the ring");
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 // direct-to-LDS load of 16 or 4 bytes per lane (lane i lands at dst + i * size); a plain
@@ -85,12 +86,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int BITS, bool HAS_ZP, int LORA>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
+template <int BITS, bool HAS_ZP, int LORA, int BMT>
+__global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmParams p) {
   constexpr int C = BITS == 8 ? 2 : 1;       // 16-byte code chunks per wave and step
-  using SL = Slot<C>;
+  constexpr int MB = BMT / 32;               // 32-row MFMA blocks per wave
+  constexpr int XQ = BMT / 32;               // X loads per wave and step (1 KiB each)
+  using SL = Slot<BMT, C>;
+  constexpr int kLdsBytes = Lds<BMT>::kBytes;
+  constexpr int kEpiOff = Lds<BMT>::kEpiOff;
   // direct loads per wave per step: 4 X, C codes, 1 scale, 1 zero point
-  constexpr int kLoadsPerStep = 4 + C + 1 + (HAS_ZP ? 1 : 0);
+  constexpr int kLoadsPerStep = XQ + C + 1 + (HAS_ZP ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
   const int tid = threadIdx.x;
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     mt = (x & 1) * bm + u % bm;
     nt = (x >> 1) * bn + u / bm;
   }
-  const int m0 = mt * BM, n0 = nt * BN;
+  const int m0 = mt * BMT, n0 = nt * BN;
   // K-steps [sbase, sbase + nsteps) of the (KB + 1) / 2; the host picks `splits` so that
   // every range is non-empty
   const int tsteps = (p.KB + 1) / 2;
@@ -137,11 +142,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   // wave's codes, scales and zero points ----
   // per-lane X source of each of the wave's 4 chunk loads at k = 0: row min(m0 + r, M - 1),
   // chunk c = position ^ ((r >> 1) & 7) of the swizzle; a step adds 64 k
-  const _Float16 *xsrc[4];
-  bool xhigh[4];                            // chunk in the step's second block
+  const _Float16 *xsrc[XQ];
+  bool xhigh[XQ];                           // chunk in the step's second block
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 32 * wave + 8 * q + (lane >> 3);
+  for (int q = 0; q < XQ; ++q) {
+    const int r = (BMT / 4) * wave + 8 * q + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     xsrc[q] = X + (size_t)min(m0 + r, p.M - 1) * p.K + c * 8;
     xhigh[q] = c >= 4;
@@ -153,9 +158,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     const bool ragged = 2 * sv + 1 >= p.KB;
     uint8_t *base = smem + slot * SL::kBytes;
 #pragma unroll
-    for (int q = 2 * half; q < 2 * half + 2; ++q) {
+    for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q) {
       const int k0 = sv * BK - ((ragged && xhigh[q]) ? 32 : 0);
-      dma(xsrc[q] + k0, base + SL::kX + (32 * wave + 8 * q) * 128, 16);
+      dma(xsrc[q] + k0, base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
     }
   };
   auto issue_w = [&](int step, int slot) {
@@ -265,9 +270,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     }
   };
 
-  f16x_t acc[4][2];
+  f16x_t acc[MB][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < MB; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -275,22 +280,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
 
   // ---- X operands of this wave's block of one K-step (read right after the barrier
   // that publishes the step, so their latency passes while the next step is prepared) ----
-  auto read_a = [&](int slot, h8_t (&af)[2][4]) {
+  auto read_a = [&](int slot, h8_t (&af)[2][MB]) {
     const uint8_t *xs = smem + slot * SL::kBytes + SL::kX;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = 4 * kh + 2 * hi + kk;      // 8-k chunk of the step (see the B operand)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         const int r = mb * 32 + l32;
         af[kk][mb] = *reinterpret_cast<const h8_t *>(xs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
       }
     }
   };
   // ---- a quarter of this wave's block of one K-step: k16 step kk, row blocks 2h, 2h+1 ----
-  auto mfma_q = [&](const h8_t (&af)[2][4], const u4_t (&bo)[2][2], int kk, int h) {
+  auto mfma_q = [&](const h8_t (&af)[2][MB], const u4_t (&bo)[2][2], int kk, int h) {
 #pragma unroll
-    for (int mb = 2 * h; mb < 2 * h + 2; ++mb)
+    for (int mb = h * (MB / 2); mb < (h + 1) * (MB / 2); ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, bo[nb][kk]), af[kk][mb],
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     }
   }
   u4_t bcur[2][2], bnext[2][2];
-  h8_t acur[2][4];
+  h8_t acur[2][MB];
   wait_vmcnt<2 * kLoadsPerStep>();       // own loads of step 0 have landed
   {
     Raw rw;
@@ -426,16 +431,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   float4 *red = reinterpret_cast<float4 *>(smem);
   if (kh == 1) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
-          red[((nh * 32 + (mb * 2 + nb) * 4 + v4) * 64) + lane] =
+          red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane] =
               float4{acc[mb][nb][4 * v4], acc[mb][nb][4 * v4 + 1], acc[mb][nb][4 * v4 + 2], acc[mb][nb][4 * v4 + 3]};
   }
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
-  _Float16 *sB = sT + BM * LDT;
+  _Float16 *sB = sT + BMT * LDT;
   if (lora_here) {
     // epilogue operands: T tile [128 m][32 r] (fp16, rounded once from the FP32 sum) and
     // the B tile transposed to [128 n][32 r]
@@ -447,8 +452,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         const h2_t hv = {(_Float16)tsum[8 * q + 2 * d], (_Float16)tsum[8 * q + 2 * d + 1]};
         o[q][d] = as_u32(hv);
       }
-    *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
-    *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
+    if (trow < BMT) {
+      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
+      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int n = n0 + bnc + e;
@@ -473,12 +480,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   __syncthreads();
   if (kh == 1) return;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
-        const float4 o = red[((nh * 32 + (mb * 2 + nb) * 4 + v4) * 64) + lane];
+        const float4 o = red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane];
         acc[mb][nb][4 * v4] += o.x;
         acc[mb][nb][4 * v4 + 1] += o.y;
         acc[mb][nb][4 * v4 + 2] += o.z;
@@ -489,15 +496,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     const int akof = 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < kRank / 16; ++kk) {
-      h8_t af[4], bf[2];
+      h8_t af[MB], bf[2];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const h8_t *>(&sT[(mb * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(nh * 64 + nb * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[mb], acc[mb][nb], 0, 0, 0);
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
     // this K range's FP32 partial; the reduction launch adds the ranges in order
     float *part = p.ypart + (size_t)ks * p.M * p.N;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const int m = m0 + mb * 32 + l32;
       if (m >= p.M) continue;
       float *prow = part + (size_t)m * p.N;
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
         bv[nb][j][e] = (p.bias && n < p.N) ? h2f(p.bias[n]) : 0.f;
       }
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + mb * 32 + l32;
     if (m >= p.M) continue;
     uint16_t *yrow = p.Y + (size_t)m * p.N;
@@ -615,18 +622,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, i
 template <int BITS, bool HAS_ZP>
 hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
   const dim3 grid(p.MT * p.NT * p.splits), block(kThreads);
+  if (p.bm == 64) {
+    switch (lora) {
+      case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0, 64>), grid, block, 0, s, p); break;
+      case 1: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 1, 64>), grid, block, 0, s, p); break;
+      default: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 2, 64>), grid, block, 0, s, p); break;
+    }
+    return hipGetLastError();
+  }
   switch (lora) {
-    case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0>), grid, block, 0, s, p); break;
-    case 1: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 1>), grid, block, 0, s, p); break;
-    default: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 2>), grid, block, 0, s, p); break;
+    case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0, 128>), grid, block, 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 1, 128>), grid, block, 0, s, p); break;
+    default: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 2, 128>), grid, block, 0, s, p); break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Tile rows.  128-row tiles (one workgroup per CU) dequantize each weight once per 128
+// rows; 64-row tiles dequantize it twice as often but run two workgroups per CU, whose
+// loads, waits and matrix work interleave.  Measured: 128 wins when the tiles fill whole
+// rounds of the 256 CUs (1024 x 4096: 56 against 60 us); 64 wins when the last round of
+// 128-row tiles would be at most half full (1024 x 9728 at M = 512: 59 against 74 us; small
+// M by 10-20%).
+int gemm_bm(int M, int N) {
+  const long t128 = (long)((M + 127) / 128) * ((N + BN - 1) / BN);
+  const long rem = t128 % kCUs;
+  return (rem == 0 || rem > kCUs / 2) ? 128 : 64;
+}
+
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s) {
-  if (p.splits < 1 || p.splits > kMaxSplits) return hipErrorInvalidValue;
+  if (p.splits < 1 || p.splits > kMaxSplits || (p.bm != 64 && p.bm != 128)) return hipErrorInvalidValue;
   const hipError_t e = bits == 2   ? (has_zp ? launch2<2, true>(lora, p, s) : launch2<2, false>(lora, p, s))
                        : bits == 4 ? (has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s))
                                    : (has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s));
@@ -647,7 +674,8 @@ hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hip
 // with t_step ~0.8 us per 64-k step of a tile, t_launch ~2 us and ~6 TB/s for the
 // partials (they stay in the Infinity Cache at these sizes); at least 2 K-steps per range.
 int gemm_splits(int M, int N, int K) {
-  const long tiles = (long)((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int bm = gemm_bm(M, N);
+  const long tiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
   const int tsteps = (K / kBlock + 1) / 2;
   if (tiles <= 0 || tsteps <= 0) return 1;
   int best = 1;
@@ -656,7 +684,8 @@ int gemm_splits(int M, int N, int K) {
     const int sps = (tsteps + S - 1) / S;
     if (S > 1 && sps < 2) break;
     if ((tsteps + sps - 1) / sps != S) continue;     // some range would be empty
-    const double rounds = (double)((tiles * S + kCUs - 1) / kCUs);
+    const long slots = bm == 64 ? 2 * kCUs : kCUs;     // workgroups resident at once
+    const double rounds = (double)((tiles * S + slots - 1) / slots);
     double us = rounds * sps * 0.8;
     if (S > 1) us += 2.0 + (2.0 * S + 0.5) * 4.0 * (double)M * N / 6e6;
     if (us < best_us * 0.97) {

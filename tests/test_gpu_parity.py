@@ -200,6 +200,18 @@ def test_small_shapes_all_paths(bits, zp, adapter):
 SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
 
 
+@pytest.mark.parametrize("adapter", [None, "f16"], ids=["base", "f16"])
+def test_gemm_tile_rows_both(adapter):
+    """Both tile heights: 128-row tiles when they fill the CUs' rounds (and most of a
+    last one), 64-row tiles otherwise."""
+    for i, (M, N, K, bm) in enumerate([(256, 12800, 512, 128), (260, 200, 320, 64), (1024, 4096, 256, 128)]):
+        _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, 1 if adapter else 0)
+        assert "tile=%dx128x64" % bm in desc, desc
+        case = si.make_random(210 + i, M, N, K, 4, True, adapter, bias=i == 1)
+        rows = [0, 1, 63, 64, 127, 128, M - 1]
+        compare(run(case)[rows], oracle.matmul(rows_case(case, rows)), what="tiles M=%d N=%d K=%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
 def test_gemm_split_k_ranges(bits, adapter):
