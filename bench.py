@@ -246,6 +246,30 @@ def main():
         context["decode_2bit_us"] = round(two_s * 1e6, 3)
         context["decode_2bit_GBps"] = round(dbytes2 / two_s / 1e9, 1)
         del w2
+    # context: the other prefill workloads (warm weights), each a replayed graph of calls
+    pre_context = None
+    if not args.no_context:
+        pre_context = {}
+        c256 = si.make_config(3, M=256)
+        X256, Y256 = t16(c256["X"]), torch.empty((256, pN), dtype=torch.float16, device=dev)
+        ws256 = torch.zeros(mnb.mnb_workspace_bytes(256, pN, pK, 4, 32), dtype=torch.uint8, device=dev)
+        s256 = graph_time(lambda j: mnb.matmul(X256, ppw, pad, out=Y256, ws=ws256), 20)
+        f256 = algorithmic_flops(256, pN, pK, 32)
+        pre_context["m256_us"] = round(s256 * 1e6, 3)
+        pre_context["m256_TFLOPs"] = round(f256 / s256 / 1e12, 2)
+        pre_context["m256_route"] = mnb.mnb_describe_route(256, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
+        c5 = si.make_config(5)
+        M5, N5, K5 = c5["M"], c5["N"], c5["K"]
+        pw5 = weight(c5)
+        a5 = c5["adapter"]
+        ad5 = mnb.Adapter(mnb.MNB_ADAPTER_Q8, torch.from_numpy(a5["A"]).to(dev), torch.from_numpy(a5["B"]).to(dev),
+                          t16(a5["A_scales"]), t16(a5["B_scales"]))
+        X5, Y5 = t16(c5["X"]), torch.empty((M5, N5), dtype=torch.float16, device=dev)
+        ws5 = torch.zeros(mnb.mnb_workspace_bytes(M5, N5, K5, 4, 32), dtype=torch.uint8, device=dev)
+        s5 = graph_time(lambda j: mnb.matmul(X5, pw5, ad5, out=Y5, ws=ws5), 20)
+        pre_context["batched_q8_us"] = round(s5 * 1e6, 3)
+        pre_context["batched_q8_TFLOPs"] = round(algorithmic_flops(M5, N5, K5, 32) / s5 / 1e12, 2)
+        pre_context["batched_q8_route"] = mnb.mnb_describe_route(M5, N5, K5, 4, False, mnb.MNB_ADAPTER_Q8)[1]
     dec_route = mnb.mnb_describe_route(dM, dN, dK, 4, False, mnb.MNB_ADAPTER_F16)[1]
     pre_route = mnb.mnb_describe_route(pM, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
     traffic = recorded_traffic("gemv")
@@ -279,6 +303,7 @@ def main():
                                  "traffic": recorded_traffic("gemm")},
                     "bytes": pbytes},
         "decode_context": context,
+        "prefill_context": pre_context,
         "wall_s": round(wall, 3),
     }
 
