@@ -327,7 +327,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   // 2 <= M <= 16, whose consumers would add the parts row by row, the projection reduces
   // them itself (per-tile arrival counter, agent-scope fences).  Above that the fences
   // cost more than they save (each writes back and invalidates an L2), so the projection
-  // uses 1024-k parts and the GEMM adds them (four loads in flight, then one at a time);
+  // uses 512-k parts and the GEMM adds them (eight loads in flight, then one at a time);
   // the M == 1 GEMV adds up to 8 with its loads in flight together.
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   int tparts = w.tparts;

@@ -310,11 +310,12 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   bool bvec = false;
   const int trow = tid >> 1, thh = (tid & 1) * 16;
   const int br = tid >> 3, bnc = (tid & 7) * 16;
-  float4 tv[4][4];
+  constexpr int kTPartsAhead = 8;            // T parts loaded before the ring starts
+  float4 tv[kTPartsAhead][4];
   if (lora_here) {
     const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+    for (int pp = 0; pp < kTPartsAhead; ++pp) {
       const int pc = pp < p.tparts ? pp : 0;
       const float *src = p.tpart + ((size_t)pc * p.M + mrow) * kRank + thh;
 #pragma unroll
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
 #pragma unroll
     for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+    for (int pp = 0; pp < kTPartsAhead; ++pp) {
       if (pp < p.tparts) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -361,7 +362,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
         }
       }
     }
-    for (int pp = 4; pp < p.tparts; ++pp) {
+    for (int pp = kTPartsAhead; pp < p.tparts; ++pp) {
       const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

@@ -173,10 +173,12 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
 
 }  // namespace
 
-// K per part: 1024; for M <= 16 (whose parts the projection adds itself) 256 when 1024-k
-// parts would give fewer than 128 workgroups
+// K per part: above M = 16 512 (the GEMM adds up to 8 parts with their loads issued before
+// its ring starts; measured 1-2 us faster per prefill call than 1024, 256 slower); for
+// M <= 16 (whose parts the projection adds itself) 1024, or 256 when that would give fewer
+// than 128 workgroups
 int tproj_kp(int M, int K) {
-  if (M > kRowsMaxM) return 1024;
+  if (M > kRowsMaxM) return 512;
   return ((M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024;
 }
 int tproj_parts(int M, int K) {
@@ -186,12 +188,14 @@ int tproj_parts(int M, int K) {
 
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s) {
   const int grid = p.MT * p.parts;
-  const bool small = tproj_kp(p.M, p.K) == 256;
+  const int kp = tproj_kp(p.M, p.K);
   if (lora == 1) {
-    if (small) hipLaunchKernelGGL((tproj_kernel<1, 256>), dim3(grid), dim3(256), 0, s, p);
+    if (kp == 256) hipLaunchKernelGGL((tproj_kernel<1, 256>), dim3(grid), dim3(256), 0, s, p);
+    else if (kp == 512) hipLaunchKernelGGL((tproj_kernel<1, 512>), dim3(grid), dim3(256), 0, s, p);
     else hipLaunchKernelGGL((tproj_kernel<1, 1024>), dim3(grid), dim3(256), 0, s, p);
   } else {
-    if (small) hipLaunchKernelGGL((tproj_kernel<2, 256>), dim3(grid), dim3(256), 0, s, p);
+    if (kp == 256) hipLaunchKernelGGL((tproj_kernel<2, 256>), dim3(grid), dim3(256), 0, s, p);
+    else if (kp == 512) hipLaunchKernelGGL((tproj_kernel<2, 512>), dim3(grid), dim3(256), 0, s, p);
     else hipLaunchKernelGGL((tproj_kernel<2, 1024>), dim3(grid), dim3(256), 0, s, p);
   }
   return hipGetLastError();
