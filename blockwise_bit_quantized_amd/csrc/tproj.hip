@@ -18,8 +18,8 @@
 namespace mnb {
 namespace {
 
-// KIND 1: F16 A, 2: INT8 A with block-32 fp16 scales; KP: K per part (1024, or 256 when
-// the M tiles alone would leave most CUs idle)
+// KIND 1: F16 A, 2: INT8 A with block-32 fp16 scales; KP: K per part (256, 512 or 1024,
+// see tproj_kp)
 template <int KIND, int KP>
 __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
   constexpr int kKP = KP;
