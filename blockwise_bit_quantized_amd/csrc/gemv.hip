@@ -34,16 +34,12 @@
 
 #include "common.h"
 
-#ifndef MNB_GEMV_WAVES
-#define MNB_GEMV_WAVES 8
-#endif
-
 namespace mnb {
 namespace {
 
 enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
 enum { T_INPASS = 0, T_PRECOMP = 1 };
-constexpr int kWaves = MNB_GEMV_WAVES;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kMaxSlicesUnrolled = 16;
 constexpr int kTSliceMax = 256;     // k rows per in-pass T slice (the host passes kt <= this)
