@@ -182,7 +182,8 @@ def test_cfg5_batched_prefill_q8():
 # ------------------------------------------------------------------------------------------
 
 SHAPES = [(1, 64, 32), (1, 100, 96), (1, 1, 32), (3, 130, 160), (7, 32, 64), (2, 200, 1024), (129, 257, 320),
-          (256, 384, 512), (1, 4096, 4096), (16, 96, 256), (9, 70, 192), (5, 513, 128), (17, 64, 96)]
+          (256, 384, 512), (1, 4096, 4096), (16, 96, 256), (9, 70, 192), (5, 513, 128), (17, 64, 96),
+          (1, 64, 16384), (3, 100, 8192)]   # long K: several load rounds, 64 T slices or parts
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
