@@ -199,9 +199,10 @@ hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStrea
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
 int tproj_parts(int M, int K);                 // K parts of the T projection
 int gemv_rows_mr(int M, int bits);                       // rows per workgroup of the small-M path
-// largest M of the small-M path: measured crossover against the MFMA GEMM on the workload
-// weights (the small-M path wins up to M = 8 on all of them, the GEMM from M = 12)
-constexpr int kSmallM = 8;
+// largest M of the small-M path: measured crossover against the MFMA GEMM (K split over
+// workgroups, 64-row tiles) on the four workload weight sets: the small-M path wins at
+// M <= 4 (by 10-20%, equal on the batched-prefill weights), the GEMM from M = 5
+constexpr int kSmallM = 4;
 constexpr int kRowsMaxM = 16;                  // largest M the multi-row GEMV takes (forced path)
 
 }  // namespace mnb

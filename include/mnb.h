@@ -174,8 +174,8 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank);
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
  * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV
- * with T computed in the same launch; 2 <= M <= 8 the T projection, then a GEMV that
- * streams the weights once for all rows; M > 8 the T projection, then the MFMA GEMM with
+ * with T computed in the same launch; 2 <= M <= 4 the T projection, then a GEMV that
+ * streams the weights once for all rows; M > 4 the T projection, then the MFMA GEMM with
  * the LoRA term in its epilogue.
  */
 int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp,

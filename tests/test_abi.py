@@ -184,16 +184,18 @@ def test_accuracy_level4_route_and_validation():
 
 
 def test_dispatcher_rule():
-    # M == 1: decode GEMV with in-pass T; 2 <= M <= 8: the small-M weight-streaming GEMV
-    # after the T projection; M > 8: T projection + MFMA GEMM
+    # M == 1: decode GEMV with in-pass T; 2 <= M <= 4: the small-M weight-streaming GEMV
+    # after the T projection; M > 4: T projection + MFMA GEMM
     assert route(1).startswith("gemv_b4_zpx_f16_inpass")
     assert route(1, kind=0).startswith("gemv_b4_zpx_none_base")
     assert route(2).startswith("tproj_f16") and "gemv_rows_b4_zpx_f16" in route(2) and "mr=4" in route(2)
-    assert "gemv_rows" in route(8) and "mr=8" in route(8)
-    assert route(9).startswith("tproj_f16") and "gemm_b4_zpx_f16" in route(9)
+    assert "gemv_rows" in route(4) and "mr=4" in route(4)
+    assert route(5).startswith("tproj_f16") and "gemm_b4_zpx_f16" in route(5)
+    assert "gemv_rows" in route(8, path=1) and "mr=8" in route(8, path=1)
     assert "gemv_rows" in route(16, path=1) and "mr=16" in route(16, path=1)
     assert route(1024, kind=2).startswith("tproj_q8") and "gemm_b4_zpx_q8" in route(1024, kind=2)
-    assert route(8, N=49152, K=576, bits=8, kind=0).startswith("gemv_rows_b8_zpx_none")
+    assert route(4, N=49152, K=576, bits=8, kind=0).startswith("gemv_rows_b8_zpx_none")
+    assert route(8, N=49152, K=576, bits=8, kind=0).startswith("gemm_b8_zpx_none")
     # overrides, as the pages keep explicit path overrides for comparisons
     assert route(1, path=2).startswith("tproj_f16") and "gemm" in route(1, path=2)
     assert route(7, path=2).startswith("tproj_f16") and "gemm" in route(7, path=2)
