@@ -466,6 +466,44 @@ def test_determinism_and_workspace_reuse():
         compare(y0[rows], oracle.matmul(rows_case(c, rows)), what="reuse %s" % (c["M"],))
 
 
+def test_graph_replay_matches_eager():
+    """Calls captured in a HIP graph (decode with the in-pass T handoff, small M, split-K
+    prefill, accuracy level 4) give, on every replay, exactly the eager results, with eager
+    calls on the same workspace between the replays: the library enqueues no memset and
+    keeps its per-call state (the T epoch, the counters) in the workspace."""
+    ws = torch.zeros(1 << 24, dtype=torch.uint8, device=DEV)
+    specs = [(1, 4096, 2048, 4, False, "f16", 0), (3, 1000, 1024, 4, True, "q8", 0),
+             (200, 512, 1024, 8, True, "f16", 0), (1, 896, 896, 4, True, None, mnb.MNB_FLAG_ACC4)]
+    calls = []
+    for i, (M, N, K, bits, zp, ad, fl) in enumerate(specs):
+        c = si.make_random(600 + i, M, N, K, bits, zp, ad, bias=i == 2)
+        pw = dev_weight(c)
+        a = dev_adapter(c["adapter"])
+        X = t16(c["X"])
+        b = t16(c["bias"]) if c.get("bias") is not None else None
+        Y = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        calls.append((X, pw, a, fl, b, Y))
+    def run_all():
+        for X, pw, a, fl, b, Y in calls:
+            mnb.matmul(X, pw, a, flags=fl, out=Y, ws=ws, bias=b)
+    run_all()
+    torch.cuda.synchronize()
+    eager = [Y.clone() for *_, Y in calls]
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        run_all()
+    for rep in range(4):
+        for *_, Y in calls:
+            Y.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        for (*_, Y), y0 in zip(calls, eager):
+            assert torch.equal(Y.view(torch.int16), y0.view(torch.int16)), rep
+        run_all()                                  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+
+
 def test_workspace_counters_return_to_zero():
     """The in-pass T handoff and the T projection's part reduction leave every counter of
     the workspace's control area at zero, never set the error word, and advance the epoch
