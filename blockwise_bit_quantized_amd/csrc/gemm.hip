@@ -36,6 +36,9 @@
 // clamped addresses into free slots, so every step has the same loads in flight.
 // Without an adapter the two epilogue k-steps are skipped, so the base accumulation order
 // is the same in every variant and a zero adapter reproduces the base output bitwise.
+// The finished tile is staged in LDS and stored by all four waves as whole row pieces
+// (16 bytes per lane, 256 contiguous bytes per row), not as the accumulator layout's
+// 16 bytes in each of 32 rows.
 #include "common.h"
 
 namespace mnb {
@@ -44,7 +47,9 @@ namespace {
 constexpr int BN = 128, BK = 64;   // tile columns and K-step; the tile rows BMT are 128 or 64
 constexpr int kThreads = 256;
 constexpr int LDT = kRank + 8; // halfs per LDS row of the epilogue operands
-constexpr int kSlots = 4;      // ring depth: loads run kSlots - 1 steps ahead
+// ring depth: loads run kSlots - 1 steps ahead (measured: 6 slots at 128 rows, 5 steps
+// ahead, gave the same times)
+constexpr int kSlots = 4;
 
 template <int BMT, int C>
 struct Slot {
@@ -55,13 +60,14 @@ struct Slot {
   static constexpr int kZp = kScale + 4 * 256;             // per wave 256 B: 32 or 64 B, repeated
   static constexpr int kBytes = kZp + 4 * 256;
 };
-template <int BMT>
+template <int BMT, int C>
 struct Lds {
-  static constexpr int kBytes = kSlots * Slot<BMT, 2>::kBytes;   // sized for 8-bit codes
+  static constexpr int kBytes = kSlots * Slot<BMT, C>::kBytes;
   static constexpr int kRed = 2 * BMT * 64 * 4;                  // the kh = 1 partials
   static constexpr int kEpiOff = kRed;                           // epilogue operands after them
+  static_assert(kSlots % 2 == 0, "the main loop alternates two B operand sets");
   static_assert(kBytes <= (BMT == 128 ? 160 : 80) * 1024, "LDS budget (two workgroups per CU at 64 rows)");
-  static_assert(kEpiOff + (BMT + BN) * LDT * 2 <= kSlots * Slot<BMT, 1>::kBytes, "epilogue buffers fit the ring");
+  static_assert(kEpiOff + (BMT + BN) * LDT * 2 <= kBytes, "epilogue buffers fit the ring");
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -92,8 +98,8 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   constexpr int MB = BMT / 32;               // 32-row MFMA blocks per wave
   constexpr int XQ = BMT / 32;               // X loads per wave and step (1 KiB each)
   using SL = Slot<BMT, C>;
-  constexpr int kLdsBytes = Lds<BMT>::kBytes;
-  constexpr int kEpiOff = Lds<BMT>::kEpiOff;
+  constexpr int kLdsBytes = Lds<BMT, C>::kBytes;
+  constexpr int kEpiOff = Lds<BMT, C>::kEpiOff;
   // direct loads per wave per step: 4 X, C codes, 1 scale, 1 zero point
   constexpr int kLoadsPerStep = XQ + C + 1 + (HAS_ZP ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
@@ -280,17 +286,18 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
 
   // ---- X operands of this wave's block of one K-step (read right after the barrier
   // that publishes the step, so their latency passes while the next step is prepared) ----
-  auto read_a = [&](int slot, h8_t (&af)[2][MB]) {
+  auto read_a_kk = [&](int slot, h8_t (&af)[2][MB], int kk) {
     const uint8_t *xs = smem + slot * SL::kBytes + SL::kX;
+    const int c = 4 * kh + 2 * hi + kk;        // 8-k chunk of the step (see the B operand)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int c = 4 * kh + 2 * hi + kk;      // 8-k chunk of the step (see the B operand)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = mb * 32 + l32;
-        af[kk][mb] = *reinterpret_cast<const h8_t *>(xs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-      }
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = mb * 32 + l32;
+      af[kk][mb] = *reinterpret_cast<const h8_t *>(xs + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
     }
+  };
+  auto read_a = [&](int slot, h8_t (&af)[2][MB]) {
+    read_a_kk(slot, af, 0);
+    read_a_kk(slot, af, 1);
   };
   // ---- a quarter of this wave's block of one K-step: k16 step kk, row blocks 2h, 2h+1 ----
   auto mfma_q = [&](const h8_t (&af)[2][MB], const u4_t (&bo)[2][2], int kk, int h) {
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     }
   }
 
-  // ---- prologue: steps 0..2 in flight, step 0 dequantized ----
+  // ---- prologue: steps 0 .. kSlots - 2 in flight, step 0 dequantized ----
 #pragma unroll
   for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
   if (lora_here) {
@@ -376,7 +383,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   }
   u4_t bcur[2][2], bnext[2][2];
   h8_t acur[2][MB];
-  wait_vmcnt<2 * kLoadsPerStep>();       // own loads of step 0 have landed
+  wait_vmcnt<(kSlots - 2) * kLoadsPerStep>();   // own loads of step 0 have landed
   {
     Raw rw;
     dq_read(0, rw);
@@ -392,9 +399,9 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   // between them, so the VALU work runs while the matrix core is busy.
   // slot: s mod kSlots, a compile-time constant at every call
   auto body = [&](int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2], const int slot) {
-    const int ls = (slot + kSlots - 1) & (kSlots - 1);
-    const int ns = (slot + 1) & (kSlots - 1);
-    wait_vmcnt<kLoadsPerStep>();         // own loads of step s+1 have landed (s+2's may not)
+    const int ls = (slot + kSlots - 1) % kSlots;
+    const int ns = (slot + 1) % kSlots;
+    wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();   // own loads of step s+1 have landed (later ones may not)
     Raw rw;
     dq_read(ns, rw);                      // past the end: unused, from a loaded slot
     __builtin_amdgcn_sched_barrier(0);
@@ -416,15 +423,18 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   };
   // unrolled by the ring depth, so ring slots are compile-time constants
   int s = 0;
-  for (; s + 3 < nsteps; s += 4) {
-    body(s, bcur, bnext, 0);
-    body(s + 1, bnext, bcur, 1);
-    body(s + 2, bcur, bnext, 2);
-    body(s + 3, bnext, bcur, 3);
+  for (; s + kSlots - 1 < nsteps; s += kSlots) {
+#pragma unroll
+    for (int i = 0; i < kSlots; i += 2) {
+      body(s + i, bcur, bnext, i);
+      body(s + i + 1, bnext, bcur, i + 1);
+    }
   }
-  if (s < nsteps) body(s, bcur, bnext, 0);
-  if (s + 1 < nsteps) body(s + 1, bnext, bcur, 1);
-  if (s + 2 < nsteps) body(s + 2, bcur, bnext, 2);
+#pragma unroll
+  for (int i = 0; i < kSlots - 1; i += 2) {   // at most kSlots - 1 steps remain
+    if (s + i < nsteps) body(s + i, bcur, bnext, i);
+    if (i + 1 < kSlots - 1 && s + i + 1 < nsteps) body(s + i + 1, bnext, bcur, i + 1);
+  }
   wait_vmcnt<0>();                        // the trailing loads into free slots are done
   lds_barrier();
 
@@ -479,103 +489,133 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     }
   }
   __syncthreads();
-  if (kh == 1) return;
+  if (kh == 0) {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const float4 o = red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane];
-        acc[mb][nb][4 * v4] += o.x;
-        acc[mb][nb][4 * v4 + 1] += o.y;
-        acc[mb][nb][4 * v4 + 2] += o.z;
-        acc[mb][nb][4 * v4 + 3] += o.w;
-      }
-
-  if (lora_here) {
-    const int akof = 8 * hi;
-#pragma unroll
-    for (int kk = 0; kk < kRank / 16; ++kk) {
-      h8_t af[MB], bf[2];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        af[mb] = *reinterpret_cast<const h8_t *>(&sT[(mb * 32 + l32) * LDT + kk * 16 + akof]);
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(nh * 64 + nb * 32 + l32) * LDT + kk * 16 + akof]);
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 o = red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane];
+          acc[mb][nb][4 * v4] += o.x;
+          acc[mb][nb][4 * v4 + 1] += o.y;
+          acc[mb][nb][4 * v4 + 2] += o.z;
+          acc[mb][nb][4 * v4 + 3] += o.w;
+        }
+
+    if (lora_here) {
+      const int akof = 8 * hi;
+#pragma unroll
+      for (int kk = 0; kk < kRank / 16; ++kk) {
+        h8_t af[MB], bf[2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          af[mb] = *reinterpret_cast<const h8_t *>(&sT[(mb * 32 + l32) * LDT + kk * 16 + akof]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(nh * 64 + nb * 32 + l32) * LDT + kk * 16 + akof]);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[mb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();   // the partials and the epilogue operands are consumed
+
+  // ---- the finished tile goes through LDS so that all four waves store whole rows ----
+  // The MFMAs computed Y^T blocks (weights as the row operand), so accumulator register v
+  // of block [mb][nb] holds tile row 32 mb + lane % 32 and tile column
+  // 64 nh + 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per
+  // register quad.  The kh = 0 waves write the tile to LDS (padded rows), then every thread
+  // copies 16 contiguous bytes of a row, so a store instruction covers whole 256-byte (fp16)
+  // or 512-byte (FP32) row pieces instead of 16 bytes in each of 32 rows.
+  constexpr int kPitchH = BN + 8;    // halfs per LDS row of the fp16 tile (rows stay 16-byte aligned)
+  constexpr int kPitchF = BN + 4;    // floats per LDS row of the FP32 partial tile
+  static_assert(BMT * kPitchF * 4 <= kLdsBytes, "the staged output tile fits the ring");
+  if (p.splits > 1) {
+    // this K range's FP32 partial; the reduction launch adds the ranges in order
+    float *tileF = reinterpret_cast<float *>(smem);
+    if (kh == 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[mb], acc[mb][nb], 0, 0, 0);
-    }
-  }
-
-  // store: the MFMAs computed Y^T blocks (weights as the row operand), so accumulator
-  // register v of block [mb][nb] holds output row m = 32 mb + lane % 32 and column
-  // n = 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per register
-  // quad, stored as one 8-byte vector (16 bytes for an FP32 partial)
-  const bool vec = (p.N & 3) == 0;
-  if (p.splits > 1) {
-    // this K range's FP32 partial; the reduction launch adds the ranges in order
-    float *part = p.ypart + (size_t)ks * p.M * p.N;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int m = m0 + mb * 32 + l32;
-      if (m >= p.M) continue;
-      float *prow = part + (size_t)m * p.N;
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4 *>(&tileF[(mb * 32 + l32) * kPitchF + nh * 64 + nb * 32 + 8 * j + 4 * hi]) =
+                float4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
+    }
+    __syncthreads();
+    float *part = p.ypart + (size_t)ks * p.M * p.N;
+    const bool vec = (p.N & 3) == 0;
+    const int c4 = tid & 31;                 // 16-byte chunk of a 512-byte row
+#pragma unroll
+    for (int pass = 0; pass < BMT / 8; ++pass) {
+      const int row = pass * 8 + (tid >> 5);
+      const int m = m0 + row;
+      const int n = n0 + 4 * c4;
+      if (m >= p.M || n >= p.N) continue;
+      const float4 v = *reinterpret_cast<const float4 *>(&tileF[row * kPitchF + 4 * c4]);
+      float *dst = part + (size_t)m * p.N + n;
+      if (vec && n + 4 <= p.N) {
+        *reinterpret_cast<float4 *>(dst) = v;
+      } else {
+        const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) dst[e] = e4[e];
+      }
+    }
+    return;
+  }
+  uint16_t *tileH = reinterpret_cast<uint16_t *>(smem);
+  if (kh == 0) {
+    // broadcast bias of this lane's columns, added in FP32 before the rounding
+    float bv[2][4][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi + e;
+          bv[nb][j][e] = (p.bias && n < p.N) ? h2f(p.bias[n]) : 0.f;
+        }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi;
-          if (vec && n + 4 <= p.N) {
-            *reinterpret_cast<float4 *>(prow + n) =
-                float4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
-          } else {
+          float y[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < p.N) prow[n + e] = acc[mb][nb][4 * j + e];
-          }
+          for (int e = 0; e < 4; ++e) y[e] = p.bias ? acc[mb][nb][4 * j + e] + bv[nb][j][e] : acc[mb][nb][4 * j + e];
+          const h2_t lo = {(_Float16)y[0], (_Float16)y[1]};
+          const h2_t hi2 = {(_Float16)y[2], (_Float16)y[3]};
+          *reinterpret_cast<u2_t *>(&tileH[(mb * 32 + l32) * kPitchH + nh * 64 + nb * 32 + 8 * j + 4 * hi]) =
+              u2_t{as_u32(lo), as_u32(hi2)};
         }
-    }
-    return;
   }
-  // broadcast bias of this lane's columns, added in FP32 before the rounding
-  float bv[2][4][4];
+  __syncthreads();
+  const bool vec = (p.N & 7) == 0;
+  const int c8 = tid & 15;                   // 16-byte chunk of a 256-byte row
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int pass = 0; pass < BMT / 16; ++pass) {
+    const int row = pass * 16 + (tid >> 4);
+    const int m = m0 + row;
+    const int n = n0 + 8 * c8;
+    if (m >= p.M || n >= p.N) continue;
+    const u4_t v = *reinterpret_cast<const u4_t *>(&tileH[row * kPitchH + 8 * c8]);
+    uint16_t *dst = p.Y + (size_t)m * p.N + n;
+    if (vec && n + 8 <= p.N) {
+      *reinterpret_cast<u4_t *>(dst) = v;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi + e;
-        bv[nb][j][e] = (p.bias && n < p.N) ? h2f(p.bias[n]) : 0.f;
-      }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + mb * 32 + l32;
-    if (m >= p.M) continue;
-    uint16_t *yrow = p.Y + (size_t)m * p.N;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = p.bias ? acc[mb][nb][4 * j + e] + bv[nb][j][e] : acc[mb][nb][4 * j + e];
-        const h2_t lo = {(_Float16)y[0], (_Float16)y[1]};
-        const h2_t hi2 = {(_Float16)y[2], (_Float16)y[3]};
-        if (vec && n + 4 <= p.N) {
-          *reinterpret_cast<u2_t *>(yrow + n) = u2_t{as_u32(lo), as_u32(hi2)};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) yrow[n + e] = __builtin_bit_cast(uint16_t, e < 2 ? lo[e] : hi2[e - 2]);
-        }
-      }
+      for (int e = 0; e < 8; ++e)
+        if (n + e < p.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+    }
   }
 }
 
