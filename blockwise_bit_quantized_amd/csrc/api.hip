@@ -110,6 +110,7 @@ int check_common(int M, int N, int K, int bits, int block) {
   if (M < 0 || N < 0 || K < 0) return MNB_ERR_INVALID_ARG;
   if (bits != 2 && bits != 4 && bits != 8) return MNB_ERR_UNSUPPORTED;
   if (block != kBlock || K % kBlock) return MNB_ERR_UNSUPPORTED;
+  if (K >= kMaxK) return MNB_ERR_UNSUPPORTED;
   return MNB_OK;
 }
 

@@ -140,35 +140,49 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   // the LoRA term is added once, by the first K range
   const bool lora_here = LORA != 0 && ks == 0;
 
-  const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
   const int wg = (n0 >> 6) + nh;             // packed row group of this wave
   const bool wrow_ok = wg < p.NG;
 
   // ---- direct-to-LDS loads of one step into one ring slot: X rows (two halves), then the
   // wave's codes, scales and zero points ----
-  // per-lane X source of each of the wave's 4 chunk loads at k = 0: row min(m0 + r, M - 1),
-  // chunk c = position ^ ((r >> 1) & 7) of the swizzle; a step adds 64 k
-  const _Float16 *xsrc[XQ];
-  bool xhigh[XQ];                           // chunk in the step's second block
+  // Addresses are a wave-uniform base plus a loop-invariant 32-bit lane offset, so the
+  // direct loads use the scalar-base form and a step costs no vector address arithmetic.
+  // X chunk load q of this wave covers tile rows r0 = (BMT/4) wave + 8 q .. r0 + 7 (8 lanes
+  // per row): uniform base row min(m0 + r0, M - 1); lane offset = (its row, clamped to
+  // M - 1, minus the base row) * 2K bytes + 16 c, with chunk c = position ^ ((r >> 1) & 7)
+  // of the swizzle (at most 7 * 2K + 112 bytes: K < 2^28 is checked by the host)
+  const uint8_t *X = reinterpret_cast<const uint8_t *>(p.X);
+  const uint8_t *xrow[XQ];
+  uint32_t xoff[XQ], xoffr[XQ];
 #pragma unroll
   for (int q = 0; q < XQ; ++q) {
-    const int r = (BMT / 4) * wave + 8 * q + (lane >> 3);
+    const int r0 = (BMT / 4) * wave + 8 * q;
+    const int rb = min(m0 + r0, p.M - 1);
+    const int r = r0 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    xsrc[q] = X + (size_t)min(m0 + r, p.M - 1) * p.K + c * 8;
-    xhigh[q] = c >= 4;
+    xrow[q] = X + (size_t)rb * p.K * 2;
+    xoff[q] = (uint32_t)(min(m0 + r, p.M - 1) - rb) * (uint32_t)p.K * 2u + (uint32_t)c * 16u;
+    // with an odd block count the last step's second block lies past K: its chunks
+    // (c >= 4) re-read the first block (any valid address; the block's scales are 0)
+    xoffr[q] = xoff[q] - (c >= 4 ? 64u : 0u);
   }
   auto issue_x = [&](int step, int slot, int half) {
     const int sv = sbase + (step < nsteps ? step : nsteps - 1);   // past the end: a valid address
-    // with an odd block count the last step's second block lies past K: those chunks
-    // re-read the first block (any valid address; the block's scales are masked to 0)
     const bool ragged = 2 * sv + 1 >= p.KB;
     uint8_t *base = smem + slot * SL::kBytes;
+    if (ragged) {
 #pragma unroll
-    for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q) {
-      const int k0 = sv * BK - ((ragged && xhigh[q]) ? 32 : 0);
-      dma(xsrc[q] + k0, base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
+      for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q)
+        dma(xrow[q] + (size_t)sv * BK * 2 + xoffr[q], base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
+    } else {
+#pragma unroll
+      for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q)
+        dma(xrow[q] + (size_t)sv * BK * 2 + xoff[q], base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
     }
   };
+  // per-lane byte offsets of the weight loads (uniform bases are per step)
+  const uint32_t lo16 = (uint32_t)lane * 16u, lo_sc = (uint32_t)l32 * 4u;
+  const uint32_t lo_zp = 4u * (uint32_t)(BITS == 2 ? (lane & 3) : BITS == 4 ? (lane & 7) : (lane & 15));
   auto issue_w = [&](int step, int slot) {
     const int sv = sbase + (step < nsteps ? step : nsteps - 1);
     uint8_t *base = smem + slot * SL::kBytes;
@@ -178,18 +192,16 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     if constexpr (BITS == 2) {
       // one chunk holds both blocks of the step (each wave uses its half)
       const size_t ch = wrow_ok ? (size_t)wg * tsteps + sv : 0;
-      dma(p.wq + (ch * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave, 16);
+      dma(p.wq + ch * kGroup * 16 + lo16, base + SL::kCodes + wave * SL::kCodesWave, 16);
     } else {
 #pragma unroll
       for (int c = 0; c < C; ++c)
-        dma(p.wq + ((t * C + c) * kGroup + lane) * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+        dma(p.wq + (t * C + c) * kGroup * 16 + lo16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
     }
-    dma(p.sc + t * kGroup + 2 * l32, base + SL::kScale + wave * 256, 4);
+    dma(reinterpret_cast<const uint8_t *>(p.sc + t * kGroup) + lo_sc, base + SL::kScale + wave * 256, 4);
     if constexpr (HAS_ZP) {
-      const uint8_t *zsrc = BITS == 2   ? p.zp + t * 16 + 4 * (lane & 3)
-                            : BITS == 4 ? p.zp + t * 32 + 4 * (lane & 7)
-                                        : p.zp + t * kGroup + 4 * (lane & 15);
-      dma(zsrc, base + SL::kZp + wave * 256, 4);
+      const uint8_t *zrow = BITS == 2 ? p.zp + t * 16 : BITS == 4 ? p.zp + t * 32 : p.zp + t * kGroup;
+      dma(zrow + lo_zp, base + SL::kZp + wave * 256, 4);
     }
   };
   auto issue = [&](int step, int slot) {

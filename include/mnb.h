@@ -45,7 +45,7 @@ extern "C" {
 enum {
   MNB_OK = 0,
   MNB_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
-  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, rank not 0/32 */
+  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, K >= 2^28, rank not 0/32 */
   MNB_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned */
   MNB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than mnb_workspace_bytes() */
   MNB_ERR_ALIAS = 5,        /* Y overlaps an input or the workspace */
@@ -170,7 +170,7 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank);
  *   ad     adapter or NULL (see mnb_adapter for when it counts as empty)
  *   Y      fp16 [M, N] row-major; must not overlap X, wq, sc, zpp, the adapter or the
  *          workspace (MNB_ERR_ALIAS)
- *   bits 2, 4 or 8, block 32, K % 32 == 0
+ *   bits 2, 4 or 8, block 32, K % 32 == 0, K < 2^28
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
  * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV

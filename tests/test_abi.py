@@ -59,6 +59,8 @@ def test_packed_sizes_rejects():
     assert mnb.mnb_packed_sizes(64, 33, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
     assert mnb.mnb_packed_sizes(64, 64, 3, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
     assert mnb.mnb_packed_sizes(64, 64, 4, 64, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
+    assert mnb.mnb_packed_sizes(64, 1 << 28, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED   # K < 2^28
+    assert mnb.mnb_packed_sizes(64, (1 << 28) - 32, 4, 32, 0)[0] == mnb.MNB_OK
     assert mnb.mnb_packed_sizes(-1, 64, 4, 32, 0)[0] == mnb.MNB_ERR_INVALID_ARG
 
 
@@ -86,6 +88,7 @@ def test_validation_status_codes():
     assert call(bits=3) == E.MNB_ERR_UNSUPPORTED
     assert call(block=64) == E.MNB_ERR_UNSUPPORTED
     assert call(K=48) == E.MNB_ERR_UNSUPPORTED
+    assert call(K=1 << 28) == E.MNB_ERR_UNSUPPORTED
     assert call(M=-1) == E.MNB_ERR_INVALID_ARG
     assert call(N=-5) == E.MNB_ERR_INVALID_ARG
     assert call(x=None) == E.MNB_ERR_INVALID_ARG
