@@ -95,8 +95,9 @@ __device__ __forceinline__ h2_t byte_pair_hi(uint32_t w) {
 // Control area at the start of the workspace (its layout depends on no shape):
 //   * 64 words: the in-pass T call epoch, the count of done-groups that have finished
 //     reading T and a sticky error word;
-//   * kDoneGroups counters of row workgroups that have read T, one per 256-byte line so
-//     that the increments of different groups do not queue on one address.
+//   * kDoneGroups counters of the in-pass launch's workgroups that have read the epoch,
+//     one per 256-byte line so that the increments of different groups do not queue on
+//     one address.
 // Every counter is back to zero when a call ends.  The in-pass T slices are written in
 // kTReplicas copies (32 words of FP32 value | call tag << 32 per slice), so that the row
 // workgroups' reads spread over many lines.
@@ -133,7 +134,7 @@ struct GemvParams {
   int q;                  // chunk-columns per wave load; a workgroup owns 64/q rows
   int gt;                 // in-pass T: number of T-slice workgroups (first in the grid)
   int kt;                 // in-pass T: k rows per slice
-  int nepi;               // in-pass T: number of row workgroups (epilogues)
+  int nepi;               // in-pass T: number of row workgroups (the launch has gt + nepi)
   int tparts;             // precomputed T: number of K-part partials
   int tmpad;              // precomputed T: rows per partial (= M of the T launch)
   int *ctrl;              // control words

@@ -27,9 +27,10 @@
 //    copy (the last slice's first word), then reads all the words, accepts them
 //    when every tag matches (no fences: the tags make a stale or early read detectable),
 //    adds the slices in slice order and leaves T in LDS for the epilogue.  The slice
-//    workgroups are dispatched first and never wait, so every bounded wait ends.  Row
-//    workgroups report that they have read T through a two-level count (kDoneGroups
-//    counters, then one); the last one resets the counts and advances the epoch.
+//    workgroups are dispatched first and never wait, so every bounded wait ends.  Every
+//    workgroup reports that it has read the epoch through a two-level count (kDoneGroups
+//    counters, then one) issued right after that read; the last arrival resets the counts
+//    and advances the epoch.
 #include <algorithm>
 
 #include "common.h"
@@ -93,6 +94,30 @@ __device__ __forceinline__ bool gather_t(const unsigned long long *tw, int gt, u
   return ok;
 }
 
+// Epoch count: every workgroup of an in-pass launch (slices and rows) arrives once, right
+// after it has read the call epoch, on the counter of its group (id % kDoneGroups, one
+// 256-byte line each); after its own work it checks the value it got back, and the last
+// arrival of a group adds the group to the second-level count, whose last arrival resets
+// both levels and advances the epoch.  So the epoch moves only once every workgroup of the
+// launch holds this call's tag, and the round trips overlap the weight stream instead of
+// delaying the epilogue.
+__device__ __forceinline__ int epoch_arrive(const GemvParams &p, int id) {
+  return __hip_atomic_fetch_add(&p.ctrl[ctrl_done_word(id % kDoneGroups)], 1, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void epoch_leave(const GemvParams &p, int id, int old, uint32_t tag) {
+  const int total = p.gt + p.nepi;
+  const int grp = id % kDoneGroups;
+  const int members = (total - grp + kDoneGroups - 1) / kDoneGroups;
+  const int groups = min(kDoneGroups, total);
+  if (old != members - 1) return;
+  __hip_atomic_store(&p.ctrl[ctrl_done_word(grp)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__hip_atomic_fetch_add(&p.ctrl[CTRL_TDONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == groups - 1) {
+    __hip_atomic_store(&p.ctrl[CTRL_TDONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.ctrl[CTRL_EPOCH], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // One in-pass T slice: words[j][r] = (sum_{k in slice j} x[k] * a[k,r], tag)   (M == 1)
 template <int LORA>
 __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
@@ -100,6 +125,8 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
   const int wave = threadIdx.x >> 6;
   const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT));
+  int arrived = 0;
+  if (threadIdx.x == 0) arrived = epoch_arrive(p, blockIdx.x);
   const int kbeg = j * p.kt;
   const int kend = min(p.K, kbeg + p.kt);
   const _Float16 *x = reinterpret_cast<const _Float16 *>(p.X);
@@ -202,6 +229,7 @@ __device__ void t_slice(const GemvParams &p, int j, float (*tsh)[kRank]) {
       __hip_atomic_store(p.tword + ((size_t)c * p.gt + j) * kRank + lane, word, __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (threadIdx.x == 0) epoch_leave(p, blockIdx.x, arrived, tag);
 }
 
 template <int BITS, bool HAS_ZP, int LORA, int TMODE, int Q, int LPW>
@@ -250,6 +278,8 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       // epilogue and reports that it has read T.
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
+      int arrived = 0;
+      if (lane == 0) arrived = epoch_arrive(p, blockIdx.x);
       const unsigned long long *rep = p.tword + (size_t)(bid % kTReplicas) * p.gt * kRank;
       // hint: one lane polls the first word of the last slice (dispatched last, so as a
       // rule done last); the gather below checks every tag anyway.  A single word per
@@ -273,23 +303,8 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
         if (lane == 0) atomic_store_agent(&p.ctrl[CTRL_ERROR], 1);
       }
       if (lane < kRank) tfin[lane] = tv;
-      // two-level count of the row workgroups that have read T; the last one resets the
-      // counts and advances the epoch for the next call
-      if (lane == 0) {
-        const int grp = bid % kDoneGroups;
-        const int members = (p.nepi - grp + kDoneGroups - 1) / kDoneGroups;
-        const int groups = min(kDoneGroups, p.nepi);
-        int *cnt = &p.ctrl[ctrl_done_word(grp)];
-        if (__hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == members - 1) {
-          __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (__hip_atomic_fetch_add(&p.ctrl[CTRL_TDONE], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-              groups - 1) {
-            __hip_atomic_store(&p.ctrl[CTRL_TDONE], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&p.ctrl[CTRL_EPOCH], (int)tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
       __syncthreads();
+      if (lane == 0) epoch_leave(p, blockIdx.x, arrived, tag);
       return;
     }
   }
