@@ -273,9 +273,10 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
 
   if constexpr (kTWave) {
     if (wave == kWaves) {
-      // T wave: carries no weight loads, so its loads return at once.  It polls one word
-      // of its replica of the final T, reads the 32 tagged words, leaves T in LDS for the
-      // epilogue and reports that it has read T.
+      // T wave: carries no weight loads.  It reads the call epoch and counts itself, polls
+      // one word of its replica of the slices, reads the tagged words of all slices and
+      // leaves T in LDS for the epilogue.  Its loads share the CU's memory pipeline with
+      // the weight stream, so they return behind the workgroup's weight loads.
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
       int arrived = 0;
