@@ -21,10 +21,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmnb.so")
 
 MNB_OK, MNB_ERR_INVALID_ARG, MNB_ERR_UNSUPPORTED, MNB_ERR_MISALIGNED = 0, 1, 2, 3
-MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP = 4, 5, 6
+MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP, MNB_ERR_HANDOFF = 4, 5, 6, 7
 MNB_ADAPTER_NONE, MNB_ADAPTER_F16, MNB_ADAPTER_Q8 = 0, 1, 2
 MNB_PATH_AUTO, MNB_PATH_GEMV, MNB_PATH_GEMM = 0, 1, 2
-MNB_FLAG_T_SEPARATE, MNB_FLAG_ACC4 = 1, 2
+MNB_FLAG_T_SEPARATE, MNB_FLAG_ACC4, MNB_FLAG_FAIL_HANDOFF = 1, 2, 4
 
 
 class mnb_adapter(C.Structure):
@@ -68,6 +68,7 @@ def _load() -> C.CDLL:
     lib.mnb_unpack.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
     lib.mnb_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.mnb_workspace_bytes.restype = S
+    lib.mnb_workspace_error.argtypes = [P, P]
     lib.mnb_matmul.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P]
     lib.mnb_matmul_ex.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, I, I, I, I, I, P, S, P,
                                   C.POINTER(mnb_options)]
@@ -78,7 +79,7 @@ def _load() -> C.CDLL:
     lib.mnb_status_string.restype = C.c_char_p
     lib.mnb_version.argtypes = []
     for f in ("mnb_packed_sizes", "mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
-              "mnb_matmul_bias", "mnb_describe_route", "mnb_version"):
+              "mnb_matmul_bias", "mnb_describe_route", "mnb_version", "mnb_workspace_error"):
         getattr(lib, f).restype = I
     return lib
 
@@ -118,6 +119,10 @@ def mnb_unpack(wq, sc, zpp, N, K, bits, block, codes, scales, zp, stream) -> int
 
 def mnb_workspace_bytes(M, N, K, bits, rank) -> int:
     return lib.mnb_workspace_bytes(M, N, K, bits, rank)
+
+
+def mnb_workspace_error(workspace, stream) -> int:
+    return lib.mnb_workspace_error(workspace, stream)
 
 
 def mnb_matmul(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream) -> int:
@@ -242,6 +247,13 @@ def workspace(dev, nbytes: int):
         ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
+
+
+def workspace_error(ws) -> int:
+    """Reports and clears the workspace's error word: MNB_ERR_HANDOFF if an in-pass T
+    handoff gave up since the last query (its outputs are NaN), else MNB_OK.  Waits for
+    the current stream of the workspace's device."""
+    return mnb_workspace_error(_ptr(ws), _stream(ws.device))
 
 
 def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,

@@ -121,7 +121,7 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
   if (st) return st;
   if (opt) {
     if (opt->path < MNB_PATH_AUTO || opt->path > MNB_PATH_GEMM) return MNB_ERR_INVALID_ARG;
-    if (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4)) return MNB_ERR_INVALID_ARG;
+    if (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4 | MNB_FLAG_FAIL_HANDOFF)) return MNB_ERR_INVALID_ARG;
     if ((opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
   }
   if (ad) {
@@ -214,7 +214,7 @@ bool log_enabled() {
 
 extern "C" {
 
-int mnb_version(void) { return 102; }
+int mnb_version(void) { return 103; }
 
 const char *mnb_status_string(int status) {
   switch (status) {
@@ -225,6 +225,7 @@ const char *mnb_status_string(int status) {
     case MNB_ERR_WORKSPACE: return "MNB_ERR_WORKSPACE: workspace missing or too small";
     case MNB_ERR_ALIAS: return "MNB_ERR_ALIAS: output overlaps an input or the workspace";
     case MNB_ERR_HIP: return "MNB_ERR_HIP: HIP runtime error";
+    case MNB_ERR_HANDOFF: return "MNB_ERR_HANDOFF: an in-pass T handoff gave up, its outputs are NaN";
     default: return "unknown mnb status";
   }
 }
@@ -244,6 +245,22 @@ size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank) {
   (void)bits;
   if (M <= 0 || N <= 0 || K < 0) return 0;
   return ws_layout(M, N, K, rank ? kRank : 0).total;
+}
+
+int mnb_workspace_error(void *workspace, void *stream) {
+  if (!workspace) return MNB_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int *word = static_cast<int *>(workspace) + CTRL_ERROR;   // the control area starts the workspace
+  int v = 0;
+  const int zero = 0;
+  if (hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MNB_ERR_HIP;
+  if (v == 0) return MNB_OK;
+  if (hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MNB_ERR_HIP;
+  return MNB_ERR_HANDOFF;
 }
 
 int mnb_pack(const uint8_t *codes, const void *scales, const uint8_t *zp, int N, int K, int bits, int block,
@@ -280,7 +297,8 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
   int st = check_common(M, N, K, bits, kBlock);
   if (st) return st;
   if (has_adapter_kind < 0 || has_adapter_kind > 2 || !buf || buf_len == 0) return MNB_ERR_INVALID_ARG;
-  if (opt && (opt->path < 0 || opt->path > 2 || (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4))))
+  if (opt && (opt->path < 0 || opt->path > 2 ||
+              (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4 | MNB_FLAG_FAIL_HANDOFF))))
     return MNB_ERR_INVALID_ARG;
   if (opt && (opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) {
@@ -366,6 +384,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     p.q = gemv_rows_split(N, p.gt > 0);
     p.kt = kTSliceRows;
     p.nepi = NG * p.q;
+    p.spin_limit = (opt && (opt->flags & MNB_FLAG_FAIL_HANDOFF)) ? -1 : kSpinLimit;
     p.tparts = tparts;
     p.tmpad = M;
     p.ctrl = reinterpret_cast<int *>(ws + w.ctrl);

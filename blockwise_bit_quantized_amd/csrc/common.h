@@ -135,6 +135,7 @@ struct GemvParams {
   int gt;                 // in-pass T: number of T-slice workgroups (first in the grid)
   int kt;                 // in-pass T: k rows per slice
   int nepi;               // in-pass T: number of row workgroups (the launch has gt + nepi)
+  int spin_limit;         // in-pass T: polls before a row workgroup gives up (-1: at once)
   int tparts;             // precomputed T: number of K-part partials
   int tmpad;              // precomputed T: rows per partial (= M of the T launch)
   int *ctrl;              // control words

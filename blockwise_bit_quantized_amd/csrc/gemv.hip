@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       // rule done last); the gather below checks every tag anyway.  A single word per
       // poll keeps the uncached polling traffic of hundreds of workgroups small.
       int spins = 0;
-      for (; spins < kSpinLimit; ++spins) {
+      for (; spins < p.spin_limit; ++spins) {
         const bool seen = lane != 0 ||
                           (uint32_t)(__hip_atomic_load(rep + (size_t)(p.gt - 1) * kRank, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT) >> 32) == tag;
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
       }
       float tv = 0.f;
       bool ok = false;
-      for (; spins <= kSpinLimit && !ok; ++spins) {
+      for (; spins <= p.spin_limit && !ok; ++spins) {
         ok = __all(gather_t(rep, p.gt, tag, lane, tv));
         if (!ok) __builtin_amdgcn_s_sleep(1);
       }

@@ -49,7 +49,8 @@ enum {
   MNB_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned */
   MNB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than mnb_workspace_bytes() */
   MNB_ERR_ALIAS = 5,        /* Y overlaps an input or the workspace */
-  MNB_ERR_HIP = 6           /* a HIP runtime call failed (no device, launch failure) */
+  MNB_ERR_HIP = 6,          /* a HIP runtime call failed (no device, launch failure) */
+  MNB_ERR_HANDOFF = 7       /* mnb_workspace_error: an in-pass T handoff gave up (outputs NaN) */
 };
 
 /* Adapter kinds (PR #33370: FP16 rank-32 adapters; block-32 INT8 adapters). */
@@ -72,7 +73,12 @@ enum {
    * for T; PR #33800 Description: the lm_head at the default accuracy level 4).  Runs the
    * GEMV family for every M (T from the projection launch when there is an adapter).
    * Requires K <= 16384 and a path of AUTO or GEMV (MNB_ERR_UNSUPPORTED otherwise). */
-  MNB_FLAG_ACC4 = 2
+  MNB_FLAG_ACC4 = 2,
+  /* Test hook for the failure path of the decode's in-pass T handoff: the row workgroups
+   * give up on T without waiting, exactly as when their bounded wait (about 2^22 polls)
+   * expires, so the call's outputs are NaN and the workspace's error word is set (see
+   * mnb_workspace_error).  Only the in-pass decode reads it; never set it for real work. */
+  MNB_FLAG_FAIL_HANDOFF = 4
 };
 
 /*
@@ -162,6 +168,16 @@ int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, in
 size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank);
 
 /*
+ * Reports and clears the workspace's sticky error word.  The decode's in-pass T handoff
+ * (M == 1 with an adapter, one launch) bounds every wait; when a row workgroup's wait
+ * expires it writes NaN for its outputs and sets this word instead of hanging.  Waits for
+ * `stream` (so it is not for use under graph capture), then reads and clears the word.
+ * Returns MNB_OK, MNB_ERR_HANDOFF if the word was set since the last query,
+ * MNB_ERR_INVALID_ARG for a NULL workspace, or MNB_ERR_HIP.
+ */
+int mnb_workspace_error(void *workspace, void *stream);
+
+/*
  * Y[M,N] = X . deq(W)^T (+ (X.A).B), fp16 output rounded to nearest even once, from FP32
  * accumulation.
  *   X      fp16 [M, K] row-major
@@ -212,7 +228,8 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
 /* Static text for a status code. */
 const char *mnb_status_string(int status);
 
-/* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias, 102 mnb_pack_kn. */
+/* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias, 102 mnb_pack_kn, 103
+ * mnb_workspace_error and MNB_FLAG_FAIL_HANDOFF. */
 int mnb_version(void);
 
 #ifdef __cplusplus

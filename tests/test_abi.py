@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for n in ("mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex", "mnb_matmul_bias",
               "mnb_workspace_bytes", "mnb_packed_sizes", "mnb_status_string", "mnb_describe_route",
-              "mnb_version"):
+              "mnb_version", "mnb_workspace_error"):
         assert n in names
 
 
@@ -41,8 +41,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert mnb.mnb_version() == 102
-    for st in range(7):
+    assert mnb.mnb_version() == 103
+    for st in range(8):
         assert mnb.mnb_status_string(st).startswith("MNB_")
     assert "unknown" in mnb.mnb_status_string(99)
 
@@ -183,7 +183,11 @@ def test_accuracy_level4_route_and_validation():
     assert st == mnb.MNB_ERR_UNSUPPORTED                                    # K above 16384
     assert call(opt=mnb.mnb_options(2, A4)) == mnb.MNB_ERR_UNSUPPORTED
     assert call(K=16416, opt=mnb.mnb_options(0, A4)) == mnb.MNB_ERR_UNSUPPORTED
-    assert call(opt=mnb.mnb_options(0, 4)) == mnb.MNB_ERR_INVALID_ARG      # unknown flag
+    assert call(opt=mnb.mnb_options(0, 8)) == mnb.MNB_ERR_INVALID_ARG      # unknown flag
+    # the handoff failure hook is a known flag (the GPU tests exercise it)
+    st, _ = mnb.mnb_describe_route(1, 8192, 2048, 4, 0, 1, mnb.mnb_options(0, mnb.MNB_FLAG_FAIL_HANDOFF))
+    assert st == mnb.MNB_OK
+    assert mnb.mnb_workspace_error(None, None) == mnb.MNB_ERR_INVALID_ARG
 
 
 def test_dispatcher_rule():

@@ -528,3 +528,27 @@ def test_workspace_counters_return_to_zero():
     # epoch: the tag of the last in-pass call, i.e. one past the previous tag per call
     assert epoch == inpass
     assert not ctrl[3:].any(), np.nonzero(ctrl[3:])[0][:8] + 3
+
+
+def test_handoff_failure_reports_and_recovers():
+    """The failure path of the in-pass decode handoff, forced from the host
+    (MNB_FLAG_FAIL_HANDOFF: the row workgroups give up on T at once, as when their bounded
+    wait expires): every output is NaN, the workspace's error word is reported once and
+    cleared, the counters still return to zero and the next call is correct."""
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    c = si.make_random(140, 1, 4096, 2048, 4, False, "f16")
+    pw = dev_weight(c)
+    a = dev_adapter(c["adapter"])
+    X = t16(c["X"])
+    Y = torch.empty((1, c["N"]), dtype=torch.float16, device=DEV)
+    assert mnb.workspace_error(ws) == mnb.MNB_OK
+    mnb.matmul(X, pw, a, flags=mnb.MNB_FLAG_FAIL_HANDOFF, out=Y, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(Y.float()).all()
+    assert mnb.workspace_error(ws) == mnb.MNB_ERR_HANDOFF
+    assert mnb.workspace_error(ws) == mnb.MNB_OK
+    mnb.matmul(X, pw, a, out=Y, ws=ws)
+    torch.cuda.synchronize()
+    compare(Y.cpu().numpy().view(np.uint16), oracle.matmul(c), what="decode after a forced handoff failure")
+    ctrl = ws[:8448].cpu().numpy().view(np.int32)
+    assert int(ctrl[1]) == 0 and int(ctrl[2]) == 0 and not ctrl[3:].any()
