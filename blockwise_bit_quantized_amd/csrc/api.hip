@@ -32,7 +32,7 @@ constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 // initialisation.
 struct WsLayout {
   size_t ctrl, tinpass, tproj, tfinal, ypart, total;
-  int gt, tparts, tmt, splits;
+  int gt, tparts, tmt, splits, tsplits, tail0;
 };
 
 WsLayout ws_layout(int M, int N, int K, int rank) {
@@ -48,10 +48,17 @@ WsLayout ws_layout(int M, int N, int K, int rank) {
   if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
   w.tfinal = off;
   if (rank) off += align_up((size_t)M * kRank * sizeof(float));
-  // prefill GEMM with K split into ranges: FP32 partial outputs [splits, M, N]
+  // prefill GEMM with K split into ranges: FP32 partial outputs [splits, M, N]; or with
+  // only the last round's tiles split: their partials [tsplits, tail tiles, bm, 128]
   w.splits = gemm_splits(M, N, K);
+  w.tsplits = gemm_tail_splits(M, N, K, &w.tail0);
   w.ypart = off;
   if (w.splits > 1) off += align_up((size_t)w.splits * M * N * sizeof(float));
+  if (w.tsplits > 1) {
+    const int bm = gemm_bm(M, N);
+    const size_t ntail = (size_t)cdiv(M, bm) * cdiv(N, 128) - w.tail0;
+    off += align_up((size_t)w.tsplits * ntail * bm * 128 * sizeof(float));
+  }
   w.total = off;
   return w;
 }
@@ -180,8 +187,13 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
     const int bm = gemm_bm(M, N);
-    snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=%dx128x64 splits=%d", tp, bits, has_zp ? "x" : "def", ln,
-             cdiv(M, bm) * cdiv(N, 128) * w.splits, bm, w.splits);
+    const int ntiles = cdiv(M, bm) * cdiv(N, 128);
+    if (w.tsplits > 1)
+      snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=%dx128x64 splits=1 tail=%dx%d", tp, bits,
+               has_zp ? "x" : "def", ln, w.tail0 + (ntiles - w.tail0) * w.tsplits, bm, ntiles - w.tail0, w.tsplits);
+    else
+      snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=%dx128x64 splits=%d", tp, bits, has_zp ? "x" : "def", ln,
+               ntiles * w.splits, bm, w.splits);
   }
 }
 
@@ -450,6 +462,8 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   g.MT = cdiv(M, g.bm);
   g.NT = cdiv(N, 128);
   g.splits = w.splits;
+  g.tsplits = w.tsplits;
+  g.tail0 = w.tail0;
   g.ypart = reinterpret_cast<float *>(ws + w.ypart);
   return launch_gemm(bits, has_zp, lora, g, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
 }

@@ -163,10 +163,13 @@ struct GemmParams {
   const float *tpart;     // T partials [tparts, M, 32]
   uint16_t *Y;
   const uint16_t *bias;   // fp16 [N] broadcast bias or null
-  float *ypart;           // splits > 1: FP32 partial outputs [splits, M, N]
+  float *ypart;           // splits > 1: FP32 partial outputs [splits, M, N];
+                          // tsplits > 1: the tail tiles' partials [tsplits, tail tiles, bm, 128]
   int M, N, K, NG, KB, MT, NT, tparts;
   int splits;             // K ranges per output tile (1: the workgroup stores Y itself)
   int bm;                 // tile rows: 128 or 64
+  int tail0;              // tsplits > 1: tiles from tail0 on (the last round) split K ...
+  int tsplits;            // ... into tsplits ranges; 1: no tail split
 };
 
 struct PackParams {
@@ -190,6 +193,8 @@ hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s);
 int gemm_splits(int M, int N, int K);         // K ranges per output tile of the prefill GEMM
+// K ranges of the tail tiles (1: none) when every tile otherwise runs whole; sets *tail0
+int gemm_tail_splits(int M, int N, int K, int *tail0);
 int gemm_bm(int M, int N);                    // tile rows of the prefill GEMM (64 or 128)
 constexpr int kMaxSplits = 16;
 // K limit: the GEMM's direct loads address X as a uniform row base plus a 32-bit lane

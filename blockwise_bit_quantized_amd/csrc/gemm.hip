@@ -116,25 +116,43 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   // grid, so its L2 fetches half of X and a quarter of the weights (against all of X with
   // column strips: 31% fewer L2 fills at 1024 x 4096 x 4096, same time).  Otherwise each
   // XCD takes a contiguous range of (K range, tile) items, M fastest, sharing weight
-  // columns.
+  // columns.  With a tail split, the head (tiles below tail0, whole K) is mapped that way
+  // and the workgroups after it take (K range, tail tile) items, tiles fastest; tiles are
+  // numbered M fastest, so the tail is the last column strips.
   const int ntiles = p.MT * p.NT;
-  const int nwg = ntiles * p.splits;
-  int item = blockIdx.x;
-  if ((nwg & 7) == 0) item = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
-  const int ks = item / ntiles;              // K range of this workgroup
-  const int tile = item - ks * ntiles;
-  int mt = tile % p.MT, nt = tile / p.MT;
-  if (p.splits == 1 && (p.MT & 1) == 0 && (p.NT & 3) == 0) {
-    const int x = blockIdx.x & 7, u = blockIdx.x >> 3;
-    const int bm = p.MT >> 1, bn = p.NT >> 2;
-    mt = (x & 1) * bm + u % bm;
-    nt = (x >> 1) * bn + u / bm;
+  const bool tailw = p.tsplits > 1 && (int)blockIdx.x >= p.tail0;
+  int ks, tile, mt, nt, nranges;
+  if (tailw) {
+    const int ntail = ntiles - p.tail0;
+    const int u = blockIdx.x - p.tail0;
+    ks = u / ntail;
+    tile = p.tail0 + (u - ks * ntail);
+    nranges = p.tsplits;
+    mt = tile % p.MT;
+    nt = tile / p.MT;
+  } else {
+    const int nhead = p.tsplits > 1 ? p.tail0 : ntiles;
+    const int nwg = nhead * p.splits;
+    int item = blockIdx.x;
+    if ((nwg & 7) == 0) item = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    ks = item / nhead;
+    tile = item - ks * nhead;
+    nranges = p.splits;
+    mt = tile % p.MT;
+    nt = tile / p.MT;
+    const int nth = nhead / p.MT;             // head column strips (when the head is whole strips)
+    if (p.splits == 1 && nhead % p.MT == 0 && (p.MT & 1) == 0 && (nth & 3) == 0) {
+      const int x = blockIdx.x & 7, u = blockIdx.x >> 3;
+      const int bm = p.MT >> 1, bn = nth >> 2;
+      mt = (x & 1) * bm + u % bm;
+      nt = (x >> 1) * bn + u / bm;
+    }
   }
   const int m0 = mt * BMT, n0 = nt * BN;
-  // K-steps [sbase, sbase + nsteps) of the (KB + 1) / 2; the host picks `splits` so that
-  // every range is non-empty
+  // K-steps [sbase, sbase + nsteps) of the (KB + 1) / 2; the host picks `splits` and
+  // `tsplits` so that every range is non-empty
   const int tsteps = (p.KB + 1) / 2;
-  const int sps = (tsteps + p.splits - 1) / p.splits;
+  const int sps = (tsteps + nranges - 1) / nranges;
   const int sbase = ks * sps;
   const int nsteps = min(tsteps, sbase + sps) - sbase;
   // the LoRA term is added once, by the first K range
@@ -546,7 +564,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   constexpr int kPitchH = BN + 8;    // halfs per LDS row of the fp16 tile (rows stay 16-byte aligned)
   constexpr int kPitchF = BN + 4;    // floats per LDS row of the FP32 partial tile
   static_assert(BMT * kPitchF * 4 <= kLdsBytes, "the staged output tile fits the ring");
-  if (p.splits > 1) {
+  if (nranges > 1) {
     // this K range's FP32 partial; the reduction launch adds the ranges in order
     float *tileF = reinterpret_cast<float *>(smem);
     if (kh == 0) {
@@ -560,9 +578,21 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
                 float4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
     }
     __syncthreads();
+    const int c4 = tid & 31;                 // 16-byte chunk of a 512-byte row
+    if (tailw) {
+      // tail tile: the whole BMT x 128 partial, compact (rows and columns past M and N are
+      // written too and never read)
+      float *tp = p.ypart + ((size_t)ks * (ntiles - p.tail0) + (tile - p.tail0)) * (BMT * BN);
+#pragma unroll
+      for (int pass = 0; pass < BMT / 8; ++pass) {
+        const int row = pass * 8 + (tid >> 5);
+        *reinterpret_cast<float4 *>(tp + row * BN + 4 * c4) =
+            *reinterpret_cast<const float4 *>(&tileF[row * kPitchF + 4 * c4]);
+      }
+      return;
+    }
     float *part = p.ypart + (size_t)ks * p.M * p.N;
     const bool vec = (p.N & 3) == 0;
-    const int c4 = tid & 31;                 // 16-byte chunk of a 512-byte row
 #pragma unroll
     for (int pass = 0; pass < BMT / 8; ++pass) {
       const int row = pass * 8 + (tid >> 5);
@@ -672,9 +702,55 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *part, i
   }
 }
 
+// Tail tiles: Y = fp16(sum over the tsplits K ranges of the compact FP32 partials
+// [tsplits, tail tiles, bm, 128], in range order, + bias).  One thread per four
+// consecutive columns of a tile row.
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const float *part, int splits, const uint16_t *bias,
+                                                          uint16_t *Y, int M, int N, int MT, int tail0, int ntail,
+                                                          int bm) {
+  const int per_tile = bm * (BN / 4);            // float4 per tile
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (long)ntail * per_tile) return;
+  const int t = (int)(g / per_tile), w = (int)(g - (long)t * per_tile);
+  const int r = w / (BN / 4), c4 = w - r * (BN / 4);
+  const int tile = tail0 + t;
+  const int m = (tile % MT) * bm + r, n = (tile / MT) * BN + 4 * c4;
+  if (m >= M || n >= N) return;
+  const size_t stride = (size_t)ntail * per_tile;   // float4 between consecutive ranges
+  const float4 *src = reinterpret_cast<const float4 *>(part) + (size_t)t * per_tile + w;
+  float4 v[kMaxSplits];
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k)
+    if (k < splits) v[k] = src[(size_t)k * stride];
+  float y[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+#pragma unroll
+  for (int k = 1; k < kMaxSplits; ++k)
+    if (k < splits) {
+      y[0] += v[k].x;
+      y[1] += v[k].y;
+      y[2] += v[k].z;
+      y[3] += v[k].w;
+    }
+  uint16_t *dst = Y + (size_t)m * N + n;
+  if ((N & 3) == 0) {
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] += h2f(bias[n + e]);
+    }
+    const h2_t lo = {(_Float16)y[0], (_Float16)y[1]};
+    const h2_t hi = {(_Float16)y[2], (_Float16)y[3]};
+    *reinterpret_cast<u2_t *>(dst) = u2_t{as_u32(lo), as_u32(hi)};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n + e < N) dst[e] = __builtin_bit_cast(uint16_t, (_Float16)(bias ? y[e] + h2f(bias[n + e]) : y[e]));
+  }
+}
+
 template <int BITS, bool HAS_ZP>
 hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
-  const dim3 grid(p.MT * p.NT * p.splits), block(kThreads);
+  const int ntiles = p.MT * p.NT;
+  const dim3 grid(p.tsplits > 1 ? p.tail0 + (ntiles - p.tail0) * p.tsplits : ntiles * p.splits), block(kThreads);
   if (p.bm == 64) {
     switch (lora) {
       case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0, 64>), grid, block, 0, s, p); break;
@@ -707,10 +783,22 @@ int gemm_bm(int M, int N) {
 
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s) {
   if (p.splits < 1 || p.splits > kMaxSplits || (p.bm != 64 && p.bm != 128)) return hipErrorInvalidValue;
+  const int ntiles = p.MT * p.NT;
+  if (p.tsplits < 1 || p.tsplits > kMaxSplits ||
+      (p.tsplits > 1 && (p.splits != 1 || p.tail0 < 1 || p.tail0 >= ntiles)))
+    return hipErrorInvalidValue;
   const hipError_t e = bits == 2   ? (has_zp ? launch2<2, true>(lora, p, s) : launch2<2, false>(lora, p, s))
                        : bits == 4 ? (has_zp ? launch2<4, true>(lora, p, s) : launch2<4, false>(lora, p, s))
                                    : (has_zp ? launch2<8, true>(lora, p, s) : launch2<8, false>(lora, p, s));
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (p.tsplits > 1) {
+    const int ntail = ntiles - p.tail0;
+    const long work = (long)ntail * p.bm * (BN / 4);
+    hipLaunchKernelGGL(tail_reduce_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, p.ypart,
+                       p.tsplits, p.bias, p.Y, p.M, p.N, p.MT, p.tail0, ntail, p.bm);
+    return hipGetLastError();
+  }
+  if (p.splits == 1) return e;
   const long MN = (long)p.M * p.N;
   const long work = (p.N & 3) == 0 ? MN / 4 : MN;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, p.ypart, p.splits,
@@ -746,6 +834,43 @@ int gemm_splits(int M, int N, int K) {
       best = S;
     }
   }
+  return best;
+}
+
+// Tail split.  Without K splitting, a grid of `ntiles` tiles over `slots` resident
+// workgroups runs floor(ntiles / slots) full rounds and a last, partly filled one that still
+// takes a whole round's K loop.  Splitting only the last round's tiles into t K ranges
+// (partials for those tiles alone, one reduction over their outputs) shortens that round;
+// t minimises steps(t) * c + [t > 1](2 us + partial bytes / 6 TB/s) over the t whose
+// workgroups still fit the round, the uniform split's model, where a step costs c = 0.8 us
+// with two 64-row workgroups per CU and 0.5 us for one alone on its CU.  Measured on the
+// batched prefill's weights: at M = 512 (608 tiles, the last 96 as 5 ranges) 57.0 -> 51.6 us;
+// at M = 1024 (last 192 tiles, alone on their CUs) splitting gained nothing, and the model
+// leaves it whole.
+int gemm_tail_splits(int M, int N, int K, int *tail0) {
+  const int bm = gemm_bm(M, N);
+  const long ntiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  *tail0 = (int)ntiles;
+  if (gemm_splits(M, N, K) > 1) return 1;
+  const long slots = bm == 64 ? 2 * kCUs : kCUs;
+  const long full = ntiles / slots, rem = ntiles % slots;
+  const int tsteps = (K / kBlock + 1) / 2;
+  if (full == 0 || rem == 0 || tsteps < 4) return 1;
+  auto step_us = [&](long wgs) { return bm == 64 && wgs <= kCUs ? 0.5 : 0.8; };
+  int best = 1;
+  double best_us = tsteps * step_us(rem);
+  for (int t = 2; t <= kMaxSplits; ++t) {
+    if (rem * t > slots) break;
+    const int sps = (tsteps + t - 1) / t;
+    if (sps < 2) break;
+    if ((tsteps + sps - 1) / sps != t) continue;     // some range would be empty
+    const double us = sps * step_us(rem * t) + 2.0 + (2.0 * t + 0.5) * 4.0 * (double)rem * bm * BN / 6e6;
+    if (us < best_us * 0.97) {
+      best_us = us;
+      best = t;
+    }
+  }
+  if (best > 1) *tail0 = (int)(full * slots);
   return best;
 }
 
