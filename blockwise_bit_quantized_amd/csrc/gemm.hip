@@ -814,64 +814,72 @@ hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hip
 //   rounds(tiles * S) * steps(S) * t_step  +  [S > 1] (t_launch + partial bytes / bandwidth)
 // with t_step ~0.8 us per 64-k step of a tile, t_launch ~2 us and ~6 TB/s for the
 // partials (they stay in the Infinity Cache at these sizes); at least 2 K-steps per range.
-int gemm_splits(int M, int N, int K) {
+namespace {
+struct Plan {
+  int splits, tsplits, tail0;
+};
+
+// The uniform split (every tile as S K ranges) and the tail split (only the last round's
+// tiles, as t ranges) from one cost model: a K-step costs 0.8 us per round of resident
+// workgroups, or 0.5 us for 64-row workgroups alone on their CUs (a sparse last round); a
+// split adds 2 us plus its partial bytes at 6 TB/s.  The uniform choice is the one measured
+// before the tail split existed (its sparse-round discount is not applied to S > 1); a tail
+// split replaces it when it is predicted 3% faster than that choice.
+Plan gemm_plan(int M, int N, int K) {
   const int bm = gemm_bm(M, N);
-  const long tiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  const long ntiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
   const int tsteps = (K / kBlock + 1) / 2;
-  if (tiles <= 0 || tsteps <= 0) return 1;
-  int best = 1;
+  Plan plan{1, 1, (int)ntiles};
+  if (ntiles <= 0 || tsteps <= 0) return plan;
+  const long slots = bm == 64 ? 2 * kCUs : kCUs;     // workgroups resident at once
   double best_us = 1e30;
   for (int S = 1; S <= kMaxSplits; ++S) {
     const int sps = (tsteps + S - 1) / S;
     if (S > 1 && sps < 2) break;
     if ((tsteps + sps - 1) / sps != S) continue;     // some range would be empty
-    const long slots = bm == 64 ? 2 * kCUs : kCUs;     // workgroups resident at once
-    const double rounds = (double)((tiles * S + slots - 1) / slots);
+    const double rounds = (double)((ntiles * S + slots - 1) / slots);
     double us = rounds * sps * 0.8;
     if (S > 1) us += 2.0 + (2.0 * S + 0.5) * 4.0 * (double)M * N / 6e6;
     if (us < best_us * 0.97) {
       best_us = us;
-      best = S;
+      plan.splits = S;
     }
   }
-  return best;
-}
-
-// Tail split.  Without K splitting, a grid of `ntiles` tiles over `slots` resident
-// workgroups runs floor(ntiles / slots) full rounds and a last, partly filled one that still
-// takes a whole round's K loop.  Splitting only the last round's tiles into t K ranges
-// (partials for those tiles alone, one reduction over their outputs) shortens that round;
-// t minimises steps(t) * c + [t > 1](2 us + partial bytes / 6 TB/s) over the t whose
-// workgroups still fit the round, the uniform split's model, where a step costs c = 0.8 us
-// with two 64-row workgroups per CU and 0.5 us for one alone on its CU.  Measured on the
-// batched prefill's weights: at M = 512 (608 tiles, the last 96 as 5 ranges) 57.0 -> 51.6 us;
-// at M = 1024 (last 192 tiles, alone on their CUs) splitting gained nothing, and the model
-// leaves it whole.
-int gemm_tail_splits(int M, int N, int K, int *tail0) {
-  const int bm = gemm_bm(M, N);
-  const long ntiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
-  *tail0 = (int)ntiles;
-  if (gemm_splits(M, N, K) > 1) return 1;
-  const long slots = bm == 64 ? 2 * kCUs : kCUs;
   const long full = ntiles / slots, rem = ntiles % slots;
-  const int tsteps = (K / kBlock + 1) / 2;
-  if (full == 0 || rem == 0 || tsteps < 4) return 1;
+  if (full == 0 || rem == 0 || tsteps < 4) return plan;
   auto step_us = [&](long wgs) { return bm == 64 && wgs <= kCUs ? 0.5 : 0.8; };
-  int best = 1;
-  double best_us = tsteps * step_us(rem);
+  const double head_us = full * tsteps * 0.8;
+  if (plan.splits == 1) best_us = head_us + tsteps * step_us(rem);   // the whole last round
+  int best_t = 1;
   for (int t = 2; t <= kMaxSplits; ++t) {
     if (rem * t > slots) break;
     const int sps = (tsteps + t - 1) / t;
     if (sps < 2) break;
-    if ((tsteps + sps - 1) / sps != t) continue;     // some range would be empty
-    const double us = sps * step_us(rem * t) + 2.0 + (2.0 * t + 0.5) * 4.0 * (double)rem * bm * BN / 6e6;
+    if ((tsteps + sps - 1) / sps != t) continue;
+    const double us = head_us + sps * step_us(rem * t) + 2.0 + (2.0 * t + 0.5) * 4.0 * (double)rem * bm * BN / 6e6;
     if (us < best_us * 0.97) {
       best_us = us;
-      best = t;
+      best_t = t;
     }
   }
-  if (best > 1) *tail0 = (int)(full * slots);
-  return best;
+  if (best_t > 1) plan = Plan{1, best_t, (int)(full * slots)};
+  return plan;
+}
+}  // namespace
+
+int gemm_splits(int M, int N, int K) { return gemm_plan(M, N, K).splits; }
+
+// Tail split.  Without K splitting, a grid of `ntiles` tiles over `slots` resident
+// workgroups runs floor(ntiles / slots) full rounds and a last, partly filled one that still
+// takes a whole round's K loop.  Splitting only the last round's tiles into t K ranges
+// (partials for those tiles alone, one reduction over their outputs) shortens that round.
+// Measured: 1024 x 9728 x 2560 at M = 512 (608 tiles of 64 x 128, the last 96 as 5 ranges)
+// 57.0 -> 51.6 us; at M = 1024 its last 192 tiles run alone on their CUs, a split gained
+// nothing and the model leaves them whole.
+int gemm_tail_splits(int M, int N, int K, int *tail0) {
+  const Plan plan = gemm_plan(M, N, K);
+  *tail0 = plan.tail0;
+  return plan.tsplits;
 }
 
 }  // namespace mnb

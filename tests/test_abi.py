@@ -160,11 +160,13 @@ def test_gemm_k_split_rule():
     # the batched prefill: 1216 tiles over 512 slots; its last 192 run alone on their CUs,
     # where splitting their K gains nothing, so all run whole
     assert route(1024, N=9728, K=2560, kind=2).endswith("tile=64x128x64 splits=1")
-    # at M = 512 (608 tiles) only the last round's 96 tiles split K, into 5 ranges
-    assert route(512, N=9728, K=2560, kind=2).endswith("tile=64x128x64 splits=1 tail=96x5")
+    # at M = 512 (608 tiles) only the last round's 96 tiles split K; at 1536x4096x4096 the
+    # tail split (256 tiles in 2) replaces a uniform split in 2 of all 768 tiles
+    assert route(512, N=9728, K=2560, kind=2).endswith("tile=64x128x64 splits=1 tail=96x2")
+    assert route(1536).endswith("tile=64x128x64 splits=1 tail=256x2")
     # a tail split needs at least one full round and a last one with room for the ranges
     assert " tail=" not in route(2048) and " tail=" not in route(1024, N=9728, K=256, kind=2)
-    assert mnb.mnb_workspace_bytes(512, 9728, 2560, 4, 0) >= 5 * 96 * 64 * 128 * 4
+    assert mnb.mnb_workspace_bytes(512, 9728, 2560, 4, 0) >= 2 * 96 * 64 * 128 * 4
     for M in (256, 64):
         assert int(route(M).rsplit("splits=", 1)[1]) > 1
     for M, N, K in ((300, 130, 800), (40, 136, 1056), (1, 64, 32), (129, 257, 320)):
