@@ -821,10 +821,12 @@ struct Plan {
 
 // The uniform split (every tile as S K ranges) and the tail split (only the last round's
 // tiles, as t ranges) from one cost model: a K-step costs 0.8 us per round of resident
-// workgroups, or 0.5 us for 64-row workgroups alone on their CUs (a sparse last round); a
-// split adds 2 us plus its partial bytes at 6 TB/s.  The uniform choice is the one measured
-// before the tail split existed (its sparse-round discount is not applied to S > 1); a tail
-// split replaces it when it is predicted 3% faster than that choice.
+// workgroups, or 0.5 us for 64-row workgroups alone on their CUs (a sparse last round).  A
+// uniform split adds 3.5 us plus its partial traffic (written once, read by the reduction)
+// at 4 TB/s, fitted to 640 x 4096 x 4096 (3 ranges of all 160 tiles: 54.1 us; whole: 43.2
+// us); a tail split adds 2 us plus its smaller partial traffic at 6 TB/s (its measured times
+// match that within 1 us).  The tail split replaces the uniform choice when predicted 3%
+// faster.
 Plan gemm_plan(int M, int N, int K) {
   const int bm = gemm_bm(M, N);
   const long ntiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
@@ -839,7 +841,7 @@ Plan gemm_plan(int M, int N, int K) {
     if ((tsteps + sps - 1) / sps != S) continue;     // some range would be empty
     const double rounds = (double)((ntiles * S + slots - 1) / slots);
     double us = rounds * sps * 0.8;
-    if (S > 1) us += 2.0 + (2.0 * S + 0.5) * 4.0 * (double)M * N / 6e6;
+    if (S > 1) us += 3.5 + (2.0 * S + 0.5) * 4.0 * (double)M * N / 4e6;
     if (us < best_us * 0.97) {
       best_us = us;
       plan.splits = S;

@@ -160,10 +160,14 @@ def test_gemm_k_split_rule():
     # the batched prefill: 1216 tiles over 512 slots; its last 192 run alone on their CUs,
     # where splitting their K gains nothing, so all run whole
     assert route(1024, N=9728, K=2560, kind=2).endswith("tile=64x128x64 splits=1")
-    # at M = 512 (608 tiles) only the last round's 96 tiles split K; at 1536x4096x4096 the
-    # tail split (256 tiles in 2) replaces a uniform split in 2 of all 768 tiles
+    # at M = 512 (608 tiles) only the last round's 96 tiles split K; at 1280x4096x4096 the
+    # tail split (128 tiles in 2) replaces a uniform split in 2 of all 640 tiles; at 1536 the
+    # last 256 tiles run alone on their CUs and stay whole
     assert route(512, N=9728, K=2560, kind=2).endswith("tile=64x128x64 splits=1 tail=96x2")
-    assert route(1536).endswith("tile=64x128x64 splits=1 tail=256x2")
+    assert route(1280).endswith("tile=64x128x64 splits=1 tail=128x2")
+    assert route(1536).endswith("tile=64x128x64 splits=1")
+    # a uniform split costs its partial traffic: none for 160 tiles of 128 rows at M = 640
+    assert route(640).endswith("tile=128x128x64 splits=1")
     # a tail split needs at least one full round and a last one with room for the ranges
     assert " tail=" not in route(2048) and " tail=" not in route(1024, N=9728, K=256, kind=2)
     assert mnb.mnb_workspace_bytes(512, 9728, 2560, 4, 0) >= 2 * 96 * 64 * 128 * 4
