@@ -230,15 +230,17 @@ def test_gemm_split_k_ranges(bits, adapter):
 TAIL_SHAPES = [(1000, 4202, 1056), (960, 4354, 1056), (1000, 4100, 640)]
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
-def test_gemm_tail_split(adapter):
+def test_gemm_tail_split(bits, adapter):
     """Shapes whose last round of tiles is mostly empty: only those tiles split K (odd
     block counts, ragged M, N % 4 != 0 for the scalar reduction, a head that ends inside a
     column strip) and must still match."""
     for i, (M, N, K) in enumerate(TAIL_SHAPES):
-        _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, {None: 0, "f16": 1, "q8": 2}[adapter], mnb.mnb_options(2, 0))
+        _, desc = mnb.mnb_describe_route(M, N, K, bits, 1, {None: 0, "f16": 1, "q8": 2}[adapter],
+                                         mnb.mnb_options(2, 0))
         assert " tail=" in desc, desc
-        case = si.make_random(230 + i, M, N, K, 4, i % 2 == 0, adapter, bias=i == 1)
+        case = si.make_random(230 + i, M, N, K, bits, i % 2 == 0, adapter, bias=i == 1)
         rows = [0, 1, 63, 64, 511, 512, M - 65, M - 1]
         compare(run(case, 2, 0)[rows], oracle.matmul(rows_case(case, rows)), what="tail M=%d N=%d K=%d" % (M, N, K))
 
