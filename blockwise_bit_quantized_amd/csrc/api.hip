@@ -356,10 +356,11 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
 
   // T projection output: FP32 partials per K-part; consumers read `tparts` parts.  For
   // 2 <= M <= 16, whose consumers would add the parts row by row, the projection reduces
-  // them itself (per-tile arrival counter, agent-scope fences).  Above that the fences
-  // cost more than they save (each writes back and invalidates an L2), so the projection
-  // uses 512-k parts and the GEMM adds them (eight loads in flight, then one at a time);
-  // the M == 1 GEMV adds up to 8 with its loads in flight together.
+  // them itself (per-tile arrival counter; device-coherent stores and loads, no fences).
+  // Above that the reduction costs more than the consumer's part loads it saves (measured
+  // for every M: 1024 x 4096 x 4096 49.7 -> 54.1 us), so the projection uses 512-k parts
+  // and the GEMM adds them (eight loads in flight, then one at a time); the M == 1 GEMV
+  // adds up to 8 with its loads in flight together.
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   int tparts = w.tparts;
   if (r.tproj) {

@@ -48,18 +48,10 @@ __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2
 __device__ __forceinline__ uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
-// Device-scope (all XCDs) ordering.  Partial sums written by one workgroup and read by
-// another that may sit on another XCD go through release/acquire at agent scope.
-__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ int atomic_add_agent(int *p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int atomic_load_agent(const int *p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Device-scope (all XCDs) store of a flag word, written through the L2 (no fence: agent-
+// scope fences write back and invalidate a whole L2 on this part).
 __device__ __forceinline__ void atomic_store_agent(int *p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Convert 4-bit codes to fp16 pairs: 0x6400 is 1024.0 in binary16, so OR-ing a 4-bit
