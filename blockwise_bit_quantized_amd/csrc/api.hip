@@ -171,8 +171,9 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   if (r.acc4) {
     const int NG = cdiv(N, kGroup);
     const int q = gemv_rows_split(N, false);
-    snprintf(buf, len, "%sgemv_acc4_b%d_zp%s_%s grid=%dx%d rows=%d q=%d", tp, bits, has_zp ? "x" : "def", ln, NG * q, M,
-             kGroup / q, q);
+    const int mr = acc4_rows_mr(M, N, K);
+    snprintf(buf, len, "%sgemv_acc4_b%d_zp%s_%s grid=%dx%d rows=%d q=%d mr=%d", tp, bits, has_zp ? "x" : "def", ln,
+             NG * q, cdiv(M, mr), kGroup / q, q, mr);
   } else if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
     const int NG = cdiv(N, kGroup);
     const int q = gemv_rows_split(N, false);
@@ -404,7 +405,8 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     p.tin = tproj_out;
     p.tword = reinterpret_cast<unsigned long long *>(ws + w.tinpass);
     if (r.acc4) {
-      // accuracy level 4: one X row per workgroup row (T from the projection launch)
+      // accuracy level 4: 4 X rows per workgroup row (M > 1, K <= 4096, wide grid) or one
+      // (T from the projection launch); grid rows count X rows here, the launcher groups them
       p.gt = 0;
       p.q = gemv_rows_split(N, false);
       for (int m0 = 0; m0 < M; m0 += 65535) {

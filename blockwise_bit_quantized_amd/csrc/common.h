@@ -180,6 +180,8 @@ hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvPar
 hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s);
 // accuracy level 4 (int8 block-quantized activations for the base product), any M
 constexpr int kAcc4MaxK = 16384;
+constexpr int kAcc4MultiRowMaxK = 4096;       // K limit of the 4-rows-per-workgroup form
+int acc4_rows_mr(int M, int N, int K);        // X rows per workgroup row (1 or 4)
 hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
                             hipStream_t s);
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);

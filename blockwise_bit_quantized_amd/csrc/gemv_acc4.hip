@@ -9,17 +9,19 @@
 // K): amax = max |x| in FP32, inv = 127 / amax, q = rint(x * inv) clamped to [-127, 127],
 // sx = amax / 127, all FP32 with round to nearest even; an all-zero block has q = 0.
 //
-// Per workgroup (8 waves, one X row, 64/Q weight rows of one 64-row group, as the decode
-// GEMV):
+// Per workgroup (8 waves, MR X rows -- 4 when M > 1, K <= 4096 and the grid is wide, else
+// 1 -- and 64/Q weight rows of one 64-row group, as the decode GEMV), so the weights stream
+// once per MR rows:
 //  * each thread loads its 16-byte pieces of the X row first, then the weight stream;
-//  * the X row is quantized into LDS: four threads share a block (max and sum by lane
+//  * the X rows are quantized into LDS: four threads share a block (max and sum by lane
 //    exchange); the int8 codes are stored in the byte order the weight codes unpack to
 //    (4-bit: (w & 0x0F0F0F0F) holds k 0, 4, 1, 5 of a word, (w >> 4) & .. k 2, 6, 3, 7;
 //    2-bit: (w >> 2e) & 0x03030303 holds k 2e, 8+2e, 2e+1, 9+2e; 8-bit: natural order),
 //    with sx per block and the code sum per 16 k;
-//  * per 16-byte chunk: exact int32 sums of q_w * q_x by v_dot4_i32_i8 (8-bit codes as
-//    q - 128), minus z_eff * sum(q_x) (z_eff = z, or z - 128 for 8-bit), so the partial
-//    is the exact integer sum of (q - z) * q_x; it is scaled once by sx * s in FP32.
+//  * per 16-byte chunk and X row: exact int32 sums of q_w * q_x by v_dot4_i32_i8 (8-bit
+//    codes as q - 128; the unpacked code words are shared by the rows), minus
+//    z_eff * sum(q_x) (z_eff = z, or z - 128 for 8-bit), so the partial is the exact
+//    integer sum of (q - z) * q_x; it is scaled once by sx * s in FP32.
 #include "common.h"
 
 namespace mnb {
@@ -43,19 +45,21 @@ __device__ __forceinline__ int xq_pos(int t) {
   }
 }
 
-template <int BITS, bool HAS_ZP, int LORA, int Q, int LPW>
+template <int BITS, bool HAS_ZP, int LORA, int Q, int LPW, int MR>
 __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
   constexpr int R = kGroup / Q;                                   // rows per workgroup
   constexpr int KPC = BITS == 2 ? 64 : 32 / (BITS / 4);           // k per chunk
-  __shared__ float red[kWaves][kGroup];
-  __shared__ __attribute__((aligned(16))) int8_t xq[kAcc4MaxK];   // quantized X row
-  __shared__ float sxs[kAcc4MaxK / 32];                           // sx per block
-  __shared__ int sqs[kAcc4MaxK / 16];                             // sum of codes per 16 k
+  constexpr int KM = MR == 1 ? kAcc4MaxK : kAcc4MultiRowMaxK;     // K capacity per X row
+  __shared__ float red[kWaves][MR][kGroup];
+  __shared__ __attribute__((aligned(16))) int8_t xq[MR * KM];     // quantized X rows
+  __shared__ float sxs[MR * KM / 32];                             // sx per block
+  __shared__ int sqs[MR * KM / 16];                               // sum of codes per 16 k
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m = blockIdx.y;
+  const int m0 = blockIdx.y * MR;                                 // first X row
+  const int nrows = min(MR, p.M - m0);
   int wgi = blockIdx.x;
   if (Q > 1 && (p.NG & 7) == 0) {
     const int x = wgi & 7, u = wgi >> 3;
@@ -69,20 +73,27 @@ __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
   const int ncc = chunk_cols(BITS, p.KB);
   const int nloads = (ncc + Q - 1) / Q;
   const size_t tile0 = (size_t)g * p.KB;
-  const _Float16 *xrow = reinterpret_cast<const _Float16 *>(p.X) + (size_t)m * p.K;
+  const _Float16 *X = reinterpret_cast<const _Float16 *>(p.X);
 
   // 1. this thread's X pieces (8 halfs each) first: their wait then does not wait for the
-  //    weight stream issued after them
-  constexpr int kMaxPieces = kAcc4MaxK / 8 / kThreads;
-  const int npieces = p.K / 8;
+  //    weight stream issued after them.  Piece pc is piece pc % (K/8) of row m0 + pc / (K/8)
+  //    (a block's four pieces never straddle two rows, as K % 32 == 0)
+  constexpr int kMaxPieces = MR * KM / 8 / kThreads;
+  const int rpieces = p.K / 8;
+  const int npieces = nrows * rpieces;
   u4_t xv[kMaxPieces];
 #pragma unroll
   for (int i = 0; i < kMaxPieces; ++i) {
+    if (i * kThreads >= npieces) break;       // uniform: passes past the last piece
     const int pc = tid + i * kThreads;
-    xv[i] = *reinterpret_cast<const u4_t *>(xrow + 8 * (pc < npieces ? pc : 0));
+    const int pcl = pc < npieces ? pc : 0;
+    const int r = pcl / rpieces;
+    xv[i] = *reinterpret_cast<const u4_t *>(X + (size_t)(m0 + r) * p.K + 8 * (pcl - r * rpieces));
   }
 
-  float acc = 0.f;
+  float acc[MR];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) acc[r] = 0.f;
   for (int l0 = 0; l0 < nloads; l0 += kWaves * LPW) {
     const int lend = min(nloads, l0 + kWaves * LPW);
     // 2. weight stream of the round
@@ -121,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
     if (l0 == 0) {
 #pragma unroll
       for (int i = 0; i < kMaxPieces; ++i) {
+        if (i * kThreads >= npieces) break;
         const int pc = tid + i * kThreads;
         float v[8];
 #pragma unroll
@@ -144,11 +156,12 @@ __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
         }
         sum += __shfl_xor(sum, 1);     // the 16 k of this piece and its neighbour
         if (pc < npieces) {
-          const int kb = pc >> 2, t0 = 8 * (pc & 3);
+          const int r = pc / rpieces, lp = pc - r * rpieces;
+          const int kb = lp >> 2, t0 = 8 * (lp & 3);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) xq[32 * kb + xq_pos<BITS>(t0 + e)] = (int8_t)q[e];
-          if ((pc & 1) == 0) sqs[pc >> 1] = sum;
-          if ((pc & 3) == 0) sxs[kb] = amax / 127.f;
+          for (int e = 0; e < 8; ++e) xq[r * KM + 32 * kb + xq_pos<BITS>(t0 + e)] = (int8_t)q[e];
+          if ((lp & 1) == 0) sqs[r * (KM / 16) + (lp >> 1)] = sum;
+          if ((lp & 3) == 0) sxs[r * (KM / 32) + kb] = amax / 127.f;
         }
       }
       __syncthreads();
@@ -161,94 +174,140 @@ __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
       const int cc = l * Q + qi;
       if (l < lend && cc < ncc) {
         const int k0 = cc * KPC;                      // first k of the chunk
-        const int *xw = reinterpret_cast<const int *>(xq + k0);
         if constexpr (BITS == 4) {
           const int kb = cc;
-          int isum = 0;
+          int wlo[4], whi[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t w = cw[i][j];
-            isum = __builtin_amdgcn_sdot4((int)(w & 0x0F0F0F0Fu), xw[2 * j], isum, false);
-            isum = __builtin_amdgcn_sdot4((int)((w >> 4) & 0x0F0F0F0Fu), xw[2 * j + 1], isum, false);
+            wlo[j] = (int)(cw[i][j] & 0x0F0F0F0Fu);
+            whi[j] = (int)((cw[i][j] >> 4) & 0x0F0F0F0Fu);
           }
-          const int part = isum - (int)zraw[i] * (sqs[2 * kb] + sqs[2 * kb + 1]);
-          acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)sraw[i]), acc);
+          const float s = h2f((uint16_t)sraw[i]);
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            if (r < nrows) {
+              const int *xw = reinterpret_cast<const int *>(xq + r * KM + k0);
+              int isum = 0;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                isum = __builtin_amdgcn_sdot4(wlo[j], xw[2 * j], isum, false);
+                isum = __builtin_amdgcn_sdot4(whi[j], xw[2 * j + 1], isum, false);
+              }
+              const int *sq = sqs + r * (KM / 16);
+              const int part = isum - (int)zraw[i] * (sq[2 * kb] + sq[2 * kb + 1]);
+              acc[r] = fmaf((float)part, sxs[r * (KM / 32) + kb] * s, acc[r]);
+            }
+          }
         } else if constexpr (BITS == 2) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int kb = 2 * cc + h;
             if (kb < p.KB) {
-              int isum = 0;
+              int wc[2][4];
 #pragma unroll
-              for (int j = 0; j < 2; ++j) {
-                const uint32_t w = cw[i][2 * h + j];
+              for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  isum = __builtin_amdgcn_sdot4((int)((w >> (2 * e)) & 0x03030303u), xw[8 * h + 4 * j + e], isum, false);
-              }
+                for (int e = 0; e < 4; ++e) wc[j][e] = (int)((cw[i][2 * h + j] >> (2 * e)) & 0x03030303u);
               const int z = (int)((zraw[i] >> (8 * h)) & 0xFFu);
-              const int part = isum - z * (sqs[2 * kb] + sqs[2 * kb + 1]);
-              acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)(sraw[i] >> (16 * h))), acc);
+              const float s = h2f((uint16_t)(sraw[i] >> (16 * h)));
+#pragma unroll
+              for (int r = 0; r < MR; ++r) {
+                if (r < nrows) {
+                  const int *xw = reinterpret_cast<const int *>(xq + r * KM + k0);
+                  int isum = 0;
+#pragma unroll
+                  for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) isum = __builtin_amdgcn_sdot4(wc[j][e], xw[8 * h + 4 * j + e], isum, false);
+                  const int *sq = sqs + r * (KM / 16);
+                  const int part = isum - z * (sq[2 * kb] + sq[2 * kb + 1]);
+                  acc[r] = fmaf((float)part, sxs[r * (KM / 32) + kb] * s, acc[r]);
+                }
+              }
             }
           }
         } else {
           const int kb = cc >> 1;
-          int isum = 0;
+          int wc[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) isum = __builtin_amdgcn_sdot4((int)(cw[i][j] ^ 0x80808080u), xw[j], isum, false);
-          const int part = isum - ((int)zraw[i] - 128) * sqs[cc];
-          acc = fmaf((float)part, sxs[kb] * h2f((uint16_t)sraw[i]), acc);
+          for (int j = 0; j < 4; ++j) wc[j] = (int)(cw[i][j] ^ 0x80808080u);
+          const float s = h2f((uint16_t)sraw[i]);
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            if (r < nrows) {
+              const int *xw = reinterpret_cast<const int *>(xq + r * KM + k0);
+              int isum = 0;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) isum = __builtin_amdgcn_sdot4(wc[j], xw[j], isum, false);
+              const int part = isum - ((int)zraw[i] - 128) * sqs[r * (KM / 16) + cc];
+              acc[r] = fmaf((float)part, sxs[r * (KM / 32) + kb] * s, acc[r]);
+            }
+          }
         }
       }
     }
   }
 
   // lanes sharing a row, then waves, in fixed order
-  if constexpr (Q >= 8) acc += __shfl_xor(acc, 8);
-  if constexpr (Q >= 4) acc += __shfl_xor(acc, 16);
-  if constexpr (Q >= 2) acc += __shfl_xor(acc, 32);
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    if constexpr (Q >= 8) acc[r] += __shfl_xor(acc[r], 8);
+    if constexpr (Q >= 4) acc[r] += __shfl_xor(acc[r], 16);
+    if constexpr (Q >= 2) acc[r] += __shfl_xor(acc[r], 32);
+    red[wave][r][lane] = acc[r];
+  }
   __syncthreads();
   if (wave != 0) return;
-  float total = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) total += red[w][rl];
 
   const bool active = lane < R && n < p.N;
-  float lora = 0.f;
-  if constexpr (LORA != LORA_NONE) {
-    // T (FP32 partials per K-part of the projection launch, added in part order) from the
-    // original FP16 X; this lane's column of B
-    const float *src = p.tin + (size_t)m * kRank + (lane & 31);
-    float tv = 0.f;
-    for (int pp = 0; pp < p.tparts; ++pp) tv += src[(size_t)pp * p.tmpad * kRank];
-    const size_t nb = active ? n : 0;
-    float bscale = 1.f;
-    if constexpr (LORA == LORA_Q8) bscale = h2f(p.sB[nb]);
+  const size_t nb = active ? n : 0;
+  float bscale = 1.f;
+  if constexpr (LORA == LORA_Q8) bscale = h2f(p.sB[nb]);
+  for (int xr = 0; xr < nrows; ++xr) {
+    const int m = m0 + xr;
+    float total = 0.f;
 #pragma unroll
-    for (int r = 0; r < kRank; ++r) {
-      const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
-      float b;
-      if constexpr (LORA == LORA_F16) b = h2f(static_cast<const uint16_t *>(p.B)[(size_t)r * p.N + nb]);
-      else b = (float)static_cast<const int8_t *>(p.B)[(size_t)r * p.N + nb];
-      lora = fmaf(tr, b, lora);
+    for (int w = 0; w < kWaves; ++w) total += red[w][xr][rl];
+    float lora = 0.f;
+    if constexpr (LORA != LORA_NONE) {
+      // T (FP32 partials per K-part of the projection launch, added in part order) from
+      // the original FP16 X; this lane's column of B
+      const float *src = p.tin + (size_t)m * kRank + (lane & 31);
+      float tv = 0.f;
+      for (int pp = 0; pp < p.tparts; ++pp) tv += src[(size_t)pp * p.tmpad * kRank];
+#pragma unroll
+      for (int r = 0; r < kRank; ++r) {
+        const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
+        float b;
+        if constexpr (LORA == LORA_F16) b = h2f(static_cast<const uint16_t *>(p.B)[(size_t)r * p.N + nb]);
+        else b = (float)static_cast<const int8_t *>(p.B)[(size_t)r * p.N + nb];
+        lora = fmaf(tr, b, lora);
+      }
+      lora *= bscale;
     }
-    lora *= bscale;
+    if (active) {
+      float y = total + lora;
+      if (p.bias) y += h2f(p.bias[n]);
+      p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
+    }
   }
-  if (active) {
-    float y = total + lora;
-    if (p.bias) y += h2f(p.bias[n]);
-    p.Y[(size_t)m * p.N + n] = __builtin_bit_cast(uint16_t, (_Float16)y);
-  }
+}
+
+template <int BITS, bool HAS_ZP, int LORA, int Q, int MR>
+hipError_t launch_m4(const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
+  const dim3 grid(gx, gy), block(kThreads);
+  if (lpw <= 2) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 2, MR>), grid, block, 0, s, p);
+  else if (lpw <= 4) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 4, MR>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 8, MR>), grid, block, 0, s, p);
+  return hipGetLastError();
 }
 
 template <int BITS, bool HAS_ZP, int LORA, int Q>
 hipError_t launch_q4(const GemvParams &p, int lpw, int gx, int gy, hipStream_t s) {
-  const dim3 grid(gx, gy), block(kThreads);
-  if (lpw <= 2) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 2>), grid, block, 0, s, p);
-  else if (lpw <= 4) hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 4>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((gemv_acc4_kernel<BITS, HAS_ZP, LORA, Q, 8>), grid, block, 0, s, p);
-  return hipGetLastError();
+  // gy counts X rows; a workgroup row takes acc4_rows_mr of them
+  const int mr = acc4_rows_mr(p.M, p.N, p.K);
+  if (mr == 4) return launch_m4<BITS, HAS_ZP, LORA, Q, 4>(p, lpw, gx, (gy + 3) / 4, s);
+  return launch_m4<BITS, HAS_ZP, LORA, Q, 1>(p, lpw, gx, gy, s);
 }
 
 template <int BITS, bool HAS_ZP, int LORA>
@@ -276,6 +335,15 @@ hipError_t launch_b4(bool has_zp, int lora, const GemvParams &p, int lpw, int gx
 }
 
 }  // namespace
+
+// X rows per workgroup row: 4 when there are several rows, they fit the LDS budget
+// (K <= kAcc4MultiRowMaxK) and one row group alone fills the chip (>= 256 workgroups), so
+// the weights stream once per 4 rows; else 1.  (8 rows measured slower: their registers
+// leave room for one workgroup per CU.)
+int acc4_rows_mr(int M, int N, int K) {
+  const int wgs = (N + kGroup - 1) / kGroup * gemv_rows_split(N, false);
+  return M >= 2 && K <= kAcc4MultiRowMaxK && wgs >= 256 ? 4 : 1;
+}
 
 hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
                             hipStream_t s) {

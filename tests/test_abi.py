@@ -189,6 +189,11 @@ def test_accuracy_level4_route_and_validation():
     assert route(1, kind=0, flags=A4).startswith("gemv_acc4_b4_zpx_none")
     assert "gemv_acc4" in route(1024, flags=A4) and "gemv_acc4" in route(5, bits=8, kind=0, flags=A4)
     assert "gemv_acc4_b2" in route(3, bits=2, flags=A4, path=1)
+    # 4 X rows per workgroup row when the grid is wide and K <= 4096, else one
+    assert route(8, N=49152, K=576, bits=8, kind=0, flags=A4).endswith("grid=768x2 rows=64 q=1 mr=4")
+    assert route(13, flags=A4).endswith("grid=512x4 rows=8 q=8 mr=4")
+    assert route(1, flags=A4).endswith("mr=1") and route(8, K=4128, flags=A4).endswith("grid=512x8 rows=8 q=8 mr=1")
+    assert route(3, N=896, K=896, flags=A4).endswith("grid=112x3 rows=8 q=8 mr=1")
     st, _ = mnb.mnb_describe_route(4, 4096, 4096, 4, 1, 1, mnb.mnb_options(2, A4))
     assert st == mnb.MNB_ERR_UNSUPPORTED                                    # forced GEMM
     st, _ = mnb.mnb_describe_route(1, 64, 16416, 4, 1, 1, mnb.mnb_options(0, A4))

@@ -391,8 +391,12 @@ def test_default_zero_point_equals_explicit():
 # accuracy level 4 (int8 block-quantized activations for the base product)
 # ------------------------------------------------------------------------------------------
 
+# M > 1 with K <= 4096 and >= 256 workgroups runs 4 X rows per workgroup row (N >= 4096:
+# M = 8, 6 and 13, the last with K = 4096, its largest K, and a ragged last group); the
+# narrow shapes and K > 4096 one row per workgroup row
 ACC4_SHAPES = [(1, 64, 32), (1, 100, 96), (3, 130, 160), (1, 8192, 2048), (2, 200, 1024), (130, 257, 320),
-               (9, 70, 192), (1, 49152, 576), (1, 64, 16384)]
+               (9, 70, 192), (1, 49152, 576), (1, 64, 16384), (8, 49152, 576), (13, 4096, 4096), (6, 4096, 640),
+               (3, 72, 4128)]
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
@@ -428,11 +432,12 @@ def acc4_exact_case(seed, M, N, K, bits, zp, kind):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("kind", [None, "f16"], ids=["base", "f16"])
-@pytest.mark.parametrize("M", [1, 6])
+@pytest.mark.parametrize("M", [1, 6, 11])
 def test_acc4_exact_bit_exact(bits, kind, M):
     """On exactly representable activations accuracy level 4 is lossless: GPU == oracle at
     level 4 == oracle at level 0, bit for bit."""
-    case = acc4_exact_case(500 + 10 * bits + M, M, 192, 320, bits, bits != 8, kind)
+    N = 4096 if M == 11 else 192           # M = 11 takes 4 X rows per workgroup row
+    case = acc4_exact_case(500 + 10 * bits + M, M, N, 320, bits, bits != 8, kind)
     want = oracle.f64_to_f16(oracle.matmul(dict(case, acc_level=4)))
     assert same_bits(want, oracle.f64_to_f16(oracle.matmul(case)))
     assert same_bits(run(case, 0, mnb.MNB_FLAG_ACC4), want)
