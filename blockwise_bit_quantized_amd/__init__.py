@@ -168,6 +168,21 @@ def _stream(dev):
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _need(t, name, dtype, shape=None, dev=None, min_numel=None):
+    """Argument check only (no arithmetic): dtype, contiguity, device and shape, so that the
+    library never reads or writes past a tensor's storage."""
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dev is not None and t.device != dev:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError("%s holds %d elements, needs at least %d" % (name, t.numel(), min_numel))
+
+
 @dataclass
 class PackedWeight:
     wq: object          # torch.uint8 device tensor
@@ -176,6 +191,15 @@ class PackedWeight:
     N: int
     K: int
     bits: int
+
+    def check(self, dev):
+        import torch
+        st, wqb, scb, zpb = mnb_packed_sizes(self.N, self.K, self.bits, 32, self.zp is not None)
+        _check(st)
+        _need(self.wq, "packed codes", torch.uint8, dev=dev, min_numel=wqb)
+        _need(self.sc, "packed scales", torch.float16, dev=dev, min_numel=scb // 2)
+        if self.zp is not None:
+            _need(self.zp, "packed zero points", torch.uint8, dev=dev, min_numel=zpb)
 
 
 @dataclass
@@ -191,14 +215,40 @@ class Adapter:
         return mnb_adapter(self.kind, self.rank, _ptr(self.A), _ptr(self.A_scales), _ptr(self.B),
                            _ptr(self.B_scales))
 
+    def is_empty(self) -> bool:
+        return self.kind == MNB_ADAPTER_NONE or self.rank == 0 or self.A is None or self.B is None
+
+    def check(self, N, K, dev):
+        """Shapes and dtypes of a non-empty adapter (rank 32; the library rejects others)."""
+        import torch
+        if self.is_empty() or self.rank != 32:
+            return
+        r = self.rank
+        if self.kind == MNB_ADAPTER_F16:
+            _need(self.A, "adapter A", torch.float16, (K, r), dev)
+            _need(self.B, "adapter B", torch.float16, (r, N), dev)
+        elif self.kind == MNB_ADAPTER_Q8:
+            _need(self.A, "adapter A", torch.int8, (K, r), dev)
+            _need(self.B, "adapter B", torch.int8, (r, N), dev)
+            if self.A_scales is None or self.B_scales is None:
+                raise ValueError("an INT8 adapter needs A_scales and B_scales")
+            _need(self.A_scales, "adapter A_scales", torch.float16, (K // 32, r), dev)
+            _need(self.B_scales, "adapter B_scales", torch.float16, None, dev, N)
+            if self.B_scales.numel() != N:
+                raise ValueError("adapter B_scales must hold N = %d values" % N)
+
 
 def pack(codes, scales, zp, bits: int) -> PackedWeight:
     """Pack device tensors codes uint8 [N,K], scales fp16 [N,K/32], zp uint8 [N,K/32] | None."""
     import torch
     N, K = codes.shape
+    dev = codes.device
+    _need(codes, "codes", torch.uint8, (N, K), dev)
+    _need(scales, "scales", torch.float16, (N, K // 32), dev)
+    if zp is not None:
+        _need(zp, "zp", torch.uint8, (N, K // 32), dev)
     st, wqb, scb, zpb = mnb_packed_sizes(N, K, bits, 32, zp is not None)
     _check(st)
-    dev = codes.device
     wq = torch.empty(wqb, dtype=torch.uint8, device=dev)
     sc = torch.empty(scb // 2, dtype=torch.float16, device=dev)
     zpp = torch.empty(zpb, dtype=torch.uint8, device=dev) if zp is not None else None
@@ -212,9 +262,13 @@ def pack_kn(codes_kn, scales_kn, zp_kn, bits: int) -> PackedWeight:
     zp uint8 [K/32,N] | None (device tensors)."""
     import torch
     K, N = codes_kn.shape
+    dev = codes_kn.device
+    _need(codes_kn, "codes_kn", torch.uint8, (K, N), dev)
+    _need(scales_kn, "scales_kn", torch.float16, (K // 32, N), dev)
+    if zp_kn is not None:
+        _need(zp_kn, "zp_kn", torch.uint8, (K // 32, N), dev)
     st, wqb, scb, zpb = mnb_packed_sizes(N, K, bits, 32, zp_kn is not None)
     _check(st)
-    dev = codes_kn.device
     wq = torch.empty(wqb, dtype=torch.uint8, device=dev)
     sc = torch.empty(scb // 2, dtype=torch.float16, device=dev)
     zpp = torch.empty(zpb, dtype=torch.uint8, device=dev) if zp_kn is not None else None
@@ -226,6 +280,7 @@ def pack_kn(codes_kn, scales_kn, zp_kn, bits: int) -> PackedWeight:
 def unpack(pw: PackedWeight):
     import torch
     dev = pw.wq.device
+    pw.check(dev)
     codes = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=dev)
     scales = torch.empty((pw.N, pw.K // 32), dtype=torch.float16, device=dev)
     zp = torch.empty((pw.N, pw.K // 32), dtype=torch.uint8, device=dev) if pw.zp is not None else None
@@ -234,19 +289,46 @@ def unpack(pw: PackedWeight):
     return codes, scales, zp
 
 
-_ws_cache: dict = {}
+class WorkspaceCache:
+    """Zero-initialised workspaces, one per (device index, stream handle).
+
+    The library keeps per-call counters and the in-pass T epoch inside the workspace, so
+    calls that may overlap in time must not share one (include/mnb.h); calls on different
+    streams may overlap, calls on one stream do not.  Keying by stream gives each stream
+    its own buffer.  `alloc(nbytes)` returns a zero-filled uint8 tensor."""
+
+    def __init__(self, alloc):
+        self._alloc = alloc
+        self._bufs = {}
+
+    def get(self, dev_index: int, stream: int, nbytes: int):
+        key = (int(dev_index), int(stream))
+        ws = self._bufs.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = self._alloc(max(nbytes, 1))
+            self._bufs[key] = ws
+        return ws
+
+    def __len__(self):
+        return len(self._bufs)
 
 
-def workspace(dev, nbytes: int):
-    """A zero-initialised workspace of at least ``nbytes`` for ``dev``, reused across calls
-    made from this process on one stream at a time (the library keeps its counters zero)."""
+_ws_caches: dict = {}
+
+
+def workspace(dev, nbytes: int, stream=None):
+    """A zero-initialised workspace of at least ``nbytes`` for ``dev`` and ``stream`` (the
+    device's current stream by default), reused by later calls on that stream."""
     import torch
-    key = (dev.type, dev.index if dev.index is not None else torch.cuda.current_device())
-    ws = _ws_cache.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
-        _ws_cache[key] = ws
-    return ws
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(index)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    cache = _ws_caches.get(index)
+    if cache is None:
+        d = torch.device("cuda", index)
+        cache = _ws_caches[index] = WorkspaceCache(lambda n: torch.zeros(n, dtype=torch.uint8, device=d))
+    return cache.get(index, handle, nbytes)
 
 
 def workspace_error(ws) -> int:
@@ -259,16 +341,34 @@ def workspace_error(ws) -> int:
 def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
            flags: int = 0, out=None, ws=None, bias=None):
     """Y = X . deq(W)^T (+ (X.A).B) (+ bias) for a device fp16 X [M, K] and an optional fp16
-    bias [N]; returns fp16 Y [M, N]."""
+    bias [N]; returns fp16 Y [M, N].
+
+    Without ``ws`` the call uses the workspace cached for the current stream of X's device;
+    under graph capture a workspace must be passed (a cached one would be allocated and
+    zeroed inside the capture)."""
     import torch
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D [M, K]")
     M, K = X.shape
     if K != pw.K:
         raise ValueError("X has K=%d, weight has K=%d" % (K, pw.K))
     dev = X.device
+    _need(X, "X", torch.float16, (M, K), dev)
+    pw.check(dev)
+    if adapter is not None:
+        adapter.check(pw.N, K, dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float16, None, dev, pw.N)
+        if bias.numel() != pw.N:
+            raise ValueError("bias must hold N = %d values" % pw.N)
     Y = out if out is not None else torch.empty((M, pw.N), dtype=torch.float16, device=dev)
+    _need(Y, "out", torch.float16, (M, pw.N), dev)
     need = mnb_workspace_bytes(M, pw.N, K, pw.bits, 32 if adapter is not None else 0)
     if ws is None:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError("pass ws= under graph capture (a zeroed workspace owned by the caller)")
         ws = workspace(dev, need)
+    _need(ws, "workspace", torch.uint8, None, dev, need)
     ad = adapter.struct() if adapter is not None else None
     opt = mnb_options(path, flags)
     _check(mnb_matmul_bias(_ptr(X), _ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), ad, _ptr(bias), _ptr(Y), M,

@@ -283,19 +283,20 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
         for (int e = 0; e < 4; ++e) bo[nb][kk][e] = as_u32((crumb_pair(v, e) - zz2) * s2);
       } else if constexpr (BITS == 4) {
         // Nibbles 0 and 2 of each half sit in mantissa bits 0-3 (after a shift by 8 for
-        // 2): OR-ing 0x6400 gives 1024 + q.  Nibbles 1 and 3 are taken in place, at bits
-        // 4-7: 1024 + 16 q; minus (1024 + 16 z) that is 16 (q - z), exact, and the scale
-        // for them is s / 16 (exact unless s < 2^-10), so each product is (q - z) s
-        // rounded once either way.
-        const h2_t z162 = as_h2((z * 0x00100010u) | 0x64006400u);
+        // 2): OR-ing 0x6400 gives 1024 + q, and minus (1024 + z) that is q - z, exact.
+        // Nibbles 1 and 3 are taken in place, at bits 4-7: 1024 + 16 q.  One fused
+        // multiply-add takes it to (1024 + 16 q) / 16 - (64 + z) = q - z: every term is
+        // exact and so is the small integer result.  Both kinds are then multiplied by the
+        // same s, so each weight is (q - z) s rounded once, for every finite scale
+        // (subnormal ones included).
+        const h2_t nz64 = as_h2(((z << 4) * 0x00010001u) | 0xD400D400u);   // -(64 + z), both halves
         const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-        const h2_t s162 = s2 * sixteenth;
         const uint32_t w = rw.cw[nb][kk];
         const uint32_t w8 = w >> 8;
         bo[nb][kk][0] = as_u32((as_h2(bfi(0x000F000Fu, w, 0x64006400u)) - zz2) * s2);
-        bo[nb][kk][1] = as_u32((as_h2(bfi(0x00F000F0u, w, 0x64006400u)) - z162) * s162);
+        bo[nb][kk][1] = as_u32(__builtin_elementwise_fma(as_h2(bfi(0x00F000F0u, w, 0x64006400u)), sixteenth, nz64) * s2);
         bo[nb][kk][2] = as_u32((as_h2(bfi(0x000F000Fu, w8, 0x64006400u)) - zz2) * s2);
-        bo[nb][kk][3] = as_u32((as_h2(bfi(0x00F000F0u, w8, 0x64006400u)) - z162) * s162);
+        bo[nb][kk][3] = as_u32(__builtin_elementwise_fma(as_h2(bfi(0x00F000F0u, w8, 0x64006400u)), sixteenth, nz64) * s2);
       } else {
         const uint32_t w0 = rw.cw[nb][2 * kk], w1 = rw.cw[nb][2 * kk + 1];
         bo[nb][kk][0] = as_u32((byte_pair_lo(w0) - zz2) * s2);

@@ -1,9 +1,10 @@
 // gemv_acc4.hip -- MatMulNBits at accuracy level 4: the base product takes int8
 // block-quantized activations and integer dot products (v_dot4_i32_i8), the rank-32 LoRA
-// term keeps the original FP16 X (T from the T projection launch).
+// term keeps the unquantized FP16 X (T from the T projection launch).
 //
 // onnxruntime PR #33370 ("[WebGPU] Fuse rank-32 quantized LoRA with MatMulNBits"), commit
-// list: DP4A activation quantization for the base, original FP16 X for T; PR #33800
+// list: the base product may use int8-quantized activations, T is computed from the
+// unquantized FP16 X; PR #33800
 // ("Fuse DQ->MatMulNBits ...", Description): the lm_head runs at the default accuracy level
 // 4.  The pages give no quantization rule; the one used (per row, per block of 32 along
 // K): amax = max |x| in FP32, inv = 127 / amax, q = rint(x * inv) clamped to [-127, 127],
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void gemv_acc4_kernel(GemvParams p) {
     float lora = 0.f;
     if constexpr (LORA != LORA_NONE) {
       // T (FP32 partials per K-part of the projection launch, added in part order) from
-      // the original FP16 X; this lane's column of B
+      // the unquantized FP16 X; this lane's column of B
       const float *src = p.tin + (size_t)m * kRank + (lane & 31);
       float tv = 0.f;
       for (int pp = 0; pp < p.tparts; ++pp) tv += src[(size_t)pp * p.tmpad * kRank];

@@ -40,8 +40,8 @@ extern "C" {
 #endif
 
 /* Status codes.  Unsupported settings return errors rather than failing on the device, as
- * the PR #33370 empty-weight split ("malformed shapes") and the PagedAttention pages
- * (NOT_IMPLEMENTED statuses) do. */
+ * the PR #33370 page's empty-weight change does for malformed shapes and the PagedAttention
+ * pages do with their not-implemented statuses. */
 enum {
   MNB_OK = 0,
   MNB_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
@@ -56,8 +56,8 @@ enum {
 /* Adapter kinds (PR #33370: FP16 rank-32 adapters; block-32 INT8 adapters). */
 enum { MNB_ADAPTER_NONE = 0, MNB_ADAPTER_F16 = 1, MNB_ADAPTER_Q8 = 2 };
 
-/* Path override (PR #33370 keeps explicit fuse_down / fuse_up overrides "for
- * comparisons"; here the override names the kernel family). */
+/* Path override (PR #33370 keeps explicit fuse_down / fuse_up overrides so that the two
+ * can be compared; here the override names the kernel family). */
 enum { MNB_PATH_AUTO = 0, MNB_PATH_GEMV = 1, MNB_PATH_GEMM = 2 };
 
 /* Option flags. */
@@ -69,8 +69,8 @@ enum {
   /* Accuracy level 4: the base product takes int8 activations, quantized per row and per
    * block of 32 along K (amax = max |x|, q = rint(x * (127 / amax)) clamped to +-127,
    * scale amax / 127, FP32), with integer dot products; the LoRA term keeps the FP16 X
-   * (PR #33370 commit list: DP4A activation quantization for the base, original FP16 X
-   * for T; PR #33800 Description: the lm_head at the default accuracy level 4).  Runs the
+   * (PR #33370 commit list: int8-quantized activations for the base product while T uses
+   * the unquantized FP16 X; PR #33800 Description: the lm_head at the default accuracy level 4).  Runs the
    * GEMV family for every M (T from the projection launch when there is an adapter).
    * Requires K <= 16384 and a path of AUTO or GEMV (MNB_ERR_UNSUPPORTED otherwise). */
   MNB_FLAG_ACC4 = 2,
@@ -114,7 +114,9 @@ typedef struct mnb_options {
 /*
  * Sizes in bytes of the packed weight buffers for an N x K weight (host only, no device
  * call).  block must be 32; bits 2, 4 or 8; has_zp selects whether a zero-point buffer
- * exists.  Layout (this library's own): rows grouped by 64 (padded), K in blocks of 32:
+ * exists.  No page defines this call or the byte layout: the pages fix only the content (2-,
+ * 4- or 8-bit codes in blocks of 32 along K, an fp16 scale and an optional zero point per
+ * block).  Layout (this library's own): rows grouped by 64 (padded), K in blocks of 32:
  *   wq: ceil(N/64) * CC * 64 * 16 bytes, CC = 16-byte chunks per row = (K/32) * bits/4
  *       for 4 and 8 bits, ceil((K/32) / 2) for 2 bits (two blocks per chunk)
  *   sc: ceil(N/64) * (K/32) * 64 * 2 bytes
@@ -153,13 +155,15 @@ int mnb_pack(const uint8_t *codes, const void *scales, const uint8_t *zp, int N,
 int mnb_pack_kn(const uint8_t *codes_kn, const void *scales_kn, const uint8_t *zp_kn, int N,
                 int K, int bits, int block, void *wq, void *sc, void *zpp, void *stream);
 
-/* Inverse of mnb_pack (for round-trip checks).  zp may be NULL iff zpp is NULL. */
+/* Inverse of mnb_pack (for round-trip checks).  zp may be NULL iff zpp is NULL.  No page
+ * defines it: it inverts this library's own packed layout (see mnb_packed_sizes). */
 int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, int bits,
                int block, uint8_t *codes, void *scales, uint8_t *zp, void *stream);
 
 /*
  * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path and
- * any adapter kind (host only).  The workspace holds partial sums (among them the prefill
+ * any adapter kind (host only).  No page defines a workspace: it is this library's own
+ * scratch, passed in by the caller so that the library allocates nothing.  The workspace holds partial sums (among them the prefill
  * GEMM's FP32 partial outputs when it splits K over several workgroups per output tile),
  * the LoRA down-projection T and a few counters.  It must be ZERO-FILLED before its first use; every call that
  * completes leaves its counters at zero again, so one workspace can be reused by

@@ -163,9 +163,10 @@ static double lora_b(int kind, const void *B, const uint16_t *sB, int N, int r, 
 }
 
 /*
- * Accuracy level 4 (int8 activations for the base product; the PR #33370 page's commit
- * list keeps "DP4A activation quantization for the base, with original FP16 X for T", and
- * the PR #33800 page runs its lm_head at the default accuracy level 4).  The pages give no
+ * Accuracy level 4 (int8 activations for the base product; on the PR #33370 page's commit
+ * list the base product may take int8-quantized activations while T is still computed
+ * from the unquantized FP16 X, and the PR #33800 page runs its lm_head at the default
+ * accuracy level 4).  The pages give no
  * quantization rule; the reading taken here, per row and per block of 32 along K:
  *   amax = max |x|  (FP32; every binary16 is exact in it)
  *   amax == 0: every code 0;  else inv = 127 / amax, q = rint(x * inv) clamped to

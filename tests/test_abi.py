@@ -242,3 +242,58 @@ def test_gemv_grid_covers_the_chip():
             ng = (N + 63) // 64
             assert q in (1, 2, 4, 8) and (ng * q >= target or q == 8) and (q == 1 or ng * q // 2 < target)
             assert gt == ((K + 255) // 256 if kind else 0) and grid == ng * q + gt
+
+
+# ------------------------------------------------------------------------------------------
+# the torch binding's own checks (CPU tensors; every case fails before any library call)
+# ------------------------------------------------------------------------------------------
+
+def test_workspace_cache_is_per_device_and_stream():
+    """Calls that may overlap must not share a workspace: the binding's cache keeps one
+    buffer per (device, stream), reuses it on that stream and grows it on demand."""
+    import torch
+    made = []
+
+    def alloc(n):
+        made.append(n)
+        return torch.zeros(n, dtype=torch.uint8)
+
+    c = mnb.WorkspaceCache(alloc)
+    a = c.get(0, 0x1000, 256)
+    b = c.get(0, 0x2000, 256)
+    d = c.get(1, 0x1000, 256)
+    assert len({a.data_ptr(), b.data_ptr(), d.data_ptr()}) == 3 and len(c) == 3
+    assert c.get(0, 0x1000, 100) is a                  # same stream: reused
+    big = c.get(0, 0x1000, 4096)                       # grows, replaces that stream's buffer only
+    assert big.numel() == 4096 and c.get(0, 0x2000, 256) is b and len(c) == 3
+    assert made == [256, 256, 256, 4096]
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    K, N = 64, 96
+    pw = mnb.PackedWeight(torch.zeros(mnb.mnb_packed_sizes(N, K, 4, 32, 0)[1], dtype=torch.uint8),
+                          torch.zeros(mnb.mnb_packed_sizes(N, K, 4, 32, 0)[2] // 2, dtype=torch.float16),
+                          None, N, K, 4)
+    X = torch.zeros((4, K), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        mnb.matmul(X.float(), pw)                                         # X not fp16
+    with pytest.raises(ValueError):
+        mnb.matmul(torch.zeros((K, 4), dtype=torch.float16).t(), pw)      # X not contiguous
+    with pytest.raises(ValueError):
+        mnb.matmul(X, pw, out=torch.zeros((4, N - 1), dtype=torch.float16))   # out too small
+    with pytest.raises(ValueError):
+        mnb.matmul(X, pw, bias=torch.zeros(N + 1, dtype=torch.float16))   # bias not [N]
+    short = mnb.PackedWeight(pw.wq[:-16], pw.sc, None, N, K, 4)
+    with pytest.raises(ValueError):
+        mnb.matmul(X, short)                                              # packed codes too short
+    bad_a = mnb.Adapter(mnb.MNB_ADAPTER_F16, torch.zeros((K, 16), dtype=torch.float16),
+                        torch.zeros((32, N), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        mnb.matmul(X, pw, bad_a)                                          # A not [K, 32]
+    q8 = mnb.Adapter(mnb.MNB_ADAPTER_Q8, torch.zeros((K, 32), dtype=torch.int8),
+                     torch.zeros((32, N), dtype=torch.int8))
+    with pytest.raises(ValueError):
+        mnb.matmul(X, pw, q8)                                             # INT8 adapter without scales
+    with pytest.raises(TypeError):
+        mnb.pack(torch.zeros((N, K), dtype=torch.int32), torch.zeros((N, K // 32), dtype=torch.float16), None, 4)
