@@ -21,7 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmnb.so")
 
 MNB_OK, MNB_ERR_INVALID_ARG, MNB_ERR_UNSUPPORTED, MNB_ERR_MISALIGNED = 0, 1, 2, 3
-MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP, MNB_ERR_HANDOFF = 4, 5, 6, 7
+MNB_ERR_WORKSPACE, MNB_ERR_ALIAS, MNB_ERR_HIP, MNB_ERR_HANDOFF, MNB_ERR_TOO_LARGE = 4, 5, 6, 7, 8
+MNB_NOALLOC_SCRATCH_BYTES = 32 << 20
 MNB_ADAPTER_NONE, MNB_ADAPTER_F16, MNB_ADAPTER_Q8 = 0, 1, 2
 MNB_PATH_AUTO, MNB_PATH_GEMV, MNB_PATH_GEMM = 0, 1, 2
 MNB_FLAG_T_SEPARATE, MNB_FLAG_ACC4, MNB_FLAG_FAIL_HANDOFF = 1, 2, 4
@@ -74,12 +75,15 @@ def _load() -> C.CDLL:
                                   C.POINTER(mnb_options)]
     lib.mnb_matmul_bias.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, P, I, I, I, I, I, P, S, P,
                                     C.POINTER(mnb_options)]
+    lib.mnb_matmul_noalloc.argtypes = [P, P, P, P, C.POINTER(mnb_adapter), P, P, I, I, I, I, I, P,
+                                       C.POINTER(mnb_options)]
     lib.mnb_describe_route.argtypes = [I, I, I, I, I, I, C.POINTER(mnb_options), C.c_char_p, S]
     lib.mnb_status_string.argtypes = [I]
     lib.mnb_status_string.restype = C.c_char_p
     lib.mnb_version.argtypes = []
     for f in ("mnb_packed_sizes", "mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex",
-              "mnb_matmul_bias", "mnb_describe_route", "mnb_version", "mnb_workspace_error"):
+              "mnb_matmul_bias", "mnb_matmul_noalloc", "mnb_describe_route", "mnb_version",
+              "mnb_workspace_error"):
         getattr(lib, f).restype = I
     return lib
 
@@ -140,6 +144,11 @@ def mnb_matmul_bias(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, workspace
     return lib.mnb_matmul_bias(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, bias, Y, M, N, K,
                                bits, block, workspace, ws_bytes, stream,
                                C.byref(opt) if opt is not None else None)
+
+
+def mnb_matmul_noalloc(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, stream, opt) -> int:
+    return lib.mnb_matmul_noalloc(X, wq, sc, zpp, C.byref(ad) if ad is not None else None, bias, Y, M, N, K,
+                                  bits, block, stream, C.byref(opt) if opt is not None else None)
 
 
 def mnb_describe_route(M, N, K, bits, has_zp, adapter_kind, opt=None):
@@ -338,14 +347,7 @@ def workspace_error(ws) -> int:
     return mnb_workspace_error(_ptr(ws), _stream(ws.device))
 
 
-def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
-           flags: int = 0, out=None, ws=None, bias=None):
-    """Y = X . deq(W)^T (+ (X.A).B) (+ bias) for a device fp16 X [M, K] and an optional fp16
-    bias [N]; returns fp16 Y [M, N].
-
-    Without ``ws`` the call uses the workspace cached for the current stream of X's device;
-    under graph capture a workspace must be passed (a cached one would be allocated and
-    zeroed inside the capture)."""
+def _matmul_args(X, pw, adapter, out, bias):
     import torch
     if X.dim() != 2:
         raise ValueError("X must be 2-D [M, K]")
@@ -363,6 +365,31 @@ def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_
             raise ValueError("bias must hold N = %d values" % pw.N)
     Y = out if out is not None else torch.empty((M, pw.N), dtype=torch.float16, device=dev)
     _need(Y, "out", torch.float16, (M, pw.N), dev)
+    return M, K, dev, Y
+
+
+def matmul_noalloc(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
+                   flags: int = 0, out=None, bias=None):
+    """matmul through mnb_matmul_noalloc: the library's static per-device scratch instead of
+    a workspace (no device allocation in the call when ``out`` is given).  Calls that
+    overlap in time on one device must not be made."""
+    M, K, dev, Y = _matmul_args(X, pw, adapter, out, bias)
+    ad = adapter.struct() if adapter is not None else None
+    _check(mnb_matmul_noalloc(_ptr(X), _ptr(pw.wq), _ptr(pw.sc), _ptr(pw.zp), ad, _ptr(bias), _ptr(Y), M,
+                              pw.N, K, pw.bits, 32, _stream(dev), mnb_options(path, flags)))
+    return Y
+
+
+def matmul(X, pw: PackedWeight, adapter: Adapter | None = None, path: int = MNB_PATH_AUTO,
+           flags: int = 0, out=None, ws=None, bias=None):
+    """Y = X . deq(W)^T (+ (X.A).B) (+ bias) for a device fp16 X [M, K] and an optional fp16
+    bias [N]; returns fp16 Y [M, N].
+
+    Without ``ws`` the call uses the workspace cached for the current stream of X's device;
+    under graph capture a workspace must be passed (a cached one would be allocated and
+    zeroed inside the capture)."""
+    import torch
+    M, K, dev, Y = _matmul_args(X, pw, adapter, out, bias)
     need = mnb_workspace_bytes(M, pw.N, K, pw.bits, 32 if adapter is not None else 0)
     if ws is None:
         if torch.cuda.is_current_stream_capturing():

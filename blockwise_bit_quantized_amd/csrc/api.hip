@@ -10,13 +10,58 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 #include "mnb.h"
 
 using namespace mnb;
 
+// Scratch of mnb_matmul_noalloc: a workspace inside the library, for callers that cannot
+// allocate.  Each device that loads the library holds its own copy until the process ends.
+// Host code never uses this name as an address: the per-device address comes from
+// hipGetSymbolAddress (scratch_for).
+static __device__ __align__(256) unsigned char scratch[MNB_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Zero the control area's counters (every word but the call epoch, which must only grow:
+// the in-pass T words left by earlier calls carry earlier tags) -- a kernel, not a memset,
+// so that a graph capturing the first call replays correctly.
+__global__ void scratch_init_kernel(int *ctrl) {
+  const int n = (int)(kCtrlBytes / sizeof(int));
+  for (int i = 1 + (int)(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += (int)(gridDim.x * blockDim.x))
+    ctrl[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // device address of `scratch` per device (guarded by g_scratch_mu)
+
+// The scratch address for the device of `s`: looked up once per device, with that device
+// current, and its counters zeroed by a kernel on `s` before the first call uses it.
+int scratch_for(hipStream_t s, void **out) {
+  int dev = 0;
+  if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return MNB_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MNB_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return MNB_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MNB_ERR_HIP;
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p) {
+      hipLaunchKernelGGL(scratch_init_kernel, dim3(8), dim3(256), 0, s, static_cast<int *>(p));
+      e = hipGetLastError();
+    }
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return MNB_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MNB_OK;
+}
 
 enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
 
@@ -121,9 +166,10 @@ int check_common(int M, int N, int K, int bits, int block) {
   return MNB_OK;
 }
 
+// check_ws false: every check but the workspace's (mnb_matmul_noalloc checks its own)
 int validate(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad,
              const void *bias, const void *Y, int M, int N, int K, int bits, int block, const void *ws,
-             size_t ws_bytes, const mnb_options *opt) {
+             size_t ws_bytes, const mnb_options *opt, bool check_ws = true) {
   int st = check_common(M, N, K, bits, block);
   if (st) return st;
   if (opt) {
@@ -145,7 +191,7 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
     return MNB_ERR_MISALIGNED;
   if (lora && (misaligned(ad->A) || misaligned(ad->B) || misaligned(ad->A_scales) || misaligned(ad->B_scales)))
     return MNB_ERR_MISALIGNED;
-  if (K > 0) {
+  if (K > 0 && check_ws) {
     const size_t need = mnb_workspace_bytes(M, N, K, bits, lora ? kRank : 0);
     if (need > 0 && (!ws || ws_bytes < need)) return MNB_ERR_WORKSPACE;
   }
@@ -227,7 +273,7 @@ bool log_enabled() {
 
 extern "C" {
 
-int mnb_version(void) { return 103; }
+int mnb_version(void) { return 104; }
 
 const char *mnb_status_string(int status) {
   switch (status) {
@@ -239,6 +285,9 @@ const char *mnb_status_string(int status) {
     case MNB_ERR_ALIAS: return "MNB_ERR_ALIAS: output overlaps an input or the workspace";
     case MNB_ERR_HIP: return "MNB_ERR_HIP: HIP runtime error";
     case MNB_ERR_HANDOFF: return "MNB_ERR_HANDOFF: an in-pass T handoff gave up, its outputs are NaN";
+    case MNB_ERR_TOO_LARGE:
+      return "MNB_ERR_TOO_LARGE: the call needs more workspace than mnb_matmul_noalloc's static scratch "
+             "(MNB_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown mnb status";
   }
 }
@@ -474,6 +523,22 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
 int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad, void *Y, int M,
                int N, int K, int bits, int block, void *workspace, size_t ws_bytes, void *stream) {
   return mnb_matmul_ex(X, wq, sc, zpp, ad, Y, M, N, K, bits, block, workspace, ws_bytes, stream, nullptr);
+}
+
+int mnb_matmul_noalloc(const void *X, const void *wq, const void *sc, const void *zpp, const mnb_adapter *ad,
+                       const void *bias, void *Y, int M, int N, int K, int bits, int block, void *stream,
+                       const mnb_options *opt) {
+  // everything the workspace does not decide, first (no device call on an invalid call)
+  int st = validate(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, nullptr, 0, opt, false);
+  if (st) return st;
+  if (M == 0 || N == 0) return MNB_OK;
+  const size_t need = mnb_workspace_bytes(M, N, K, bits, effective_lora(ad) ? kRank : 0);
+  if (need > MNB_NOALLOC_SCRATCH_BYTES) return MNB_ERR_TOO_LARGE;
+  void *ws = nullptr;
+  st = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (st) return st;
+  return mnb_matmul_bias(X, wq, sc, zpp, ad, bias, Y, M, N, K, bits, block, ws, MNB_NOALLOC_SCRATCH_BYTES, stream,
+                         opt);
 }
 
 }  // extern "C"

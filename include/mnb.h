@@ -50,7 +50,8 @@ enum {
   MNB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than mnb_workspace_bytes() */
   MNB_ERR_ALIAS = 5,        /* Y overlaps an input or the workspace */
   MNB_ERR_HIP = 6,          /* a HIP runtime call failed (no device, launch failure) */
-  MNB_ERR_HANDOFF = 7       /* mnb_workspace_error: an in-pass T handoff gave up (outputs NaN) */
+  MNB_ERR_HANDOFF = 7,      /* mnb_workspace_error: an in-pass T handoff gave up (outputs NaN) */
+  MNB_ERR_TOO_LARGE = 8     /* mnb_matmul_noalloc: workspace need exceeds MNB_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Adapter kinds (PR #33370: FP16 rank-32 adapters; block-32 INT8 adapters). */
@@ -229,11 +230,34 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
 int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapter_kind,
                        const mnb_options *opt, char *buf, size_t buf_len);
 
+/*
+ * mnb_matmul_bias without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The call allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine); its workspace is a static device array of MNB_NOALLOC_SCRATCH_BYTES inside the
+ * library, one copy per device, held from the library's load until the process ends.
+ *   - Arguments and results as mnb_matmul_bias (opt may be NULL).
+ *   - A call whose workspace (mnb_workspace_bytes) would exceed the array returns
+ *     MNB_ERR_TOO_LARGE and enqueues nothing; use mnb_matmul_bias with a caller workspace.
+ *   - The first call on a device looks the array up and zeroes its counters with a kernel
+ *     on `stream` (no memset), ahead of its own kernels.
+ *   - Every call on a device shares that device's array, which keeps the last call's
+ *     contents: calls on one device that overlap in time (several streams, threads or
+ *     concurrently replayed graphs) race and give wrong results; consecutive calls on one
+ *     stream are fine.
+ *   - The in-pass T handoff's error word lives in the array and is not reported; a handoff
+ *     that gives up still writes NaN outputs.
+ */
+#define MNB_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int mnb_matmul_noalloc(const void *X, const void *wq, const void *sc, const void *zpp,
+                       const mnb_adapter *ad, const void *bias, void *Y, int M, int N, int K,
+                       int bits, int block, void *stream, const mnb_options *opt);
+
 /* Static text for a status code. */
 const char *mnb_status_string(int status);
 
 /* ABI version (major * 100 + minor): 101 adds mnb_matmul_bias, 102 mnb_pack_kn, 103
- * mnb_workspace_error and MNB_FLAG_FAIL_HANDOFF. */
+ * mnb_workspace_error and MNB_FLAG_FAIL_HANDOFF, 104 mnb_matmul_noalloc. */
 int mnb_version(void);
 
 #ifdef __cplusplus

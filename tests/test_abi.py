@@ -30,7 +30,7 @@ def test_header_declares_the_abi():
     names = header_functions()
     for n in ("mnb_pack", "mnb_pack_kn", "mnb_unpack", "mnb_matmul", "mnb_matmul_ex", "mnb_matmul_bias",
               "mnb_workspace_bytes", "mnb_packed_sizes", "mnb_status_string", "mnb_describe_route",
-              "mnb_version", "mnb_workspace_error"):
+              "mnb_version", "mnb_workspace_error", "mnb_matmul_noalloc"):
         assert n in names
 
 
@@ -41,8 +41,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert mnb.mnb_version() == 103
-    for st in range(8):
+    assert mnb.mnb_version() == 104
+    for st in range(9):
         assert mnb.mnb_status_string(st).startswith("MNB_")
     assert "unknown" in mnb.mnb_status_string(99)
 
@@ -297,3 +297,20 @@ def test_binding_rejects_bad_tensors_before_the_library():
         mnb.matmul(X, pw, q8)                                             # INT8 adapter without scales
     with pytest.raises(TypeError):
         mnb.pack(torch.zeros((N, K), dtype=torch.int32), torch.zeros((N, K // 32), dtype=torch.float16), None, 4)
+
+
+def test_noalloc_validation_before_any_device_call():
+    """mnb_matmul_noalloc validates like mnb_matmul_bias (no workspace argument) and refuses
+    a call whose workspace would exceed its static scratch, before touching the device."""
+    def na(M=1, N=64, K=64, bits=4, x=X, y=Y, ad=None, opt=None):
+        return mnb.mnb_matmul_noalloc(x, WQ, SC, ZP, ad, None, y, M, N, K, bits, 32, None, opt)
+    assert na(bits=3) == mnb.MNB_ERR_UNSUPPORTED
+    assert na(M=-1) == mnb.MNB_ERR_INVALID_ARG
+    assert na(x=None) == mnb.MNB_ERR_INVALID_ARG
+    assert na(y=Y + 8) == mnb.MNB_ERR_MISALIGNED
+    assert na(y=X) == mnb.MNB_ERR_ALIAS
+    assert na(M=0, x=None, y=None) == mnb.MNB_OK
+    big = (256, 12288, 16384)                     # K split into FP32 partials: 48 MiB of workspace
+    assert mnb.mnb_workspace_bytes(*big, 4, 0) > mnb.MNB_NOALLOC_SCRATCH_BYTES
+    assert na(*big) == mnb.MNB_ERR_TOO_LARGE
+    assert "MNB_ERR_TOO_LARGE" in mnb.mnb_status_string(mnb.MNB_ERR_TOO_LARGE)
