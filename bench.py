@@ -6,14 +6,22 @@ A step is one pass of the whole path over one batch of synthetic input:
     default zero point and a rank-32 F16 LoRA fused in the same launch (in-pass T);
   * prefill: Y[1024, 4096] = X[1024, 4096] . deq(W)^T + (X.A).B, INT4 block-32 with explicit
     zero points, rank-32 F16 LoRA (T projection launch + MFMA GEMM with the T.B epilogue).
-Inputs are resident in HBM before timing.  Decode rotates over enough copies of its
-weights and adapter (default >= 1 GiB, four times the 256 MB Infinity Cache) that every
-call streams from HBM; the prefill GEMM is MFMA-bound and uses one copy.
+Inputs are resident in HBM before timing.  Decode-shaped (HBM-bound) runs rotate over
+enough copies of their weights, activations and adapter (default >= 1 GiB, four times the
+256 MB Infinity Cache) that every call streams from HBM; prefill-shaped (MFMA-bound) runs
+use one copy.
 
-The timed region replays two captured HIP graphs on one stream: K decode calls, then K
-prefill calls; HIP events bracket each graph.  `value` is the decode GEMV's effective HBM
-bandwidth (algorithmic bytes / mean decode call time, GB/s); the prefill TFLOP/s rides
-along in `prefill`.
+Timing: every figure comes from replays of captured HIP graphs of calls, events bracketing
+each replay on the stream the kernels run on.  Each graph (or, for cold runs, each of the
+graphs that together cover every copy once) is replayed four times untimed -- the first
+replays of a new graph run up to 20% slower -- and then five times timed; the figure is the
+median of the five.  The headline graphs hold exactly --steps calls each.
+
+`value` is the decode GEMV's effective HBM bandwidth (algorithmic bytes / decode call time,
+GB/s); the prefill TFLOP/s rides along in `prefill`; `runs` holds every decode and prefill
+workload (µs, rate, fraction of the roofline, route) and `ceilings` what the same GPU does
+on plain work of the same size: a streaming read of the decode byte counts (cold) and the
+dense FP16 GEMM of the prefill shape.
 """
 from __future__ import annotations
 
@@ -50,11 +58,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cold-mib", type=int, default=1024, help="bytes of rotated decode copies")
+    ap.add_argument("--cold-mib", type=int, default=1024, help="bytes of rotated copies for HBM-bound runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle decode baseline")
     ap.add_argument("--no-context", action="store_true",
-                    help="skip the warm / two-launch / empty-adapter context runs (counter collection)")
+                    help="only the two headline graphs (counter collection and kernel traces)")
+    ap.add_argument("--only", choices=["decode", "prefill"],
+                    help="with --no-context: only that headline graph (a cold-only decode trace)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 10 device-to-device copies of MIB MiB (calibrates FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--summarize", metavar="DIR",
@@ -85,7 +95,60 @@ def summarize(root):
                 val = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-3
             rows.setdefault(key, []).append(val)
     for (name, grid, what), v in sorted(rows.items()):
-        print("%-60s grid=%-12s %-14s n=%-5d mean=%.6g" % (name[:60], grid, what, len(v), sum(v) / len(v)))
+        v = sorted(v)
+        print("%-60s grid=%-12s %-26s n=%-5d mean=%.6g median=%.6g" % (name[:60], grid, what, len(v),
+                                                                      sum(v) / len(v), v[len(v) // 2]))
+
+
+class Timer:
+    """Median-of-five timing of captured graphs on one stream (four untimed replays first)."""
+
+    def __init__(self, torch, stream):
+        self.torch = torch
+        self.stream = stream
+
+    def capture(self, fn, calls):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g, stream=self.stream):
+            for j in calls:
+                fn(j)
+        return g
+
+    def time_graphs(self, graphs, n_calls):
+        """Seconds per call: graphs are replayed round-robin (4 untimed, 5 timed); each timed
+        replay holds n_calls calls; returns the median replay / n_calls."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        i = 0
+        for _ in range(4):
+            graphs[i % len(graphs)].replay()
+            i += 1
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(self.stream):
+                a.record()
+                graphs[i % len(graphs)].replay()
+                b.record()
+            i += 1
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3 / n_calls)
+        return sorted(times)[2]
+
+    def per_call(self, fn, n_items, n_calls):
+        """Seconds per call of fn(j), n_calls calls per graph.  fn rotates over n_items items
+        (cold copies) by j; with more items than calls per graph, consecutive graphs take
+        consecutive items, so that a replay finds its items cold."""
+        fn(0)                              # eager first: libraries initialise outside capture
+        self.torch.cuda.synchronize()
+        if n_items <= n_calls:
+            graphs = [self.capture(fn, range(n_calls))]
+        else:
+            graphs = [self.capture(fn, range(s, s + n_calls)) for s in range(0, n_items - n_calls + 1, n_calls)]
+        t = self.time_graphs(graphs, n_calls)
+        del graphs
+        return t
 
 
 def main():
@@ -134,153 +197,168 @@ def main():
         zp = torch.from_numpy(case["zp"]).to(dev) if case["zp"] is not None else None
         return mnb.pack(torch.from_numpy(case["codes"]).to(dev), t16(case["scales"]), zp, case["bits"])
 
-    # ---- decode workload, rotated copies ----
+    def adapter(case):
+        a = case.get("adapter")
+        if a is None:
+            return None
+        if a["kind"] == "f16":
+            return mnb.Adapter(mnb.MNB_ADAPTER_F16, t16(a["A"]), t16(a["B"]))
+        return mnb.Adapter(mnb.MNB_ADAPTER_Q8, torch.from_numpy(a["A"]).to(dev), torch.from_numpy(a["B"]).to(dev),
+                           t16(a["A_scales"]), t16(a["B_scales"]))
+
+    def clone_weight(pw):
+        return mnb.PackedWeight(pw.wq.clone(), pw.sc.clone(), None if pw.zp is None else pw.zp.clone(),
+                                pw.N, pw.K, pw.bits)
+
+    def clone_adapter(a):
+        if a is None:
+            return None
+        c = lambda t: None if t is None else t.clone()
+        return mnb.Adapter(a.kind, c(a.A), c(a.B), c(a.A_scales), c(a.B_scales))
+
+    def route(case, ad_kind, flags=0):
+        opt = mnb.mnb_options(0, flags) if flags else None
+        return mnb.mnb_describe_route(case["M"], case["N"], case["K"], case["bits"], case["zp"] is not None,
+                                      ad_kind, opt)[1]
+
+    def cold_copies(case, nbytes):
+        """(X, weight, adapter) copies whose total bytes reach --cold-mib, so that a call
+        finds none of its inputs in the 256 MB Infinity Cache."""
+        r = max(1, math.ceil(args.cold_mib * 2**20 / nbytes))
+        pw, ad, X = weight(case), adapter(case), t16(case["X"])
+        return [(X.clone(), clone_weight(pw), clone_adapter(ad)) for _ in range(r)]
+
+    timer = Timer(torch, torch.cuda.Stream())
+    K = args.steps
+
+    # ---- headline: cold decode (cfg2 + F16 LoRA) and prefill (cfg3, M = 1024) ----
     dec = si.make_config(2)
     dM, dN, dK = dec["M"], dec["N"], dec["K"]
     dbytes = algorithmic_bytes(dM, dN, dK, 4, False, 32)
-    copies = max(1, math.ceil(args.cold_mib * 2**20 / dbytes))
-    pw0 = weight(dec)
-    X0, A0, B0 = t16(dec["X"]), t16(dec["adapter"]["A"]), t16(dec["adapter"]["B"])
-    dcopies = []
-    for _ in range(copies):
-        pw = mnb.PackedWeight(pw0.wq.clone(), pw0.sc.clone(), None, dN, dK, 4)
-        dcopies.append((X0.clone(), pw, mnb.Adapter(mnb.MNB_ADAPTER_F16, A0.clone(), B0.clone())))
+    dcopies = cold_copies(dec, dbytes)
     Yd = torch.empty((dM, dN), dtype=torch.float16, device=dev)
 
-    # ---- prefill workload ----
     pre = si.make_config(3)
     pM, pN, pK = pre["M"], pre["N"], pre["K"]
     pflops = algorithmic_flops(pM, pN, pK, 32)
     pbytes = algorithmic_bytes(pM, pN, pK, 4, True, 32)
-    ppw = weight(pre)
-    pX = t16(pre["X"])
-    pad = mnb.Adapter(mnb.MNB_ADAPTER_F16, t16(pre["adapter"]["A"]), t16(pre["adapter"]["B"]))
+    ppw, pX, pad = weight(pre), t16(pre["X"]), adapter(pre)
     Yp = torch.empty((pM, pN), dtype=torch.float16, device=dev)
 
-    ws = mnb.workspace(dev, max(mnb.mnb_workspace_bytes(dM, dN, dK, 4, 32),
-                                mnb.mnb_workspace_bytes(pM, pN, pK, 4, 32)))
+    ws = torch.zeros(max(mnb.mnb_workspace_bytes(dM, dN, dK, 4, 32), mnb.mnb_workspace_bytes(pM, pN, pK, 4, 32),
+                         mnb.mnb_workspace_bytes(256, pN, pK, 4, 32), 1 << 20), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def decode(i):
-        X, pw, ad = dcopies[i % copies]
+    def decode(j):
+        X, pw, ad = dcopies[j % len(dcopies)]
         mnb.matmul(X, pw, ad, out=Yd, ws=ws)
 
-    def prefill():
+    def prefill(j):
         mnb.matmul(pX, ppw, pad, out=Yp, ws=ws)
 
     for i in range(args.warmup):
         decode(i)
-        prefill()
+        prefill(i)
     torch.cuda.synchronize()
-
-    # The timed region replays two captured graphs: K decode calls (rotating over the cold
-    # copies) and then K prefill calls.  Graph replay keeps Python launch overhead out of
-    # the measurement; events bracket each graph on the stream the kernels run on.
-    K = args.steps
-    cap = torch.cuda.Stream()
-    g_dec, g_pre = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_dec, stream=cap):
-        for i in range(K):
-            decode(i)
-    with torch.cuda.graph(g_pre, stream=cap):
-        for i in range(K):
-            prefill()
-    torch.cuda.synchronize()
-    g_dec.replay()                          # first replay (untimed): graph upload
-    g_pre.replay()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     wall0 = time.perf_counter()
-    with torch.cuda.stream(cap):
-        ev[0].record()
-        g_dec.replay()
-        ev[1].record()
-        g_pre.replay()
-        ev[2].record()
-    torch.cuda.synchronize()
+    dec_s = pre_s = 0.0
+    if args.only != "prefill":
+        dec_s = timer.per_call(decode, len(dcopies), K)
+    if args.only != "decode":
+        pre_s = timer.per_call(prefill, 1, K)
     wall = time.perf_counter() - wall0
-    dec_s = ev[0].elapsed_time(ev[1]) * 1e-3 / K
-    pre_s = ev[1].elapsed_time(ev[2]) * 1e-3 / K
-    total_ms = ev[0].elapsed_time(ev[2])
-    dec_gbps = dbytes / dec_s / 1e9
-    pre_tflops = pflops / pre_s / 1e12
+    dec_gbps = dbytes / dec_s / 1e9 if dec_s else 0.0
+    pre_tflops = pflops / pre_s / 1e12 if pre_s else 0.0
+    dec_route = route(dec, mnb.MNB_ADAPTER_F16)
+    pre_route = route(pre, mnb.MNB_ADAPTER_F16)
 
-    # context: warm (Infinity-Cache resident) decode, the two-launch decode variant and the
-    # empty-adapter decode, each as a replayed graph of K calls
-    def graph_time(fn, n):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            for j in range(n):
-                fn(j)
-        # untimed replays first: the first few replays of a new graph run up to 20% slower
-        # (measured on the batched prefill: 110, 101, 100, 97, 94 us, then ~88.5 us); the
-        # figure is the median of five timed replays
-        for _ in range(4):
-            g.replay()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(5):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(cap):
-                a.record()
-                g.replay()
-                b.record()
-            torch.cuda.synchronize()
-            times.append(a.elapsed_time(b) * 1e-3 / n)
-        return sorted(times)[2]
-
-    dbytes_base = algorithmic_bytes(dM, dN, dK, 4, False, 0)
-    context = None
+    runs = ceilings = context = None
     if not args.no_context:
-        n_ctx = min(K, 100)
-        warm_s = graph_time(lambda j: mnb.matmul(*dcopies[0], out=Yd, ws=ws), n_ctx)
-        tsep_s = graph_time(lambda j: mnb.matmul(*dcopies[j % copies], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd,
-                                                 ws=ws), n_ctx)
-        base_s = graph_time(lambda j: mnb.matmul(dcopies[j % copies][0], dcopies[j % copies][1], None, out=Yd,
-                                                 ws=ws), n_ctx)
-        context = {"warm_us": round(warm_s * 1e6, 3), "warm_GBps": round(dbytes / warm_s / 1e9, 1),
-                   "t_separate_us": round(tsep_s * 1e6, 3),
-                   "empty_adapter_us": round(base_s * 1e6, 3),
-                   "empty_adapter_GBps": round(dbytes_base / base_s / 1e9, 1)}
-        # the same decode shape with 2-bit codes (default zero point 2) and the F16 adapter,
-        # cold copies of the weights
+        runs, ceilings, context = {}, {}, {}
+
+        def hbm_run(name, case, ad_kind, nbytes, flags=0, with_adapter=True):
+            copies = cold_copies(case, nbytes)
+            Y = torch.empty((case["M"], case["N"]), dtype=torch.float16, device=dev)
+            w = torch.zeros(max(mnb.mnb_workspace_bytes(case["M"], case["N"], case["K"], case["bits"], 32), 1),
+                            dtype=torch.uint8, device=dev)
+
+            def call(j):
+                X, pw, ad = copies[j % len(copies)]
+                mnb.matmul(X, pw, ad if with_adapter else None, flags=flags, out=Y, ws=w)
+            s = timer.per_call(call, len(copies), min(K, 100))
+            runs[name] = {"us": round(s * 1e6, 3), "GBps": round(nbytes / s / 1e9, 1),
+                          "frac": round(nbytes / s / 1e9 / HBM_PEAK_GBPS, 4), "bytes": nbytes, "cold": True,
+                          "copies": len(copies), "route": route(case, ad_kind if with_adapter else 0, flags)}
+            del copies
+            return s
+
+        def mfma_run(name, case, ad_kind, n_calls=20):
+            pw, ad, X = weight(case), adapter(case), t16(case["X"])
+            M, N, Kc = case["M"], case["N"], case["K"]
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            w = torch.zeros(max(mnb.mnb_workspace_bytes(M, N, Kc, case["bits"], 32), 1), dtype=torch.uint8,
+                            device=dev)
+            s = timer.per_call(lambda j: mnb.matmul(X, pw, ad, out=Y, ws=w), 1, n_calls)
+            fl = algorithmic_flops(M, N, Kc, 32 if ad is not None else 0)
+            runs[name] = {"us": round(s * 1e6, 3), "TFLOPs": round(fl / s / 1e12, 2),
+                          "frac": round(fl / s / 1e12 / FP16_PEAK_TFLOPS, 4), "flops": fl, "cold": False,
+                          "route": route(case, ad_kind)}
+            return s
+
+        # every decode and prefill run of the workloads
+        c1 = si.make_config(1)
+        hbm_run("cfg1_m1", c1, mnb.MNB_ADAPTER_F16, algorithmic_bytes(1, 896, 896, 4, True, 32))
+        runs["cfg2_m1_lora"] = {"us": round(dec_s * 1e6, 3), "GBps": round(dec_gbps, 1),
+                                "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "bytes": dbytes, "cold": True,
+                                "copies": len(dcopies), "route": dec_route, "note": "headline"}
+        hbm_run("cfg2_m1_empty", dec, 0, algorithmic_bytes(1, dN, dK, 4, False, 0), with_adapter=False)
+        runs["cfg3_m1024"] = {"us": round(pre_s * 1e6, 3), "TFLOPs": round(pre_tflops, 2),
+                              "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4), "flops": pflops, "cold": False,
+                              "route": pre_route, "note": "headline"}
+        mfma_run("cfg3_m256", si.make_config(3, M=256), mnb.MNB_ADAPTER_F16)
+        mfma_run("cfg3_m1024_empty", si.make_config(3, adapter=False), 0)
+        hbm_run("cfg3_m1", si.make_config(3, M=1), mnb.MNB_ADAPTER_F16, algorithmic_bytes(1, pN, pK, 4, True, 32))
+        hbm_run("cfg4_m1", si.make_config(4, M=1), 0, algorithmic_bytes(1, 49152, 576, 8, True, 0))
+        hbm_run("cfg4_m8", si.make_config(4, M=8), 0, algorithmic_bytes(8, 49152, 576, 8, True, 0))
+        c5 = si.make_config(5)
+        mfma_run("cfg5_m1024", c5, mnb.MNB_ADAPTER_Q8)
+        mfma_run("cfg5_m1024_empty", si.make_config(5, adapter=False), 0)
+
+        # ceilings: a plain streaming read of the decode byte counts (cold), and the dense
+        # FP16 GEMM at the prefill shape (hipBLASLt through torch)
+        ceilings.update(stream_read_ceilings(torch, dev, timer, args.cold_mib, min(K, 100),
+                                             {"cfg2_m1_lora": dbytes,
+                                              "cfg4_m1": algorithmic_bytes(1, 49152, 576, 8, True, 0)}))
+        Wd = torch.randn((pN, pK), dtype=torch.float16, device=dev) * 0.02
+        Xd = torch.randn((pM, pK), dtype=torch.float16, device=dev)
+        Yg = torch.empty((pM, pN), dtype=torch.float16, device=dev)
+        sg = timer.per_call(lambda j: torch.matmul(Xd, Wd.t(), out=Yg), 1, 20)
+        ceilings["dense_fp16_gemm_1024x4096x4096"] = {
+            "us": round(sg * 1e6, 3), "TFLOPs": round(2 * pM * pN * pK / sg / 1e12, 2),
+            "frac": round(2 * pM * pN * pK / sg / 1e12 / FP16_PEAK_TFLOPS, 4),
+            "what": "torch.matmul of fp16 X[1024,4096] by W^T (dense fp16 weights, rocBLAS/hipBLASLt), no LoRA"}
+        del Wd, Xd, Yg
+
+        # context: warm decode, the two-launch decode, and 2-bit codes
+        warm = dcopies[0]
+        s = timer.per_call(lambda j: mnb.matmul(*warm, out=Yd, ws=ws), 1, min(K, 100))
+        context["cfg2_warm_us"] = round(s * 1e6, 3)
+        context["cfg2_warm_GBps"] = round(dbytes / s / 1e9, 1)
+        s = timer.per_call(lambda j: mnb.matmul(*dcopies[j % len(dcopies)], flags=mnb.MNB_FLAG_T_SEPARATE, out=Yd,
+                                                ws=ws), len(dcopies), min(K, 100))
+        context["cfg2_t_separate_us"] = round(s * 1e6, 3)
         dec2 = si.make_random(2002, dM, dN, dK, 2, False, None)
         pw2 = weight(dec2)
         dbytes2 = algorithmic_bytes(dM, dN, dK, 2, False, 32)
-        copies2 = max(1, math.ceil(args.cold_mib * 2**20 / dbytes2))
-        w2 = [mnb.PackedWeight(pw2.wq.clone(), pw2.sc.clone(), None, dN, dK, 2) for _ in range(copies2)]
-        two_s = graph_time(lambda j: mnb.matmul(X0, w2[j % copies2], dcopies[0][2], out=Yd, ws=ws), n_ctx)
-        context["decode_2bit_us"] = round(two_s * 1e6, 3)
-        context["decode_2bit_GBps"] = round(dbytes2 / two_s / 1e9, 1)
+        r2 = max(1, math.ceil(args.cold_mib * 2**20 / dbytes2))
+        w2 = [clone_weight(pw2) for _ in range(r2)]
+        s = timer.per_call(lambda j: mnb.matmul(dcopies[0][0], w2[j % r2], dcopies[0][2], out=Yd, ws=ws), r2,
+                           min(K, 100))
+        context["cfg2_2bit_us"] = round(s * 1e6, 3)
+        context["cfg2_2bit_GBps"] = round(dbytes2 / s / 1e9, 1)
         del w2
-    # context: the other prefill workloads (warm weights), each a replayed graph of calls
-    pre_context = None
-    if not args.no_context:
-        pre_context = {}
-        c256 = si.make_config(3, M=256)
-        X256, Y256 = t16(c256["X"]), torch.empty((256, pN), dtype=torch.float16, device=dev)
-        ws256 = torch.zeros(mnb.mnb_workspace_bytes(256, pN, pK, 4, 32), dtype=torch.uint8, device=dev)
-        s256 = graph_time(lambda j: mnb.matmul(X256, ppw, pad, out=Y256, ws=ws256), 20)
-        f256 = algorithmic_flops(256, pN, pK, 32)
-        pre_context["m256_us"] = round(s256 * 1e6, 3)
-        pre_context["m256_TFLOPs"] = round(f256 / s256 / 1e12, 2)
-        pre_context["m256_route"] = mnb.mnb_describe_route(256, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
-        c5 = si.make_config(5)
-        M5, N5, K5 = c5["M"], c5["N"], c5["K"]
-        pw5 = weight(c5)
-        a5 = c5["adapter"]
-        ad5 = mnb.Adapter(mnb.MNB_ADAPTER_Q8, torch.from_numpy(a5["A"]).to(dev), torch.from_numpy(a5["B"]).to(dev),
-                          t16(a5["A_scales"]), t16(a5["B_scales"]))
-        X5, Y5 = t16(c5["X"]), torch.empty((M5, N5), dtype=torch.float16, device=dev)
-        ws5 = torch.zeros(mnb.mnb_workspace_bytes(M5, N5, K5, 4, 32), dtype=torch.uint8, device=dev)
-        s5 = graph_time(lambda j: mnb.matmul(X5, pw5, ad5, out=Y5, ws=ws5), 20)
-        pre_context["batched_q8_us"] = round(s5 * 1e6, 3)
-        pre_context["batched_q8_TFLOPs"] = round(algorithmic_flops(M5, N5, K5, 32) / s5 / 1e12, 2)
-        pre_context["batched_q8_route"] = mnb.mnb_describe_route(M5, N5, K5, 4, False, mnb.MNB_ADAPTER_Q8)[1]
-    dec_route = mnb.mnb_describe_route(dM, dN, dK, 4, False, mnb.MNB_ADAPTER_F16)[1]
-    pre_route = mnb.mnb_describe_route(pM, pN, pK, 4, True, mnb.MNB_ADAPTER_F16)[1]
-    traffic = recorded_traffic("gemv")
 
+    traffic = recorded_traffic("gemv")
     out = {
         "metric": METRIC,
         "value": round(dec_gbps, 1),
@@ -288,7 +366,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(total_ms / K, 5),
+        "ms_per_step": round((dec_s + pre_s) * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -297,8 +375,9 @@ def main():
         "config": {
             "workload": "decode GEMV M=1 N=8192 K=2048 int4 block-32 default-zp + rank-32 F16 LoRA "
                         "(cold HBM, %d rotated copies) + prefill M=1024 N=4096 K=4096 int4 block-32 "
-                        "explicit-zp + rank-32 F16 LoRA" % copies,
+                        "explicit-zp + rank-32 F16 LoRA" % len(dcopies),
             "decode_bytes": dbytes, "prefill_flops": pflops,
+            "timing": "median of 5 timed replays of %d-call graphs after 4 untimed replays" % K,
         },
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
@@ -309,14 +388,48 @@ def main():
                                  "unit": "TFLOP/s", "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4),
                                  "traffic": recorded_traffic("gemm")},
                     "bytes": pbytes},
+        "runs": runs,
+        "ceilings": ceilings,
         "decode_context": context,
-        "prefill_context": pre_context,
         "wall_s": round(wall, 3),
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.no_context:
         out["cpu_baseline"] = cpu_baseline(si, dec, pre, dbytes, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def stream_read_ceilings(torch, dev, timer, cold_mib, n_calls, sizes):
+    """A plain streaming read (ceiling.hip) of each byte count, cold: copies totalling
+    cold_mib rotate; the best of 1, 2, 4 and 8 16-byte loads per thread is reported."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(ROOT, "blockwise_bit_quantized_amd", "libmnb_ceiling.so"))
+    lib.mnb_ceiling_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_int, C.c_void_p, C.c_void_p]
+    lib.mnb_ceiling_stream_read.restype = C.c_int
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    out = {}
+    for name, nbytes in sizes.items():
+        nb = (nbytes + 15) // 16 * 16
+        r = max(1, math.ceil(cold_mib * 2**20 / nb))
+        bufs = [torch.randint(0, 255, (nb,), dtype=torch.uint8, device=dev) for _ in range(r)]
+        best = None
+        for u in (1, 2, 4, 8):
+            def call(j, u=u):
+                st = lib.mnb_ceiling_stream_read(bufs[j % r].data_ptr(), nb, u, sink.data_ptr(),
+                                                 torch.cuda.current_stream(dev).cuda_stream)
+                if st != 0:
+                    raise RuntimeError("stream read launch failed: %d" % st)
+            s = timer.per_call(call, r, n_calls)
+            if best is None or s < best[0]:
+                best = (s, u)
+        out["stream_read_" + name] = {"us": round(best[0] * 1e6, 3), "bytes": nb,
+                                      "GBps": round(nb / best[0] / 1e9, 1),
+                                      "frac": round(nb / best[0] / 1e9 / HBM_PEAK_GBPS, 4),
+                                      "loads_per_thread": best[1], "copies": r,
+                                      "what": "one launch reading the bytes once (16 B loads, 256 threads per "
+                                              "workgroup), cold, best of 1/2/4/8 loads per thread"}
+        del bufs
+    return out
 
 
 def recorded_traffic(kernel):
@@ -324,7 +437,6 @@ def recorded_traffic(kernel):
     profiles/<kernel>_*_traffic.md, if the kernel sources still hash to the recorded value
     (else None: the counters describe a kernel that no longer exists)."""
     import glob
-    import hashlib
     import re
     for path in glob.glob(os.path.join(ROOT, "profiles", kernel + "_*_traffic.md")):
         text = open(path).read()
@@ -346,8 +458,19 @@ def kernel_source_hash(kernel):
     return d.hexdigest()
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(si, dec, pre, dbytes, budget_s):
-    """The FP64 oracle as it stands, on this host's cores, on a bounded sample."""
+    """The FP64 oracle as it stands, on this host's cores: full decode calls (median over
+    about 0.6 x budget_s) and one full prefill call of all 1024 rows."""
     import numpy as np
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
@@ -361,16 +484,16 @@ def cpu_baseline(si, dec, pre, dbytes, budget_s):
         oracle.matmul(dec)
         t.append(time.perf_counter() - a)
     dec_s = float(np.median(t))
-    rows = 8
     a = time.perf_counter()
-    oracle.matmul(dict(pre, X=pre["X"][:rows], M=rows))
+    oracle.matmul(pre)
     pre_s = time.perf_counter() - a
-    pre_flops = algorithmic_flops(rows, pre["N"], pre["K"], 32)
+    pre_flops = algorithmic_flops(pre["M"], pre["N"], pre["K"], 32)
     return {"value": round(dbytes / dec_s / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "decode 8192x2048 int4 + F16 LoRA, full call, median of %d runs (%.3f s each); "
-                      "prefill sample %d of 1024 rows of 1024x4096x4096: %.4f TFLOP/s"
-                      % (len(t), dec_s, rows, pre_flops / pre_s / 1e12),
-            "decode_s": round(dec_s, 4), "prefill_rows_s": round(pre_s, 3),
+            "cpu_model": cpu_model(),
+            "sample": "decode 8192x2048 int4 + F16 LoRA, full call, median of %d runs (%.4f s each); "
+                      "prefill 1024x4096x4096 int4 + F16 LoRA, one full call (all 1024 rows): %.3f s, "
+                      "%.4f TFLOP/s" % (len(t), dec_s, pre_s, pre_flops / pre_s / 1e12),
+            "decode_s": round(dec_s, 5), "prefill_s": round(pre_s, 3),
             "prefill_TFLOPs": round(pre_flops / pre_s / 1e12, 6)}
 
 

@@ -15,6 +15,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmnb.so")
+# measurement helper for the benchmark (a streaming-read ceiling kernel), not the ABI
+CEILING_LIB = os.path.join(PKG, "libmnb_ceiling.so")
+CEILING_SOURCE = "ceiling.hip"
 OBJ = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "gemv.hip", "gemv_rows.hip", "gemv_acc4.hip", "tproj.hip", "gemm.hip", "pack.hip"]
 ARCH = os.environ.get("MNB_OFFLOAD_ARCH", "gfx950")
@@ -64,7 +67,19 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         raise RuntimeError("link failed:\n" + r.stderr)
     _check_undefined(tmp)
     os.replace(tmp, LIB)
+    _build_ceiling(hipcc, verbose)
     return LIB
+
+
+def _build_ceiling(hipcc: str, verbose: bool) -> None:
+    tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc, *HIPCC_FLAGS, "-shared", os.path.join(CSRC, CEILING_SOURCE), "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (CEILING_SOURCE, r.stderr))
+    os.replace(tmp, CEILING_LIB)
 
 
 def _check_undefined(path: str) -> None:
