@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <climits>
 #include <mutex>
 
 #include "common.h"
@@ -66,7 +67,8 @@ int scratch_for(hipStream_t s, void **out) {
 enum { LORA_NONE = 0, LORA_F16 = 1, LORA_Q8 = 2 };
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
-int cdiv(int a, int b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b >= 1 (64-bit sum: a may be INT_MAX)
+int cdiv(int a, int b) { return (int)(((long)a + b - 1) / b); }
 
 // ---- plan -------------------------------------------------------------------------------
 
@@ -163,6 +165,10 @@ int check_common(int M, int N, int K, int bits, int block) {
   if (bits != 2 && bits != 4 && bits != 8) return MNB_ERR_UNSUPPORTED;
   if (block != kBlock || K % kBlock) return MNB_ERR_UNSUPPORTED;
   if (K >= kMaxK) return MNB_ERR_UNSUPPORTED;
+  // every launch's grid fits an int: 64 x 128 GEMM tiles with up to kMaxSplits K ranges
+  // each, and 32-row T-projection tiles with up to ceil(K / 256) K parts each
+  if ((long)cdiv(M, 64) * cdiv(N, 128) * kMaxSplits > INT_MAX) return MNB_ERR_UNSUPPORTED;
+  if ((long)cdiv(M, 32) * cdiv(K, 256) > INT_MAX) return MNB_ERR_UNSUPPORTED;
   return MNB_OK;
 }
 
@@ -234,7 +240,7 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
     const int bm = gemm_bm(M, N);
-    const int ntiles = cdiv(M, bm) * cdiv(N, 128);
+    const int ntiles = cdiv(M, bm) * cdiv(N, 128);   // fits: check_common bounds the grid
     if (w.tsplits > 1)
       snprintf(buf, len, "%sgemm_b%d_zp%s_%s grid=%d tile=%dx128x64 splits=1 tail=%dx%d", tp, bits,
                has_zp ? "x" : "def", ln, w.tail0 + (ntiles - w.tail0) * w.tsplits, bm, ntiles - w.tail0, w.tsplits);
@@ -306,6 +312,7 @@ int mnb_packed_sizes(int N, int K, int bits, int block, int has_zp, size_t *wq_b
 size_t mnb_workspace_bytes(int M, int N, int K, int bits, int rank) {
   (void)bits;
   if (M <= 0 || N <= 0 || K < 0) return 0;
+  if (check_common(M, N, K, 4, kBlock) != MNB_OK) return 0;   // no call accepts these sizes
   return ws_layout(M, N, K, rank ? kRank : 0).total;
 }
 

@@ -777,7 +777,7 @@ hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
 // 128-row tiles would be at most half full (1024 x 9728 at M = 512: 59 against 74 us; small
 // M by 10-20%).
 int gemm_bm(int M, int N) {
-  const long t128 = (long)((M + 127) / 128) * ((N + BN - 1) / BN);
+  const long t128 = (((long)M + 127) / 128) * (((long)N + BN - 1) / BN);
   const long rem = t128 % kCUs;
   return (rem == 0 || rem > kCUs / 2) ? 128 : 64;
 }
@@ -830,7 +830,7 @@ struct Plan {
 // faster.
 Plan gemm_plan(int M, int N, int K) {
   const int bm = gemm_bm(M, N);
-  const long ntiles = (long)((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  const long ntiles = (((long)M + bm - 1) / bm) * (((long)N + BN - 1) / BN);
   const int tsteps = (K / kBlock + 1) / 2;
   Plan plan{1, 1, (int)ntiles};
   if (ntiles <= 0 || tsteps <= 0) return plan;

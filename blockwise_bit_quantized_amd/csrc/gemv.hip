@@ -541,7 +541,7 @@ int loads_per_wave(int K, int bits, int q) {
 // 8192 x 2048 decode: 6.5 us at 256 against 6.9 us at 512; base-only 4.97 us at 512
 // against 5.29 us at 256).
 int gemv_rows_split(int N, bool inpass_t) {
-  const int NG = (N + kGroup - 1) / kGroup;
+  const int NG = (int)(((long)N + kGroup - 1) / kGroup);
   const int target = inpass_t ? 256 : 512;
   int q = 1;
   while (q < 8 && NG * q < target) q *= 2;

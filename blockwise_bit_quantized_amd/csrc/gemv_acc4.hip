@@ -342,7 +342,7 @@ hipError_t launch_b4(bool has_zp, int lora, const GemvParams &p, int lpw, int gx
 // the weights stream once per 4 rows; else 1.  (8 rows measured slower: their registers
 // leave room for one workgroup per CU.)
 int acc4_rows_mr(int M, int N, int K) {
-  const int wgs = (N + kGroup - 1) / kGroup * gemv_rows_split(N, false);
+  const long wgs = ((long)N + kGroup - 1) / kGroup * gemv_rows_split(N, false);
   return M >= 2 && K <= kAcc4MultiRowMaxK && wgs >= 256 ? 4 : 1;
 }
 

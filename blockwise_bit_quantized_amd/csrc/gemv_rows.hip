@@ -295,7 +295,7 @@ hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x,
   const int ncc = chunk_cols(bits, p.KB);
   const int nloads = (ncc + p.q - 1) / p.q;
   const int lpw = (nloads + kWaves - 1) / kWaves;
-  const int gy = (p.M + mr - 1) / mr;
+  const int gy = (int)(((long)p.M + mr - 1) / mr);
   if (bits == 2) return launch_bits<2>(p, lora, mr, lpw, grid_x, gy, s);
   return bits == 4 ? launch_bits<4>(p, lora, mr, lpw, grid_x, gy, s) : launch_bits<8>(p, lora, mr, lpw, grid_x, gy, s);
 }

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
 // than 128 workgroups
 int tproj_kp(int M, int K) {
   if (M > kRowsMaxM) return 512;
-  return ((M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024;
+  return (((long)M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024;
 }
 int tproj_parts(int M, int K) {
   const int kp = tproj_kp(M, K);

@@ -45,7 +45,9 @@ extern "C" {
 enum {
   MNB_OK = 0,
   MNB_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
-  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, K >= 2^28, rank not 0/32 */
+  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, K >= 2^28, rank not 0/32,
+                               or a launch grid past INT_MAX: ceil(M/64) * ceil(N/128) * 16 or
+                               ceil(M/32) * ceil(K/256) */
   MNB_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned */
   MNB_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than mnb_workspace_bytes() */
   MNB_ERR_ALIAS = 5,        /* Y overlaps an input or the workspace */
@@ -164,7 +166,8 @@ int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, in
 /*
  * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path and
  * any adapter kind (host only).  No page defines a workspace: it is this library's own
- * scratch, passed in by the caller so that the library allocates nothing.  The workspace holds partial sums (among them the prefill
+ * scratch, passed in by the caller so that the library allocates nothing.  Returns 0 for
+ * M or N <= 0 and for sizes every call rejects (K % 32 != 0, K >= 2^28, grids past INT_MAX).  The workspace holds partial sums (among them the prefill
  * GEMM's FP32 partial outputs when it splits K over several workgroups per output tile),
  * the LoRA down-projection T and a few counters.  It must be ZERO-FILLED before its first use; every call that
  * completes leaves its counters at zero again, so one workspace can be reused by

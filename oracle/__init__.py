@@ -19,8 +19,9 @@ _libs: dict[str, C.CDLL] = {}
 
 
 def load(path: str | None = None) -> C.CDLL:
-    """Load (building if absent) the oracle library, or a mutated copy at ``path``."""
-    path = path or _build.LIB
+    """Load (building if absent) the oracle library, or a mutated copy at ``path``.  The
+    environment variable MNB_ORACLE_LIB names another build of it (the sanitizer build)."""
+    path = path or os.environ.get("MNB_ORACLE_LIB") or _build.LIB
     if path in _libs:
         return _libs[path]
     if path == _build.LIB and (not os.path.exists(path) or
