@@ -235,7 +235,7 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   } else if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
-    const int q = gemv_rows_split(N, extra > 0);
+    const int q = gemv_decode_split(N, K, bits, extra > 0);
     snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
@@ -451,7 +451,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     p.NG = NG;
     p.KB = KB;
     p.gt = (lora && r.tmode == 0) ? w.gt : 0;
-    p.q = gemv_rows_split(N, p.gt > 0);
+    p.q = gemv_decode_split(N, K, bits, p.gt > 0);
     p.kt = kTSliceRows;
     p.nepi = NG * p.q;
     p.spin_limit = (opt && (opt->flags & MNB_FLAG_FAIL_HANDOFF)) ? -1 : kSpinLimit;

@@ -201,6 +201,7 @@ hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStrea
 
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
+int gemv_decode_split(int N, int K, int bits, bool inpass_t);   // q of the M == 1 decode GEMV
 int tproj_parts(int M, int K);                 // K parts of the T projection
 int gemv_rows_mr(int M, int bits);                       // rows per workgroup of the small-M path
 // largest M of the small-M path: measured crossover against the MFMA GEMM (K split over

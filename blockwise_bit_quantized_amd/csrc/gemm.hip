@@ -341,23 +341,29 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   };
 
   // LoRA epilogue operands, fetched first (ordinary loads that complete ahead of the ring
-  // loads): T rows (FP32 K-part partials, added in part order) and this thread's B slice
+  // loads): T rows (FP32 K-part partials, added in part order) and this thread's B slice.
+  // Two threads per tile row: for 64-row tiles only waves 0 and 1 load T, and only the
+  // parts that exist (the others' loads would be wasted L2 traffic in every tile).
   float tsum[16];
   u4_t braw[2];
   uint32_t bsc[8];
   bool bvec = false;
   const int trow = tid >> 1, thh = (tid & 1) * 16;
+  const bool t_loader = trow < BMT;            // wave-uniform
   const int br = tid >> 3, bnc = (tid & 7) * 16;
   constexpr int kTPartsAhead = 8;            // T parts loaded before the ring starts
   float4 tv[kTPartsAhead][4];
   if (lora_here) {
     const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
+    if (t_loader) {
 #pragma unroll
-    for (int pp = 0; pp < kTPartsAhead; ++pp) {
-      const int pc = pp < p.tparts ? pp : 0;
-      const float *src = p.tpart + ((size_t)pc * p.M + mrow) * kRank + thh;
+      for (int pp = 0; pp < kTPartsAhead; ++pp) {
+        if (pp < p.tparts) {
+          const float *src = p.tpart + ((size_t)pp * p.M + mrow) * kRank + thh;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tv[pp][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
+          for (int q = 0; q < 4; ++q) tv[pp][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
+        }
+      }
     }
     const int n = n0 + bnc;
     if constexpr (LORA == 1) {
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
 #pragma unroll
     for (int pp = 0; pp < kTPartsAhead; ++pp) {
-      if (pp < p.tparts) {
+      if (t_loader && pp < p.tparts) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           tsum[4 * q + 0] += tv[pp][q].x;
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
         }
       }
     }
-    for (int pp = kTPartsAhead; pp < p.tparts; ++pp) {
+    for (int pp = kTPartsAhead; t_loader && pp < p.tparts; ++pp) {
       const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
