@@ -231,16 +231,24 @@ def test_dispatcher_rule():
 
 def test_gemv_grid_covers_the_chip():
     # decode: 64/q rows per workgroup with the smallest q in {1, 2, 4, 8} that gives at least
-    # 512 row workgroups (two per CU), or 256 when T is computed in the same launch, plus
+    # 512 row workgroups (two per CU), or 256 when T is computed in the same launch, then
+    # doubled (up to 8) while one of the 8 waves would issue more than 4 weight loads; plus
     # the T-slice workgroups (K/256 of them)
-    for N, K, bits in ((8192, 2048, 4), (4096, 4096, 4), (49152, 576, 8), (896, 896, 4)):
+    for N, K, bits in ((8192, 2048, 4), (4096, 4096, 4), (49152, 576, 8), (896, 896, 4), (1024, 16384, 4),
+                       (8192, 2048, 2)):
         for kind, target in ((1, 256), (0, 512)):
             t = route(1, N=N, K=K, bits=bits, zp=0, kind=kind)
             grid = int(re.search(r"grid=(\d+)x1", t).group(1))
             q = int(re.search(r" q=(\d+)", t).group(1))
             gt = int(re.search(r"gt=(\d+)", t).group(1))
             ng = (N + 63) // 64
-            assert q in (1, 2, 4, 8) and (ng * q >= target or q == 8) and (q == 1 or ng * q // 2 < target)
+            ncc = (K // 32 + 1) // 2 if bits == 2 else K // 32 * bits // 4
+            loads = lambda qq: -(-(-(-ncc // qq)) // 8)          # loads per wave: ceil(ceil(ncc/q)/8)
+            q0 = next(qq for qq in (1, 2, 4, 8) if ng * qq >= target or qq == 8)
+            want = q0
+            while want < 8 and loads(want) > 4:
+                want *= 2
+            assert q == want, (N, K, bits, kind, q, want)
             assert gt == ((K + 255) // 256 if kind else 0) and grid == ng * q + gt
 
 
