@@ -78,7 +78,7 @@ constexpr int kTSliceRows = 256;  // in-pass T: K rows per slice workgroup
 // workspace stays valid for calls of any shape), then data regions that need no
 // initialisation.
 struct WsLayout {
-  size_t ctrl, tinpass, tproj, tfinal, ypart, total;
+  size_t ctrl, tinpass, tproj, tfinal, xq, ypart, total;
   int gt, tparts, tmt, splits, tsplits, tail0;
 };
 
@@ -95,6 +95,9 @@ WsLayout ws_layout(int M, int N, int K, int rank) {
   if (rank) off += align_up((size_t)w.tparts * M * kRank * sizeof(float));
   w.tfinal = off;
   if (rank) off += align_up((size_t)M * kRank * sizeof(float));
+  // accuracy level 4 on the GEMM path: the block-quantized X, fp16 [M, K]
+  w.xq = off;
+  off += align_up((size_t)M * K * 2);
   // prefill GEMM with K split into ranges: FP32 partial outputs [splits, M, N]; or with
   // only the last round's tiles split: their partials [tsplits, tail tiles, bm, 128]
   w.splits = gemm_splits(M, N, K);
@@ -115,7 +118,7 @@ struct Route {
   int lora;      // LORA_*
   int tmode;     // 0 in-pass, 1 precomputed by the T projection launch
   bool tproj;
-  bool acc4;     // int8 activations for the base product (GEMV family, every M)
+  bool acc4;     // block-quantized int8 activations for the base product
 };
 
 Route route(int M, int lora, const mnb_options *opt) {
@@ -130,7 +133,9 @@ Route route(int M, int lora, const mnb_options *opt) {
   r.tproj = false;
   r.acc4 = (flags & MNB_FLAG_ACC4) != 0;
   if (r.acc4) {
-    r.path = MNB_PATH_GEMV;
+    // the GEMV family (integer dot products) up to kRowsMaxM rows; above, the MFMA GEMM on
+    // the block-quantized X; T always from the projection launch and the unquantized X
+    if (path == MNB_PATH_AUTO) r.path = M <= kRowsMaxM ? MNB_PATH_GEMV : MNB_PATH_GEMM;
     r.tproj = lora != 0;
     return r;
   }
@@ -181,7 +186,9 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
   if (opt) {
     if (opt->path < MNB_PATH_AUTO || opt->path > MNB_PATH_GEMM) return MNB_ERR_INVALID_ARG;
     if (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4 | MNB_FLAG_FAIL_HANDOFF)) return MNB_ERR_INVALID_ARG;
-    if ((opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
+    if ((opt->flags & MNB_FLAG_ACC4) && K > kAcc4MaxK &&
+        (opt->path == MNB_PATH_GEMV || (opt->path == MNB_PATH_AUTO && M <= kRowsMaxM)))
+      return MNB_ERR_UNSUPPORTED;   // the GEMV family's LDS holds at most kAcc4MaxK quantized X
   }
   if (ad) {
     if (ad->kind < MNB_ADAPTER_NONE || ad->kind > MNB_ADAPTER_Q8 || ad->rank < 0) return MNB_ERR_INVALID_ARG;
@@ -218,9 +225,14 @@ int validate(const void *X, const void *wq, const void *sc, const void *zpp, con
 void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, const Route &r) {
   const WsLayout w = ws_layout(M, N, K, r.lora ? kRank : 0);
   const char *ln = r.lora == LORA_NONE ? "none" : (r.lora == LORA_F16 ? "f16" : "q8");
-  char tp[96] = "";
+  char tp[160] = "";
   if (r.tproj) snprintf(tp, sizeof tp, "tproj_%s grid=%d parts=%d; ", ln, w.tmt * w.tparts, w.tparts);
-  if (r.acc4) {
+  if (r.acc4 && r.path == MNB_PATH_GEMM) {
+    // block quantization of X, then the GEMM below on it
+    const size_t n = strlen(tp);
+    snprintf(tp + n, sizeof tp - n, "acc4_xquant grid=%ld; ", ((long)M * (K / kBlock) * 4 + 255) / 256);
+  }
+  if (r.acc4 && r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int q = gemv_rows_split(N, false);
     const int mr = acc4_rows_mr(M, N, K);
@@ -235,7 +247,7 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
   } else if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
-    const int q = gemv_decode_split(N, K, bits, extra > 0);
+    const int q = gemv_rows_split(N, extra > 0);
     snprintf(buf, len, "%sgemv_b%d_zp%s_%s_%s grid=%dx%d rows=%d q=%d gt=%d", tp, bits, has_zp ? "x" : "def", ln,
              r.lora ? (r.tmode == 0 ? "inpass" : "tprecomp") : "base", NG * q + extra, M, kGroup / q, q, extra);
   } else {
@@ -369,7 +381,9 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
   if (opt && (opt->path < 0 || opt->path > 2 ||
               (opt->flags & ~(MNB_FLAG_T_SEPARATE | MNB_FLAG_ACC4 | MNB_FLAG_FAIL_HANDOFF))))
     return MNB_ERR_INVALID_ARG;
-  if (opt && (opt->flags & MNB_FLAG_ACC4) && (opt->path == MNB_PATH_GEMM || K > kAcc4MaxK)) return MNB_ERR_UNSUPPORTED;
+  if (opt && (opt->flags & MNB_FLAG_ACC4) && K > kAcc4MaxK &&
+      (opt->path == MNB_PATH_GEMV || (opt->path == MNB_PATH_AUTO && M <= kRowsMaxM)))
+    return MNB_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) {
     snprintf(buf, buf_len, "noop");
     return MNB_OK;
@@ -451,7 +465,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     p.NG = NG;
     p.KB = KB;
     p.gt = (lora && r.tmode == 0) ? w.gt : 0;
-    p.q = gemv_decode_split(N, K, bits, p.gt > 0);
+    p.q = gemv_rows_split(N, p.gt > 0);
     p.kt = kTSliceRows;
     p.nepi = NG * p.q;
     p.spin_limit = (opt && (opt->flags & MNB_FLAG_FAIL_HANDOFF)) ? -1 : kSpinLimit;
@@ -501,6 +515,12 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
 
   GemmParams g{};
   g.X = static_cast<const uint16_t *>(X);
+  if (r.acc4) {
+    // accuracy level 4: the GEMM multiplies the block-quantized X (T above used the X given)
+    uint16_t *xq = reinterpret_cast<uint16_t *>(ws + w.xq);
+    if (launch_acc4_xquant(g.X, xq, M, K, s) != hipSuccess) return MNB_ERR_HIP;
+    g.X = xq;
+  }
   g.wq = static_cast<const uint8_t *>(wq);
   g.sc = static_cast<const uint16_t *>(sc);
   g.zp = static_cast<const uint8_t *>(zpp);

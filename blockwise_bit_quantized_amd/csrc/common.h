@@ -182,6 +182,8 @@ hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x,
 constexpr int kAcc4MaxK = 16384;
 constexpr int kAcc4MultiRowMaxK = 4096;       // K limit of the 4-rows-per-workgroup form
 int acc4_rows_mr(int M, int N, int K);        // X rows per workgroup row (1 or 4)
+// accuracy level 4 on the GEMM path: Xq = fp16(block-quantized X), [M, K]
+hipError_t launch_acc4_xquant(const uint16_t *X, uint16_t *Xq, int M, int K, hipStream_t s);
 hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
                             hipStream_t s);
 hipError_t launch_tproj(int lora, const TprojParams &p, hipStream_t s);
@@ -201,7 +203,6 @@ hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStrea
 
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
-int gemv_decode_split(int N, int K, int bits, bool inpass_t);   // q of the M == 1 decode GEMV
 int tproj_parts(int M, int K);                 // K parts of the T projection
 int gemv_rows_mr(int M, int bits);                       // rows per workgroup of the small-M path
 // largest M of the small-M path: measured crossover against the MFMA GEMM (K split over

@@ -548,16 +548,6 @@ int gemv_rows_split(int N, bool inpass_t) {
   return q;
 }
 
-// The M == 1 decode: that split, made finer while a wave would issue more than 4 weight
-// loads (more workgroups with fewer loads each keep more of the stream in flight; the
-// 49152 x 576 int8 lm_head, 36 chunk-columns per row, ran 7% faster with 2 workgroups per
-// 64-row group (3 loads per wave) than with one (5 loads per wave)).
-int gemv_decode_split(int N, int K, int bits, bool inpass_t) {
-  int q = gemv_rows_split(N, inpass_t);
-  const int ncc = chunk_cols(bits, K / kBlock);
-  while (q < 8 && ((ncc + q - 1) / q + kWaves - 1) / kWaves > 4) q *= 2;
-  return q;
-}
 
 size_t gemv_lds_bytes(int K, int bits, int q) {
   const int lpw = loads_per_wave(K, bits, q);

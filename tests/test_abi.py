@@ -180,25 +180,29 @@ def test_gemm_k_split_rule():
         sps = -(-steps // S)
         assert 1 <= S <= 16 and (S - 1) * sps < steps, (M, N, K, S)
     assert mnb.mnb_workspace_bytes(256, 4096, 4096, 4, 0) >= 2 * 256 * 4096 * 4
-    assert mnb.mnb_workspace_bytes(1024, 4096, 4096, 4, 0) < 1 << 20
+    # no partials at 1024 x 4096: the control area and accuracy level 4's quantized X [M, K]
+    assert mnb.mnb_workspace_bytes(1024, 4096, 4096, 4, 0) < (1 << 20) + 1024 * 4096 * 2
 
 
 def test_accuracy_level4_route_and_validation():
     A4 = mnb.MNB_FLAG_ACC4
     assert route(1, flags=A4).startswith("tproj_f16") and "gemv_acc4_b4_zpx_f16" in route(1, flags=A4)
     assert route(1, kind=0, flags=A4).startswith("gemv_acc4_b4_zpx_none")
-    assert "gemv_acc4" in route(1024, flags=A4) and "gemv_acc4" in route(5, bits=8, kind=0, flags=A4)
-    assert "gemv_acc4_b2" in route(3, bits=2, flags=A4, path=1)
+    assert "gemv_acc4" in route(16, flags=A4) and "gemv_acc4" in route(5, bits=8, kind=0, flags=A4)
+    assert "gemv_acc4_b2" in route(3, bits=2, flags=A4, path=1) and "gemv_acc4" in route(1024, flags=A4, path=1)
+    # above 16 rows (or with the GEMM path forced): the block quantization of X, then the GEMM
+    for r in (route(17, flags=A4), route(1024, flags=A4), route(4, flags=A4, path=2)):
+        assert r.startswith("tproj_f16") and "; acc4_xquant grid=" in r and "; gemm_b4_zpx_f16" in r, r
+    assert route(1024, kind=0, flags=A4).startswith("acc4_xquant grid=2048; gemm_b4_zpx_none")   # 4 threads per block
     # 4 X rows per workgroup row when the grid is wide and K <= 4096, else one
     assert route(8, N=49152, K=576, bits=8, kind=0, flags=A4).endswith("grid=768x2 rows=64 q=1 mr=4")
     assert route(13, flags=A4).endswith("grid=512x4 rows=8 q=8 mr=4")
     assert route(1, flags=A4).endswith("mr=1") and route(8, K=4128, flags=A4).endswith("grid=512x8 rows=8 q=8 mr=1")
     assert route(3, N=896, K=896, flags=A4).endswith("grid=112x3 rows=8 q=8 mr=1")
-    st, _ = mnb.mnb_describe_route(4, 4096, 4096, 4, 1, 1, mnb.mnb_options(2, A4))
-    assert st == mnb.MNB_ERR_UNSUPPORTED                                    # forced GEMM
     st, _ = mnb.mnb_describe_route(1, 64, 16416, 4, 1, 1, mnb.mnb_options(0, A4))
-    assert st == mnb.MNB_ERR_UNSUPPORTED                                    # K above 16384
-    assert call(opt=mnb.mnb_options(2, A4)) == mnb.MNB_ERR_UNSUPPORTED
+    assert st == mnb.MNB_ERR_UNSUPPORTED                                    # GEMV family, K above 16384
+    st, _ = mnb.mnb_describe_route(17, 64, 16416, 4, 1, 1, mnb.mnb_options(0, A4))
+    assert st == mnb.MNB_OK                                                 # the GEMM takes any K
     assert call(K=16416, opt=mnb.mnb_options(0, A4)) == mnb.MNB_ERR_UNSUPPORTED
     assert call(opt=mnb.mnb_options(0, 8)) == mnb.MNB_ERR_INVALID_ARG      # unknown flag
     # the handoff failure hook is a known flag (the GPU tests exercise it)
@@ -231,8 +235,7 @@ def test_dispatcher_rule():
 
 def test_gemv_grid_covers_the_chip():
     # decode: 64/q rows per workgroup with the smallest q in {1, 2, 4, 8} that gives at least
-    # 512 row workgroups (two per CU), or 256 when T is computed in the same launch, then
-    # doubled (up to 8) while one of the 8 waves would issue more than 4 weight loads; plus
+    # 512 row workgroups (two per CU), or 256 when T is computed in the same launch, plus
     # the T-slice workgroups (K/256 of them)
     for N, K, bits in ((8192, 2048, 4), (4096, 4096, 4), (49152, 576, 8), (896, 896, 4), (1024, 16384, 4),
                        (8192, 2048, 2)):
@@ -242,12 +245,7 @@ def test_gemv_grid_covers_the_chip():
             q = int(re.search(r" q=(\d+)", t).group(1))
             gt = int(re.search(r"gt=(\d+)", t).group(1))
             ng = (N + 63) // 64
-            ncc = (K // 32 + 1) // 2 if bits == 2 else K // 32 * bits // 4
-            loads = lambda qq: -(-(-(-ncc // qq)) // 8)          # loads per wave: ceil(ceil(ncc/q)/8)
-            q0 = next(qq for qq in (1, 2, 4, 8) if ng * qq >= target or qq == 8)
-            want = q0
-            while want < 8 and loads(want) > 4:
-                want *= 2
+            want = next(qq for qq in (1, 2, 4, 8) if ng * qq >= target or qq == 8)
             assert q == want, (N, K, bits, kind, q, want)
             assert gt == ((K + 255) // 256 if kind else 0) and grid == ng * q + gt
 
