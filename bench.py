@@ -292,17 +292,17 @@ def main():
             del copies
             return s
 
-        def mfma_run(name, case, ad_kind, n_calls=20):
+        def mfma_run(name, case, ad_kind, n_calls=20, flags=0):
             pw, ad, X = weight(case), adapter(case), t16(case["X"])
             M, N, Kc = case["M"], case["N"], case["K"]
             Y = torch.empty((M, N), dtype=torch.float16, device=dev)
             w = torch.zeros(max(mnb.mnb_workspace_bytes(M, N, Kc, case["bits"], 32), 1), dtype=torch.uint8,
                             device=dev)
-            s = timer.per_call(lambda j: mnb.matmul(X, pw, ad, out=Y, ws=w), 1, n_calls)
+            s = timer.per_call(lambda j: mnb.matmul(X, pw, ad, flags=flags, out=Y, ws=w), 1, n_calls)
             fl = algorithmic_flops(M, N, Kc, 32 if ad is not None else 0)
             runs[name] = {"us": round(s * 1e6, 3), "TFLOPs": round(fl / s / 1e12, 2),
                           "frac": round(fl / s / 1e12 / FP16_PEAK_TFLOPS, 4), "flops": fl, "cold": False,
-                          "route": route(case, ad_kind)}
+                          "route": route(case, ad_kind, flags)}
             return s
 
         # every decode and prefill run of the workloads
@@ -323,6 +323,8 @@ def main():
         c5 = si.make_config(5)
         mfma_run("cfg5_m1024", c5, mnb.MNB_ADAPTER_Q8)
         mfma_run("cfg5_m1024_empty", si.make_config(5, adapter=False), 0)
+        # accuracy level 4 (block-quantized activations) at the prefill shape
+        mfma_run("cfg3_m1024_acc4", pre, mnb.MNB_ADAPTER_F16, flags=mnb.MNB_FLAG_ACC4)
 
         # ceilings: a plain streaming read of the decode byte counts (cold), and the dense
         # FP16 GEMM at the prefill shape (hipBLASLt through torch)

@@ -346,6 +346,51 @@ int acc4_rows_mr(int M, int N, int K) {
   return M >= 2 && K <= kAcc4MultiRowMaxK && wgs >= 256 ? 4 : 1;
 }
 
+namespace {
+
+// Accuracy level 4 for the prefill GEMM: X' = fp16(q * sx) for every row and block of 32
+// along K, with q and sx decided exactly as the GEMV path above does (FP32 amax, 127 / amax,
+// rint, clamp, amax / 127), so that the MFMA GEMM multiplies the block-quantized
+// activations.  Four threads per block (8 values each, 16-byte loads and stores); the
+// block's amax is combined across the four lanes by shuffles.
+__global__ __launch_bounds__(256) void acc4_xquant_kernel(const uint16_t *X, uint16_t *Xq, long nblocks) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const long blk = t >> 2;
+  const bool in = blk < nblocks;
+  u4_t raw = u4_t{0u, 0u, 0u, 0u};
+  if (in) raw = *reinterpret_cast<const u4_t *>(X + 8 * t);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)as_h2(raw[e >> 1])[e & 1];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));      // the four lanes of a block are adjacent
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const float inv = amax > 0.f ? 127.f / amax : 0.f;
+  const float sx = amax / 127.f;
+  u4_t out;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float q0 = fminf(fmaxf(rintf(v[e] * inv), -127.f), 127.f);
+    const float q1 = fminf(fmaxf(rintf(v[e + 1] * inv), -127.f), 127.f);
+    const h2_t h = {(_Float16)(q0 * sx), (_Float16)(q1 * sx)};
+    out[e >> 1] = as_u32(h);
+  }
+  if (in) *reinterpret_cast<u4_t *>(Xq + 8 * t) = out;
+}
+
+}  // namespace
+
+hipError_t launch_acc4_xquant(const uint16_t *X, uint16_t *Xq, int M, int K, hipStream_t s) {
+  if (K % kBlock) return hipErrorInvalidValue;
+  const long nblocks = (long)M * (K / kBlock);
+  const long threads = 4 * nblocks;
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(acc4_xquant_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, X, Xq, nblocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_acc4(int bits, bool has_zp, int lora, const GemvParams &p, int grid_x, int grid_y,
                             hipStream_t s) {
   if (p.K > kAcc4MaxK || p.K % kBlock) return hipErrorInvalidValue;

@@ -71,11 +71,13 @@ enum {
   MNB_FLAG_T_SEPARATE = 1,
   /* Accuracy level 4: the base product takes int8 activations, quantized per row and per
    * block of 32 along K (amax = max |x|, q = rint(x * (127 / amax)) clamped to +-127,
-   * scale amax / 127, FP32), with integer dot products; the LoRA term keeps the FP16 X
-   * (PR #33370 commit list: int8-quantized activations for the base product while T uses
-   * the unquantized FP16 X; PR #33800 Description: the lm_head at the default accuracy level 4).  Runs the
-   * GEMV family for every M (T from the projection launch when there is an adapter).
-   * Requires K <= 16384 and a path of AUTO or GEMV (MNB_ERR_UNSUPPORTED otherwise). */
+   * scale amax / 127, FP32); the LoRA term keeps the FP16 X (PR #33370 commit list:
+   * int8-quantized activations for the base product while T uses the unquantized FP16 X;
+   * PR #33800 Description: the lm_head at the default accuracy level 4).  T comes from the
+   * projection launch when there is an adapter.  Up to 16 rows (or with MNB_PATH_GEMV) the
+   * GEMV family runs integer dot products on the codes (requires K <= 16384, else
+   * MNB_ERR_UNSUPPORTED); above 16 rows (or with MNB_PATH_GEMM) a pre-pass writes
+   * q * sx rounded to fp16 into the workspace and the MFMA GEMM multiplies it. */
   MNB_FLAG_ACC4 = 2,
   /* Test hook for the failure path of the decode's in-pass T handoff: the row workgroups
    * give up on T without waiting, exactly as when their bounded wait (about 2^22 polls)
@@ -164,12 +166,13 @@ int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, in
                int block, uint8_t *codes, void *scales, uint8_t *zp, void *stream);
 
 /*
- * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path and
- * any adapter kind (host only).  No page defines a workspace: it is this library's own
+ * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path, any
+ * adapter kind and any flags (host only).  No page defines a workspace: it is this library's own
  * scratch, passed in by the caller so that the library allocates nothing.  Returns 0 for
  * M or N <= 0 and for sizes every call rejects (K % 32 != 0, K >= 2^28, grids past INT_MAX).  The workspace holds partial sums (among them the prefill
  * GEMM's FP32 partial outputs when it splits K over several workgroups per output tile),
- * the LoRA down-projection T and a few counters.  It must be ZERO-FILLED before its first use; every call that
+ * the LoRA down-projection T, accuracy level 4's block-quantized X for the GEMM path
+ * (fp16 [M, K]) and a few counters.  It must be ZERO-FILLED before its first use; every call that
  * completes leaves its counters at zero again, so one workspace can be reused by
  * consecutive calls on one stream.  Calls that overlap in time must not share a workspace.
  */

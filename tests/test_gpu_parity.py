@@ -454,9 +454,21 @@ def test_acc4_against_oracle(bits, adapter):
         rows = list(range(M)) if M <= 16 else [0, 1, 63, 64, M - 1]
         ref4 = oracle.matmul(dict(rows_case(case, rows), acc_level=4))
         pw = dev_weight(case)
-        for path in (0, 1):
+        for path in (0, 1, 2):           # auto, the GEMV family, the GEMM on the quantized X
             y = run(case, path, mnb.MNB_FLAG_ACC4, pw=pw)
             compare(y[rows], ref4, what="acc4 path=%d M=%d N=%d K=%d" % (path, M, N, K))
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_acc4_prefill_workloads(cfg):
+    """Accuracy level 4 at the prefill workloads (the GEMM on the block-quantized X, T from the
+    unquantized X): every output against the oracle at level 4."""
+    case = si.make_config(cfg)
+    assert "acc4_xquant" in mnb.mnb_describe_route(case["M"], case["N"], case["K"], case["bits"],
+                                                   case["zp"] is not None, 1 if cfg == 3 else 2,
+                                                   mnb.mnb_options(0, mnb.MNB_FLAG_ACC4))[1]
+    y = run(case, 0, mnb.MNB_FLAG_ACC4)
+    compare(y, oracle.matmul(dict(case, acc_level=4)), what="acc4 cfg%d" % cfg)
 
 
 def acc4_exact_case(seed, M, N, K, bits, zp, kind):
@@ -472,20 +484,32 @@ def acc4_exact_case(seed, M, N, K, bits, zp, kind):
             c = r.integers(-127, 128, size=32)
             c[r.integers(0, 32)] = 127
             X[m, 32 * b:32 * b + 32] = c * 2.0 ** -int(r.integers(8, 11))
+    if kind == "f16":
+        # A nonzero in 4 rows of one block per rank column, so that T = X.A (one power of two
+        # times at most 4 products of 7-bit and 2-bit integers) is exact in fp16 as well: the
+        # GEMM path rounds T to an fp16 MFMA operand, the GEMV family keeps it in FP32
+        A = np.zeros((K, 32))
+        b0 = int(r.integers(0, K // 32))
+        for col in range(32):
+            ks = 32 * b0 + r.choice(32, size=4, replace=False)
+            A[ks, col] = r.integers(-3, 4, size=4) * 0.25
+        case["adapter"] = dict(case["adapter"], A=si.to_f16_bits(A))
     return dict(case, X=si.to_f16_bits(X))
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("kind", [None, "f16"], ids=["base", "f16"])
-@pytest.mark.parametrize("M", [1, 6, 11])
+@pytest.mark.parametrize("M", [1, 6, 11, 40])
 def test_acc4_exact_bit_exact(bits, kind, M):
     """On exactly representable activations accuracy level 4 is lossless: GPU == oracle at
-    level 4 == oracle at level 0, bit for bit."""
+    level 4 == oracle at level 0, bit for bit, on every path (M = 40 routes to the GEMM)."""
     N = 4096 if M == 11 else 192           # M = 11 takes 4 X rows per workgroup row
     case = acc4_exact_case(500 + 10 * bits + M, M, N, 320, bits, bits != 8, kind)
     want = oracle.f64_to_f16(oracle.matmul(dict(case, acc_level=4)))
     assert same_bits(want, oracle.f64_to_f16(oracle.matmul(case)))
-    assert same_bits(run(case, 0, mnb.MNB_FLAG_ACC4), want)
+    pw = dev_weight(case)
+    for path in (0, 1, 2):
+        assert same_bits(run(case, path, mnb.MNB_FLAG_ACC4, pw=pw), want), path
 
 
 def test_acc4_differs_from_fp16_activations():
@@ -537,12 +561,13 @@ def test_determinism_and_workspace_reuse():
 def test_graph_replay_matches_eager():
     """Calls captured in a HIP graph (decode with the in-pass T handoff, small M with the T
     reduction in the projection, split-K prefill, a prefill whose last round of tiles splits
-    K, accuracy level 4 with one and with four X rows per workgroup) give, on every replay, exactly the eager results, with eager calls
+    K, accuracy level 4 with one and with four X rows per workgroup and on the GEMM path) give, on every replay, exactly the eager results, with eager calls
     on the same workspace between the replays: the library enqueues no memset and keeps its
     per-call state (the T epoch, the counters) in the workspace."""
     specs = [(1, 4096, 2048, 4, False, "f16", 0), (3, 1000, 1024, 4, True, "q8", 0),
              (200, 512, 1024, 8, True, "f16", 0), (1000, 4100, 640, 4, False, "f16", 0),
-             (1, 896, 896, 4, True, None, mnb.MNB_FLAG_ACC4), (6, 4096, 640, 4, True, "f16", mnb.MNB_FLAG_ACC4)]
+             (1, 896, 896, 4, True, None, mnb.MNB_FLAG_ACC4), (6, 4096, 640, 4, True, "f16", mnb.MNB_FLAG_ACC4),
+             (300, 640, 512, 4, True, "f16", mnb.MNB_FLAG_ACC4)]
     assert mnb.mnb_describe_route(6, 4096, 640, 4, 1, 1, mnb.mnb_options(0, mnb.MNB_FLAG_ACC4))[1].endswith("mr=4")
     assert " tail=" in mnb.mnb_describe_route(1000, 4100, 640, 4, 0, 1)[1]
     ws = torch.zeros(max(mnb.mnb_workspace_bytes(M, N, K, b, 32) for M, N, K, b, *_ in specs), dtype=torch.uint8,
