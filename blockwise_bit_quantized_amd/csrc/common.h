@@ -48,6 +48,15 @@ __device__ __forceinline__ h2_t as_h2(uint32_t v) { return __builtin_bit_cast(h2
 __device__ __forceinline__ uint32_t as_u32(h2_t v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float h2f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// Raw buffer descriptor over [base, base + bytes) (gfx9-family word 3: 32-bit data format,
+// no swizzle, stride 0).  A buffer load whose byte offset lies at or past `bytes` returns
+// zeros instead of touching memory; `bytes` is clamped to [0, 2^31 - 1].  The offsets
+// passed with it are VGPR offsets (the range check covers them), the SGPR offset is 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, long bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7fffffffL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
 // Device-scope (all XCDs) store of a flag word, written through the L2 (no fence: agent-
 // scope fences write back and invalidate a whole L2 on this part).
 __device__ __forceinline__ void atomic_store_agent(int *p, int v) {

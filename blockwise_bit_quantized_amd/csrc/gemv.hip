@@ -13,12 +13,20 @@
 //    sums leave the workgroup.  One wave load of 16 B per lane covers R rows x Q
 //    chunk-columns (Q contiguous segments of R*16 B inside the 1 KiB chunks of the packed
 //    layout); Q is chosen so the grid has enough workgroups to spread over the 256 CUs;
-//  * every wave issues all of its code, scale and zero-point loads first; the X slice the
-//    workgroup needs is staged into LDS meanwhile, so the only memory round trip before
-//    the arithmetic is the weight stream itself;
-//  * (q - z) is formed exactly in fp16 and dotted with X pairs by v_dot2_f32_f16; each
-//    chunk's partial is scaled once in FP32.  The Q lanes that share a row are combined by
-//    lane exchange, the waves through LDS, both in fixed order;
+//  * every wave issues its X slice and then all of its code, scale and zero-point loads
+//    before it waits on anything, so the only memory round trip before the arithmetic is
+//    the weight stream itself.  The weight streams are read through buffer descriptors
+//    that end at the group's last block (the hardware range check returns zeros past it),
+//    so no lane computes a clamped address: the address work per load is one add;
+//  * arithmetic is what bounds this kernel once its single round trip has landed (the
+//    dequantization runs after the data arrives, on every SIMD at once), so each pair of
+//    codes costs one v_bfi_b32 (codes into fp16 mantissas: 1024 + q, or 1024 + 16 q /
+//    1024 + 4^e q for fields taken in place) and one v_dot2_f32_f16 against X.  The
+//    offsets and the zero point leave the inner loop: each block subtracts C + z S once,
+//    with S the block's X sum and C its X sum weighted by the fields' offsets, both
+//    computed while X is staged (default zero point: one number).  Each chunk's partial is
+//    scaled once in FP32.  The Q lanes that share a row are combined by lane exchange, the
+//    waves through LDS, both in fixed order;
 //  * in-pass T: the first `gt` workgroups of the grid compute T over K-slices of `kt` rows.
 //    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
 //    where the tag identifies this call (a per-call epoch kept in the workspace, never 0),
@@ -92,6 +100,45 @@ __device__ __forceinline__ bool gather_t(const unsigned long long *tw, int gt, u
   }
   t = s;
   return ok;
+}
+
+// Lane exchanges for sums (each returns the partner lane's value): xor 1 and xor 2 by DPP
+// quad permutes, xor 8 and xor 16 by ds_swizzle (bit-mask mode inside 32 lanes), xor 32 by
+// ds_bpermute.  None needs the generic shuffle's width bookkeeping.
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+template <int MASK>
+__device__ __forceinline__ float lane_xor_swz(float v) {
+  static_assert(MASK > 0 && MASK < 32, "ds_swizzle exchanges inside 32 lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), (MASK << 10) | 0x1F));
+}
+__device__ __forceinline__ float lane_xor32(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, v)));
+}
+
+// LoRA term of this lane's row: sum_r t[r] * b[r] in r order, with t[r] in LDS (lane r
+// reads it, then each is broadcast by v_readlane) and b[r] packed two per word (F16, or
+// INT8 in the low byte of each half with the column scale `bs` applied once at the end).
+// (A form that reads t as 16-byte LDS broadcasts into four accumulators measured 0.3 us
+// slower per 8192 x 2048 call.)
+template <int LORA>
+__device__ __forceinline__ float lora_dot(const float *t, const uint32_t *bpk, float bs) {
+  const float tv = t[threadIdx.x & 31];
+  float lora = 0.f;
+#pragma unroll
+  for (int r = 0; r < kRank; ++r) {
+    const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
+    float b;
+    if constexpr (LORA == LORA_F16) b = (float)__builtin_bit_cast(_Float16, (uint16_t)(bpk[r / 2] >> (16 * (r & 1))));
+    else b = (float)(int8_t)((bpk[r / 2] >> (16 * (r & 1))) & 0xff);
+    lora = fmaf(tr, b, lora);
+  }
+  if constexpr (LORA == LORA_Q8) lora *= bs;
+  return lora;
 }
 
 // Epoch count: every workgroup of an in-pass launch (slices and rows) arrives once, right
@@ -240,8 +287,9 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
   constexpr bool kTWave = LORA != LORA_NONE && TMODE == T_INPASS;
   __shared__ float red[kWaves][kGroup];
   __shared__ float tsh[kWaves][kRank];
-  __shared__ float tfin[kRank];
   __shared__ __attribute__((aligned(16))) _Float16 xs[kWaves][XW];   // per-wave X slices
+  __shared__ float2 xsum[kWaves][XW / 8 / (BITS == 8 ? 2 : 4)];       // per-block X sums (C, S)
+  __shared__ __attribute__((aligned(16))) float tfin[kRank];              // T for the epilogue
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -313,9 +361,34 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
   const int ncc = chunk_cols(BITS, p.KB); // chunk-columns per row
   const int nloads = (ncc + Q - 1) / Q; // wave loads per workgroup
   const _Float16 *xrow = reinterpret_cast<const _Float16 *>(p.X) + (size_t)m * p.K;
-  const size_t tile0 = (size_t)g * p.KB;
+  // Per-lane byte offsets inside one wave load's window (Q chunk-columns, this lane's row);
+  // the uniform part of each load's offset is added per load.  Codes, scales and zero points
+  // are read through buffer descriptors that end at the group's last block, so a lane whose
+  // chunk-column lies past the row (K not a multiple of Q chunk-columns), and every load of a
+  // slot past the last wave load, reads zeros; its X is staged as zeros too, so it adds
+  // exactly nothing.
+  constexpr int kZpLane = BITS == 4 ? 32 : (BITS == 8 ? 64 : 16);   // zero-point bytes per block
+  const uint32_t w_lane = (uint32_t)(qi * kGroup + row) * 16u;
+  uint32_t s_lane, z_lane;
+  if constexpr (BITS == 4) {
+    s_lane = (uint32_t)(qi * kGroup + row) * 2u;
+    z_lane = (uint32_t)(qi * kZpLane + (row >> 1));
+  } else if constexpr (BITS == 8) {
+    s_lane = (uint32_t)((qi >> 1) * kGroup + row) * 2u;
+    z_lane = (uint32_t)((qi >> 1) * kZpLane + row);
+  } else {
+    s_lane = (uint32_t)(2 * qi * kGroup + row) * 2u;
+    z_lane = (uint32_t)(2 * qi * kZpLane + (row >> 2));
+  }
+  // X: piece pc (8 halfs, 16 B) of this wave's slots; its byte offset minus the uniform
+  // (l0 + wave) * Q * KPC * 2 part, and the correction slot it contributes to
+  constexpr int kPieces = XW / 8;
+  constexpr int kPiecesPerChunk = KPC / 8;
+  constexpr int kPiecesPerSum = BITS == 8 ? 2 : 4;       // one sum per 32-k block (8-bit: per chunk)
+  constexpr int kSums = kPieces / kPiecesPerSum;
 
-  // LoRA: this lane's column of B, loaded with the weight stream (independent of T)
+
+  // LoRA: this lane's column of B, loaded ahead of the weight stream (independent of T)
   uint32_t bpk[kRank / 2];
   float bscale = 0.f;
   if constexpr (LORA != LORA_NONE) {
@@ -339,68 +412,93 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
   float acc = 0.f;
   // rounds of up to kWaves*LPW wave loads (one round at the decode workloads)
   for (int l0 = 0; l0 < nloads; l0 += kWaves * LPW) {
-    const int lend = min(nloads, l0 + kWaves * LPW);
-    // 1. weight stream: all of this wave's loads of the round (clamped addresses)
+    const int c0 = l0 * Q;                                   // first chunk-column of the round
+    const int kb0 = BITS == 4 ? c0 : (BITS == 8 ? c0 / 2 : 2 * c0);   // its first block
+    const auto rw = buffer_rsrc(p.wq + ((size_t)g * ncc + c0) * kGroup * 16, (long)(ncc - c0) * kGroup * 16);
+    const auto rs = buffer_rsrc(p.sc + ((size_t)g * p.KB + kb0) * kGroup, (long)(p.KB - kb0) * kGroup * 2);
+    const auto rz = buffer_rsrc(HAS_ZP ? p.zp + ((size_t)g * p.KB + kb0) * kZpLane : p.wq,
+                                HAS_ZP ? (long)(p.KB - kb0) * kZpLane : 0);
+    // 1. X first (its loads return first), then this wave's weight stream
+    u4_t xv[(kPieces + 63) / 64];
+    {
+      const auto rx = buffer_rsrc(xrow, (long)p.K * 2);
+#pragma unroll
+      for (int t = 0; t < (kPieces + 63) / 64; ++t) {
+        const int pc = lane + 64 * t;
+        const int j = pc / kPiecesPerChunk, sub = pc % kPiecesPerChunk;
+        const int cc = (l0 + wave + kWaves * (j / Q)) * Q + j % Q;
+        const uint32_t off = pc < kPieces ? (uint32_t)(cc * KPC + sub * 8) * 2u : 0x7ffffff0u;
+        xv[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+      }
+    }
     u4_t cw[LPW];
     uint32_t sraw[LPW], zraw[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int l = l0 + wave + kWaves * i;
-      const int cc = l * Q + qi;
-      const bool ok = l < lend && cc < ncc;
-      const int ccl = ok ? cc : 0;
-      cw[i] = *reinterpret_cast<const u4_t *>(p.wq + (((size_t)g * ncc + ccl) * kGroup + row) * 16);
-      if constexpr (BITS == 2) {
-        // two blocks per chunk: both scales in one word (0 for a block past K), both
-        // zero-point bytes in the low two bytes
-        const int kb0 = 2 * ccl, kb1 = min(2 * ccl + 1, p.KB - 1);
-        const uint32_t s1 = 2 * ccl + 1 < p.KB ? p.sc[(tile0 + kb1) * kGroup + row] : 0u;
-        sraw[i] = p.sc[(tile0 + kb0) * kGroup + row] | (s1 << 16);
-        zraw[i] = 0;
-        if constexpr (HAS_ZP)
-          zraw[i] = p.zp[(tile0 + kb0) * 16 + (row >> 2)] | ((uint32_t)p.zp[(tile0 + kb1) * 16 + (row >> 2)] << 8);
+      const uint32_t rel = (uint32_t)(wave + kWaves * i);    // load index within the round
+      cw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + rel * (Q * kGroup * 16), 0, 0);
+      if constexpr (BITS == 4) {
+        sraw[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_lane + rel * (Q * kGroup * 2), 0, 0);
+        zraw[i] = HAS_ZP ? __builtin_amdgcn_raw_buffer_load_b8(rz, z_lane + rel * (Q * kZpLane), 0, 0) : 0u;
+      } else if constexpr (BITS == 8) {
+        const uint32_t tl = (rel * Q) >> 1;                  // block of the load (Q = 1: two loads per block)
+        sraw[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, s_lane + tl * (kGroup * 2), 0, 0);
+        zraw[i] = HAS_ZP ? __builtin_amdgcn_raw_buffer_load_b8(rz, z_lane + tl * kZpLane, 0, 0) : 0u;
       } else {
-        const size_t tile = tile0 + ccl / (BITS / 4);
-        sraw[i] = p.sc[tile * kGroup + row];
-        zraw[i] = 0;
-        if constexpr (HAS_ZP) {
-          if constexpr (BITS == 4) zraw[i] = p.zp[tile * 32 + (row >> 1)];
-          else zraw[i] = p.zp[tile * kGroup + row];
-        }
+        // two blocks per chunk: both scales in one word, both zero-point bytes in the low two
+        const uint32_t so = s_lane + rel * (Q * kGroup * 4), zo = z_lane + rel * (Q * kZpLane * 2);
+        sraw[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, so, 0, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, so + kGroup * 2, 0, 0) << 16);
+        zraw[i] = HAS_ZP ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, zo, 0, 0) |
+                               ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rz, zo + kZpLane, 0, 0) << 8)
+                         : 0u;
       }
     }
-    // 2. this wave's X: slot j = i*Q + qi holds the KPC values of chunk-column
-    //    (l0 + wave + kWaves*i)*Q + qi, loaded 16 B per lane (clamped past the end)
-    constexpr int kPieces = XW / 8;
+    // 2. X to LDS, with each block's X sums: the codes enter the dot products as 1024 + q
+    //    (and 1024 + 16 q or 1024 + 4^e q for the in-place fields), so every block subtracts
+    //    C + z S once, where S is the block's X sum and C the X sum weighted by each field's
+    //    offset (default zero point: C + z S is one number, folded into the constants).
+    //    xsum[wave] is written and read by this wave only: LDS order suffices.
 #pragma unroll
-    for (int pc = lane; pc < kPieces; pc += 64) {
-      const int j = pc / (KPC / 8), sub = pc % (KPC / 8);
-      const int i = j / Q, q = j % Q;
-      const int cc = (l0 + wave + kWaves * i) * Q + q;
-      // (2-bit: the second block of the last chunk of an odd block count lies past K; its
-      // X is staged as zeros, its scale is 0)
-      const int k = cc * KPC + sub * 8;
-      const bool kin = cc < ncc && k < p.K;
-      u4_t xv = *reinterpret_cast<const u4_t *>(xrow + (kin ? k : 0));
-      if (!kin) xv = u4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u4_t *>(&xs[wave][pc * 8]) = xv;
+    for (int t = 0; t < (kPieces + 63) / 64; ++t) {
+      const int pc = lane + 64 * t;
+      if (pc < kPieces) *reinterpret_cast<u4_t *>(&xs[wave][pc * 8]) = xv[t];
+      constexpr float zd = (float)(1 << (BITS - 1));          // default zero point
+      const float zc = HAS_ZP ? 0.f : zd;
+      float c = 0.f, s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // field offset of word e of the piece: 4-bit 1024, 64 (the 16x fields, rescaled);
+        // 8-bit 1024; 2-bit 1024 / 4^e
+        const float off = BITS == 8 ? 1024.f : (BITS == 4 ? ((e & 1) ? 64.f : 1024.f) : 1024.f / (float)(1 << (2 * e)));
+        const _Float16 k = (_Float16)(off + zc);
+        c = __builtin_amdgcn_fdot2(as_h2(xv[t][e]), h2_t{k, k}, c, false);
+        if constexpr (HAS_ZP) s = __builtin_amdgcn_fdot2(as_h2(xv[t][e]), h2_t{(_Float16)1.f, (_Float16)1.f}, s, false);
+      }
+      c += lane_xor1(c);
+      if constexpr (HAS_ZP) s += lane_xor1(s);
+      if constexpr (kPiecesPerSum == 4) {
+        c += lane_xor2(c);
+        if constexpr (HAS_ZP) s += lane_xor2(s);
+      }
+      if (pc < kPieces && pc % kPiecesPerSum == 0) xsum[wave][pc / kPiecesPerSum] = make_float2(c, s);
     }
-    // 3. arithmetic (xs[wave] is written and read by this wave only: LDS order suffices)
+    // 3. arithmetic: a slot past the last wave load is skipped (the condition is uniform)
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int l = l0 + wave + kWaves * i;
-      const int cc = l * Q + qi;
-      if (l < lend && cc < ncc) {
-        const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xs[wave][(i * Q + qi) * KPC]);
+      if (l < nloads) {
+        const int slot = i * Q + qi;
+        const uint32_t *xw = reinterpret_cast<const uint32_t *>(&xs[wave][slot * KPC]);
         if constexpr (BITS == 2) {
           // two blocks; in each 32-bit word the four 2-bit field pairs of a byte are taken
-          // in place (v_bfi_b32): pair e comes out as 4^e (q - z), exact, into its own
+          // in place (v_bfi_b32): pair e comes out as 1024 + 4^e q into its own
           // accumulator pe, which a power-of-two FP32 rescale puts back exactly
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            uint32_t z = 2u;
-            if constexpr (HAS_ZP) z = ((zraw[i] >> (8 * h)) >> ((row & 3) * 2)) & 3u;
-            float pe[4] = {0.f, 0.f, 0.f, 0.f};
+            const float2 cs = xsum[wave][2 * slot + h];
+            float pe[4] = {-cs.x, 0.f, 0.f, 0.f};
+            if constexpr (HAS_ZP) pe[0] = fmaf(-(float)(((zraw[i] >> (8 * h)) >> ((row & 3) * 2)) & 3u), cs.y, -cs.x);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const u4_t xa = *reinterpret_cast<const u4_t *>(xw + 16 * h + 8 * j);
@@ -409,54 +507,55 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const uint32_t mask = 0x00030003u << (2 * e);
-                const h2_t zz = as_h2(((z << (2 * e)) * 0x00010001u) | 0x64006400u);   // 1024 + 4^e z
-                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w, 0x64006400u)) - zz, as_h2(xa[e]), pe[e], false);
-                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w8, 0x64006400u)) - zz, as_h2(xb[e]), pe[e], false);
+                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w, 0x64006400u)), as_h2(xa[e]), pe[e], false);
+                pe[e] = __builtin_amdgcn_fdot2(as_h2(bfi(mask, w8, 0x64006400u)), as_h2(xb[e]), pe[e], false);
               }
             }
-            const float blk = pe[0] + pe[1] * 0.25f + pe[2] * 0.0625f + pe[3] * 0.015625f;
+            const float blk = fmaf(pe[3], 0.015625f, fmaf(pe[2], 0.0625f, fmaf(pe[1], 0.25f, pe[0])));
             acc = fmaf(blk, h2f((uint16_t)(sraw[i] >> (16 * h))), acc);
           }
           continue;
         }
-        uint32_t z = 1u << (BITS - 1);
-        if constexpr (HAS_ZP) z = BITS == 4 ? (zraw[i] >> ((row & 1) * 4)) & 0xFu : zraw[i];
-        const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);   // 1024 + z, both halves
-        float p0 = 0.f, p1 = 0.f;
+        const float2 cs = xsum[wave][slot];
+        float p0 = -cs.x, p1 = 0.f;
+        if constexpr (HAS_ZP) {
+          const uint32_t z = BITS == 4 ? (zraw[i] >> ((row & 1) * 4)) & 0xFu : zraw[i];
+          p0 = fmaf(-(float)z, cs.y, -cs.x);
+        }
         if constexpr (BITS == 4) {
-          // pairs 1 and 3 come out as 16 (q - z) (nib_hi16): p1 holds 16x its terms, which
-          // the power-of-two rescale below undoes exactly
-          const h2_t zz16 = as_h2((z * 0x00100010u) | 0x64006400u);   // 1024 + 16 z
+          // fields 1 and 3 of each half are taken in place as 1024 + 16 q (nib_hi16): p1
+          // holds 16x its terms, which the power-of-two rescale below undoes exactly
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const u4_t xv = *reinterpret_cast<const u4_t *>(xw + 4 * j);
+            const u4_t x4 = *reinterpret_cast<const u4_t *>(xw + 4 * j);
             const uint32_t w = cw[i][j], w8 = w >> 8;
-            p0 = __builtin_amdgcn_fdot2(nib_lo(w) - zz2, as_h2(xv[0]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_hi16(w) - zz16, as_h2(xv[1]), p1, false);
-            p0 = __builtin_amdgcn_fdot2(nib_lo(w8) - zz2, as_h2(xv[2]), p0, false);
-            p1 = __builtin_amdgcn_fdot2(nib_hi16(w8) - zz16, as_h2(xv[3]), p1, false);
+            p0 = __builtin_amdgcn_fdot2(nib_lo(w), as_h2(x4[0]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_hi16(w), as_h2(x4[1]), p1, false);
+            p0 = __builtin_amdgcn_fdot2(nib_lo(w8), as_h2(x4[2]), p0, false);
+            p1 = __builtin_amdgcn_fdot2(nib_hi16(w8), as_h2(x4[3]), p1, false);
           }
-          p1 *= 0.0625f;
+          acc = fmaf(fmaf(p1, 0.0625f, p0), h2f((uint16_t)sraw[i]), acc);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; j += 2) {
-            const u4_t xv = *reinterpret_cast<const u4_t *>(xw + 2 * j);
+            const u4_t x4 = *reinterpret_cast<const u4_t *>(xw + 2 * j);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
               const uint32_t w = cw[i][j + jj];
-              p0 = __builtin_amdgcn_fdot2(byte_pair_lo(w) - zz2, as_h2(xv[2 * jj]), p0, false);
-              p1 = __builtin_amdgcn_fdot2(byte_pair_hi(w) - zz2, as_h2(xv[2 * jj + 1]), p1, false);
+              p0 = __builtin_amdgcn_fdot2(byte_pair_lo(w), as_h2(x4[2 * jj]), p0, false);
+              p1 = __builtin_amdgcn_fdot2(byte_pair_hi(w), as_h2(x4[2 * jj + 1]), p1, false);
             }
           }
+          acc = fmaf(p0 + p1, h2f((uint16_t)sraw[i]), acc);
         }
-        acc = fmaf(p0 + p1, h2f((uint16_t)sraw[i]), acc);
       }
     }
   }
+
   // lanes sharing a row, then waves, in fixed order
-  if constexpr (Q >= 8) acc += __shfl_xor(acc, 8);
-  if constexpr (Q >= 4) acc += __shfl_xor(acc, 16);
-  if constexpr (Q >= 2) acc += __shfl_xor(acc, 32);
+  if constexpr (Q >= 8) acc += lane_xor_swz<8>(acc);
+  if constexpr (Q >= 4) acc += lane_xor_swz<16>(acc);
+  if constexpr (Q >= 2) acc += lane_xor32(acc, lane);
   red[wave][lane] = acc;
   __syncthreads();
   if (wave != 0) return;
@@ -466,22 +565,12 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
 
   float lora = 0.f;
   if constexpr (LORA != LORA_NONE) {
-    float tv;
-    if constexpr (TMODE == T_INPASS) {
-      tv = tfin[lane & 31];
-    } else {
+    if constexpr (!kTWave) {
       // T from the T-projection launch: FP32 partials per K-part, added in part order
-      tv = sum_parts<8>(p.tin + (size_t)m * kRank + (lane & 31), (size_t)p.tmpad * kRank, p.tparts);
+      const float tv = sum_parts<8>(p.tin + (size_t)m * kRank + (lane & 31), (size_t)p.tmpad * kRank, p.tparts);
+      if (lane < kRank) tfin[lane] = tv;     // read back below by this wave only: LDS order suffices
     }
-#pragma unroll
-    for (int r = 0; r < kRank; ++r) {
-      const float tr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tv), r));
-      float b;
-      if constexpr (LORA == LORA_F16) b = (float)__builtin_bit_cast(_Float16, (uint16_t)(bpk[r / 2] >> (16 * (r & 1))));
-      else b = (float)(int8_t)((bpk[r / 2] >> (16 * (r & 1))) & 0xff);
-      lora = fmaf(tr, b, lora);
-    }
-    if constexpr (LORA == LORA_Q8) lora *= bscale;
+    lora = lora_dot<LORA>(tfin, bpk, bscale);
   }
   if (active) {
     float y = total + lora;
@@ -498,6 +587,8 @@ hipError_t launch5(const GemvParams &p, int lpw, int gx, int gy, size_t lds, hip
     hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 2>), dim3(gx, gy), dim3(nt), 0, s, p);
   else if (lpw <= 4)
     hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 4>), dim3(gx, gy), dim3(nt), 0, s, p);
+  else if (lpw <= 6)
+    hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 6>), dim3(gx, gy), dim3(nt), 0, s, p);
   else
     hipLaunchKernelGGL((gemv_kernel<BITS, HAS_ZP, LORA, TMODE, Q, 8>), dim3(gx, gy), dim3(nt), 0, s, p);
   return hipGetLastError();
@@ -530,7 +621,7 @@ int loads_per_wave(int K, int bits, int q) {
   const int ncc = chunk_cols(bits, K / kBlock);
   const int nloads = (ncc + q - 1) / q;
   const int lpw = (nloads + kWaves - 1) / kWaves;
-  return lpw <= 2 ? 2 : (lpw <= 4 ? 4 : 8);
+  return lpw <= 2 ? 2 : (lpw <= 4 ? 4 : (lpw <= 6 ? 6 : 8));
 }
 
 }  // namespace
