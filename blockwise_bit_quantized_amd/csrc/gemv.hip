@@ -31,10 +31,9 @@
 //    Each slice is written as 32 (value, tag) 64-bit words with device-coherent stores,
 //    where the tag identifies this call (a per-call epoch kept in the workspace, never 0),
 //    into kTReplicas copies, so that the readers spread over many lines.  Each row
-//    workgroup has one extra wave that carries no weight loads: it polls one word of its
-//    copy (the last slice's first word), then reads all the words, accepts them
-//    when every tag matches (no fences: the tags make a stale or early read detectable),
-//    adds the slices in slice order and leaves T in LDS for the epilogue.  The slice
+//    workgroup has one extra wave that carries no weight loads: it reads all the words of
+//    its copy until every tag matches (no fences: the tags make a stale or early read
+//    detectable), adds the slices in slice order and leaves T in LDS for the epilogue.  The slice
 //    workgroups are dispatched first and never wait, so every bounded wait ends.  Every
 //    workgroup reports that it has read the epoch through a two-level count (kDoneGroups
 //    counters, then one) issued right after that read; the last arrival resets the counts
@@ -321,26 +320,20 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
 
   if constexpr (kTWave) {
     if (wave == kWaves) {
-      // T wave: carries no weight loads.  It reads the call epoch and counts itself, polls
-      // one word of its replica of the slices, reads the tagged words of all slices and
-      // leaves T in LDS for the epilogue.  Its loads share the CU's memory pipeline with
-      // the weight stream, so they return behind the workgroup's weight loads.
+      // T wave: carries no weight loads.  It reads the call epoch and counts itself, then
+      // reads the tagged words of all slices of its replica until every tag is this call's,
+      // and leaves T in LDS for the epilogue.  Each read of the words is the poll: a
+      // separate one-word poll before the read cost one more memory round trip between the
+      // slices landing and T being in hand (4096 x 4096 M = 1: 6.87 -> 6.50 us), while the
+      // extra polling traffic (gt x 256 B per read per workgroup) goes to lines that stay
+      // in the device cache.  Its loads share the CU's memory pipeline with the weight
+      // stream, so they return behind the workgroup's weight loads.
       const uint32_t tag = call_tag(__hip_atomic_load((const uint32_t *)&p.ctrl[CTRL_EPOCH], __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT));
       int arrived = 0;
       if (lane == 0) arrived = epoch_arrive(p, blockIdx.x);
       const unsigned long long *rep = p.tword + (size_t)(bid % kTReplicas) * p.gt * kRank;
-      // hint: one lane polls the first word of the last slice (dispatched last, so as a
-      // rule done last); the gather below checks every tag anyway.  A single word per
-      // poll keeps the uncached polling traffic of hundreds of workgroups small.
       int spins = 0;
-      for (; spins < p.spin_limit; ++spins) {
-        const bool seen = lane != 0 ||
-                          (uint32_t)(__hip_atomic_load(rep + (size_t)(p.gt - 1) * kRank, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT) >> 32) == tag;
-        if (__all(seen)) break;
-        __builtin_amdgcn_s_sleep(8);
-      }
       float tv = 0.f;
       bool ok = false;
       for (; spins <= p.spin_limit && !ok; ++spins) {
