@@ -191,6 +191,40 @@ def test_small_shapes_all_paths(bits, zp, adapter):
             compare(run(case, path, flags, pw=pw), ref, what="%s M=%d N=%d K=%d" % (name, M, N, K))
 
 
+# decode shapes for the X-range test: one 64-row group (8 chunk-columns per wave load and a
+# ragged last load at K = 96), ragged K against the load width, the decode width, and a
+# 625-group lm_head-like shape (one chunk-column per wave load); M = 3 takes the small-M path
+X_RANGE_SHAPES = [(1, 64, 96), (1, 200, 1056), (1, 8192, 2080), (1, 40000, 576), (3, 200, 1056)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("zp", [True, False], ids=["zp", "zpdef"])
+@pytest.mark.parametrize("x_std,s_lo,s_hi", [(1e-3, 0.01, 0.02), (30.0, 1e-4, 1e-3)], ids=["small_x", "large_x"])
+def test_decode_x_range(bits, zp, x_std, s_lo, s_hi):
+    """The decode path enters the codes as 1024 + q (and 1024 + 16 q, 1024 + 4^e q for the
+    fields taken in place) and subtracts each block's offset-weighted X sum once, so its
+    block sums pass through values near 1024 * sum(X).  X from 1e-3 to 30 in spread, with
+    one value per 32-k block raised 40-fold (an outlier the block sum carries), against the
+    oracle.  The weight scales are then scaled down (once, as fp16) until the largest output
+    is at most 8, where the fp16 output rounding stays far below the max-abs bar; the
+    adapter (whose T is an ordinary FP32 product) rides along with the small X only."""
+    for i, (M, N, K) in enumerate(X_RANGE_SHAPES):
+        adapter = "f16" if i % 2 and x_std < 1 else None
+        case = si.make_random(300 + i, M, N, K, bits, zp, adapter, s_lo=s_lo, s_hi=s_hi, x_std=x_std)
+        x = case["X"].view(np.float16).astype(np.float32)
+        x[:, 7::32] *= 40.0
+        case["X"] = np.clip(x, -60000, 60000).astype(np.float16).view(np.uint16)
+        ref = oracle.matmul(case)
+        peak = float(np.abs(ref).max())
+        if peak > 8.0:
+            sc = case["scales"].view(np.float16).astype(np.float32) * np.float32(8.0 / peak)
+            case["scales"] = sc.astype(np.float16).view(np.uint16)
+            ref = oracle.matmul(case)
+        pw = dev_weight(case)
+        for path in (0, 1):
+            compare(run(case, path, 0, pw=pw), ref, what="path %d M=%d N=%d K=%d" % (path, M, N, K))
+
+
 SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
 
 
