@@ -136,6 +136,32 @@ class Timer:
             times.append(a.elapsed_time(b) * 1e-3 / n_calls)
         return sorted(times)[2]
 
+    def paired(self, fn_a, fn_b, n_calls):
+        """Seconds per call of fn_a and of fn_b (warm, no rotation): one graph of n_calls calls
+        each, replayed alternately (4 untimed pairs, then 5 timed), so that both see the same
+        clocks and cache state; returns the two medians."""
+        torch = self.torch
+        fn_a(0)
+        fn_b(0)
+        torch.cuda.synchronize()
+        ga, gb = self.capture(fn_a, range(n_calls)), self.capture(fn_b, range(n_calls))
+        for _ in range(4):
+            ga.replay()
+            gb.replay()
+        torch.cuda.synchronize()
+        ta, tb = [], []
+        for _ in range(5):
+            for g, out in ((ga, ta), (gb, tb)):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(self.stream):
+                    a.record()
+                    g.replay()
+                    b.record()
+                torch.cuda.synchronize()
+                out.append(a.elapsed_time(b) * 1e-3 / n_calls)
+        del ga, gb
+        return sorted(ta)[2], sorted(tb)[2]
+
     def per_call(self, fn, n_items, n_calls):
         """Seconds per call of fn(j), n_calls calls per graph.  fn rotates over n_items items
         (cold copies) by j; with more items than calls per graph, consecutive graphs take
@@ -305,6 +331,27 @@ def main():
                           "route": route(case, ad_kind, flags)}
             return s
 
+        def mfma_pair(name, name_empty, case, case_empty, ad_kind, n_calls=50):
+            """The prefill with its adapter and without, timed interleaved (same clocks and
+            cache state), and the adapter's cost as their difference.  Graphs of 50 calls,
+            like the headline's: with the adapter (two launches per call) the time per call
+            still falls with the graph's length (1024x4096x4096: 53 us at 20 calls, 50 at 50,
+            48.7 at 100), without it it is flat from 5 calls on."""
+            pw, ad, X = weight(case), adapter(case), t16(case["X"])
+            M, N, Kc = case["M"], case["N"], case["K"]
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            w = torch.zeros(max(mnb.mnb_workspace_bytes(M, N, Kc, case["bits"], 32), 1), dtype=torch.uint8,
+                            device=dev)
+            sa, sb = timer.paired(lambda j: mnb.matmul(X, pw, ad, out=Y, ws=w),
+                                  lambda j: mnb.matmul(X, pw, None, out=Y, ws=w), n_calls)
+            for nm, sec, kind, r in ((name, sa, ad_kind, 32), (name_empty, sb, 0, 0)):
+                fl = algorithmic_flops(M, N, Kc, r)
+                runs[nm] = {"us": round(sec * 1e6, 3), "TFLOPs": round(fl / sec / 1e12, 2),
+                            "frac": round(fl / sec / 1e12 / FP16_PEAK_TFLOPS, 4), "flops": fl, "cold": False,
+                            "route": route(case if kind else case_empty, kind, 0)}
+            runs[name]["lora_cost_us"] = round((sa - sb) * 1e6, 3)
+            runs[name]["timing"] = "replayed alternately with %s" % name_empty
+
         # every decode and prefill run of the workloads
         c1 = si.make_config(1)
         hbm_run("cfg1_m1", c1, mnb.MNB_ADAPTER_F16, algorithmic_bytes(1, 896, 896, 4, True, 32))
@@ -316,13 +363,13 @@ def main():
                               "frac": round(pre_tflops / FP16_PEAK_TFLOPS, 4), "flops": pflops, "cold": False,
                               "route": pre_route, "note": "headline"}
         mfma_run("cfg3_m256", si.make_config(3, M=256), mnb.MNB_ADAPTER_F16)
-        mfma_run("cfg3_m1024_empty", si.make_config(3, adapter=False), 0)
+        mfma_pair("cfg3_m1024_paired", "cfg3_m1024_empty", pre, si.make_config(3, adapter=False),
+                  mnb.MNB_ADAPTER_F16)
         hbm_run("cfg3_m1", si.make_config(3, M=1), mnb.MNB_ADAPTER_F16, algorithmic_bytes(1, pN, pK, 4, True, 32))
         hbm_run("cfg4_m1", si.make_config(4, M=1), 0, algorithmic_bytes(1, 49152, 576, 8, True, 0))
         hbm_run("cfg4_m8", si.make_config(4, M=8), 0, algorithmic_bytes(8, 49152, 576, 8, True, 0))
-        c5 = si.make_config(5)
-        mfma_run("cfg5_m1024", c5, mnb.MNB_ADAPTER_Q8)
-        mfma_run("cfg5_m1024_empty", si.make_config(5, adapter=False), 0)
+        mfma_pair("cfg5_m1024", "cfg5_m1024_empty", si.make_config(5), si.make_config(5, adapter=False),
+                  mnb.MNB_ADAPTER_Q8)
         # accuracy level 4 (block-quantized activations) at the prefill shape
         mfma_run("cfg3_m1024_acc4", pre, mnb.MNB_ADAPTER_F16, flags=mnb.MNB_FLAG_ACC4)
 
