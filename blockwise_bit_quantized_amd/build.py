@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libmnb.so")
 CEILING_LIB = os.path.join(PKG, "libmnb_ceiling.so")
 CEILING_SOURCE = "ceiling.hip"
 OBJ = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "gemv.hip", "gemv_rows.hip", "gemv_acc4.hip", "tproj.hip", "gemm.hip", "pack.hip"]
+SOURCES = ["api.hip", "gemv.hip", "gemv_mfma.hip", "gemv_acc4.hip", "tproj.hip", "gemm.hip", "pack.hip"]
 ARCH = os.environ.get("MNB_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

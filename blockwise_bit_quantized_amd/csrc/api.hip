@@ -121,13 +121,17 @@ struct Route {
   bool acc4;     // block-quantized int8 activations for the base product
 };
 
-Route route(int M, int lora, const mnb_options *opt) {
+Route route(int M, int K, int lora, const mnb_options *opt) {
   Route r{};
   const int path = opt ? opt->path : MNB_PATH_AUTO;
   const int flags = opt ? opt->flags : 0;
   // automatic rule: the GEMV family for M <= kSmallM (M == 1 decode, the small-M
-  // multi-row variant above it: both stream the weights once), the MFMA GEMM above
+  // matrix-core variant above it: both stream the weights once), the MFMA GEMM above
   r.path = path != MNB_PATH_AUTO ? path : (M <= kSmallM ? MNB_PATH_GEMV : MNB_PATH_GEMM);
+  // the small-M kernel reads X through one 32-bit buffer range: beyond it, the GEMM
+  if (!(flags & MNB_FLAG_ACC4) && r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM &&
+      (long)M * K * 2 > INT_MAX)
+    r.path = MNB_PATH_GEMM;
   r.lora = lora;
   r.tmode = 1;
   r.tproj = false;
@@ -239,11 +243,12 @@ void describe(char *buf, size_t len, int M, int N, int K, int bits, int has_zp, 
     snprintf(buf, len, "%sgemv_acc4_b%d_zp%s_%s grid=%dx%d rows=%d q=%d mr=%d", tp, bits, has_zp ? "x" : "def", ln,
              NG * q, cdiv(M, mr), kGroup / q, q, mr);
   } else if (r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM) {
-    const int NG = cdiv(N, kGroup);
-    const int q = gemv_rows_split(N, false);
-    const int mr = gemv_rows_mr(M, bits);
-    snprintf(buf, len, "%sgemv_rows_b%d_zp%s_%s grid=%dx%d rows=%d q=%d mr=%d", tp, bits, has_zp ? "x" : "def", ln,
-             NG * q, cdiv(M, mr), kGroup / q, q, mr);
+    if (gemv_mfma_wide(M, N, K, bits))
+      snprintf(buf, len, "%sgemv_mfma_wide_b%d_zp%s_%s grid=%d rows=64 mr=%d", tp, bits, has_zp ? "x" : "def", ln,
+               cdiv(N, kGroup), M <= 8 ? 8 : 16);
+    else
+      snprintf(buf, len, "%sgemv_mfma_b%d_zp%s_%s grid=%d rows=16 mr=%d", tp, bits, has_zp ? "x" : "def", ln,
+               cdiv(N, kGroup) * 4, M <= 8 ? 8 : 16);
   } else if (r.path == MNB_PATH_GEMV) {
     const int NG = cdiv(N, kGroup);
     const int extra = (r.lora && r.tmode == 0) ? w.gt : 0;
@@ -392,7 +397,7 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
     snprintf(buf, buf_len, "fill");
     return MNB_OK;
   }
-  describe(buf, buf_len, M, N, K, bits, has_zp, route(M, has_adapter_kind, opt));
+  describe(buf, buf_len, M, N, K, bits, has_zp, route(M, K, has_adapter_kind, opt));
   return MNB_OK;
 }
 
@@ -414,7 +419,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   if (K == 0) return launch_fill(Yh, bh, M, N, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
 
   const int lora = effective_lora(ad);
-  const Route r = route(M, lora, opt);
+  const Route r = route(M, K, lora, opt);
   const WsLayout w = ws_layout(M, N, K, lora ? kRank : 0);
   char *ws = static_cast<char *>(workspace);
   const int NG = cdiv(N, kGroup), KB = K / kBlock;
@@ -491,11 +496,12 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
       return MNB_OK;
     }
     if (M > 1 && M <= kRowsMaxM) {
-      // small M: one pass over the weights for all rows (T from the projection launch)
+      // small M: one pass over the weights for all rows on the matrix cores (T from the
+      // projection launch; route() sends X beyond one 32-bit buffer range to the GEMM)
       p.M = M;
       p.gt = 0;
-      p.q = gemv_rows_split(N, false);
-      if (launch_gemv_rows(bits, lora, p, NG * p.q, s) != hipSuccess) return MNB_ERR_HIP;
+      p.q = 4;
+      if (launch_gemv_mfma(bits, lora, p, s) != hipSuccess) return MNB_ERR_HIP;
       return MNB_OK;
     }
     // rows in chunks that respect the grid's y limit (the in-pass T path has M == 1)

@@ -186,7 +186,9 @@ struct PackParams {
 // Host-side launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_gemv(int bits, bool has_zp, int lora, int tmode, const GemvParams &p,
                        int grid_x, int grid_y, hipStream_t s);
-hipError_t launch_gemv_rows(int bits, int lora, const GemvParams &p, int grid_x, hipStream_t s);
+// small M (2..16) on the matrix cores: 16 weight rows per workgroup, grid 4 * NG
+hipError_t launch_gemv_mfma(int bits, int lora, const GemvParams &p, hipStream_t s);
+bool gemv_mfma_wide(int M, int N, int K, int bits);   // the one-workgroup-per-row-group form
 // accuracy level 4 (int8 block-quantized activations for the base product), any M
 constexpr int kAcc4MaxK = 16384;
 constexpr int kAcc4MultiRowMaxK = 4096;       // K limit of the 4-rows-per-workgroup form
@@ -213,11 +215,11 @@ hipError_t launch_fill(uint16_t *Y, const uint16_t *bias, int M, int N, hipStrea
 // planning helpers shared by the dispatcher and the launchers
 int gemv_rows_split(int N, bool inpass_t);    // q: 1, 2, 4 or 8
 int tproj_parts(int M, int K);                 // K parts of the T projection
-int gemv_rows_mr(int M, int bits);                       // rows per workgroup of the small-M path
-// largest M of the small-M path: measured crossover against the MFMA GEMM (K split over
-// workgroups, 64-row tiles) on the four workload weight sets: the small-M path wins at
-// M <= 4 (by 10-20%, equal on the batched-prefill weights), the GEMM from M = 5
-constexpr int kSmallM = 4;
-constexpr int kRowsMaxM = 16;                  // largest M the multi-row GEMV takes (forced path)
+// largest M of the small-M path (the matrix-core GEMV): measured against the MFMA GEMM (K
+// split over workgroups, 64-row tiles) on the four workload weight sets, cold, it is faster
+// at every M up to 16 (8192 x 2048 int4 + LoRA at M = 8: 10.3 against 15.7 us; 49152 x 576
+// int8: 11.5 against 12.4 us; 9728 x 2560 with INT8 adapters at M = 16: 20.2 against 20.3)
+constexpr int kSmallM = 16;
+constexpr int kRowsMaxM = 16;                  // largest M the small-M path takes (its MFMA's rows)
 
 }  // namespace mnb

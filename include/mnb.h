@@ -201,9 +201,10 @@ int mnb_workspace_error(void *workspace, void *stream);
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
  * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV
- * with T computed in the same launch; 2 <= M <= 4 the T projection, then a GEMV that
- * streams the weights once for all rows; M > 4 the T projection, then the MFMA GEMM with
- * the LoRA term in its epilogue.
+ * with T computed in the same launch; 2 <= M <= 16 the T projection, then a GEMV that
+ * streams the weights once for all rows and multiplies them with the rows on the matrix
+ * cores; M > 16 the T projection, then the MFMA GEMM with the LoRA term in its epilogue.
+ * A forced GEMV path with 2 <= M <= 16 and M * K * 2 > 2^31 - 1 runs the GEMM.
  */
 int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp,
                const mnb_adapter *ad, void *Y, int M, int N, int K, int bits, int block,

@@ -84,7 +84,7 @@ int main() {
   mnb_adapter q8_noscale{MNB_ADAPTER_Q8, 32, A, nullptr, B, nullptr};
   mnb_adapter rank16{MNB_ADAPTER_F16, 16, A, nullptr, B, nullptr};
   mnb_adapter badkind{9, 32, A, nullptr, B, nullptr};
-  mnb_options bad_path{5, 0}, bad_flags{0, 1 << 10}, acc4_gemm{MNB_PATH_GEMM, MNB_FLAG_ACC4};
+  mnb_options bad_path{5, 0}, bad_flags{0, 1 << 10}, acc4_gemv{MNB_PATH_GEMV, MNB_FLAG_ACC4};
   for (int M : {1, 3, 64, 1024})
     for (int N : {1, 70, 4096})
       for (int K : {32, 4096}) {
@@ -119,8 +119,11 @@ int main() {
                MNB_ERR_INVALID_ARG, "path");
         expect(mnb_matmul_bias(X, WQ, SC, ZP, nullptr, nullptr, Y, M, N, K, 4, 32, WS, big, nullptr, &bad_flags),
                MNB_ERR_INVALID_ARG, "flags");
-        expect(mnb_matmul_bias(X, WQ, SC, ZP, nullptr, nullptr, Y, M, N, K, 4, 32, WS, big, nullptr, &acc4_gemm),
-               MNB_ERR_UNSUPPORTED, "ACC4 on the GEMM path");
+        // the GEMV family's LDS holds at most 16384 quantized X values per row (the GEMM
+        // path takes accuracy level 4 at any K)
+        expect(mnb_matmul_bias(X, WQ, SC, ZP, nullptr, nullptr, Y, M, N, K + 16384, 4, 32, WS, big, nullptr,
+                               &acc4_gemv),
+               MNB_ERR_UNSUPPORTED, "ACC4 on the GEMV path past its K limit");
         expect(mnb_matmul_bias(X, WQ, SC, ZP, nullptr, BIAS, Y, 0, N, K, 4, 32, WS, big, nullptr, nullptr), MNB_OK,
                "M == 0");
         expect(mnb_matmul_noalloc(X, WQ, SC, ZP, nullptr, nullptr, Y, M, N, K + 16, 4, 32, nullptr, nullptr),

@@ -212,22 +212,32 @@ def test_accuracy_level4_route_and_validation():
 
 
 def test_dispatcher_rule():
-    # M == 1: decode GEMV with in-pass T; 2 <= M <= 4: the small-M weight-streaming GEMV
-    # after the T projection; M > 4: T projection + MFMA GEMM
+    # M == 1: decode GEMV with in-pass T; 2 <= M <= 16: the small-M matrix-core GEMV after
+    # the T projection (one 64-row group per workgroup when the rows are many and short,
+    # else 16 rows per workgroup); M > 16: T projection + MFMA GEMM
     assert route(1).startswith("gemv_b4_zpx_f16_inpass")
     assert route(1, kind=0).startswith("gemv_b4_zpx_none_base")
-    assert route(2).startswith("tproj_f16") and "gemv_rows_b4_zpx_f16" in route(2) and "mr=4" in route(2)
-    assert "gemv_rows" in route(4) and "mr=4" in route(4)
-    assert route(5).startswith("tproj_f16") and "gemm_b4_zpx_f16" in route(5)
-    assert "gemv_rows" in route(8, path=1) and "mr=8" in route(8, path=1)
-    assert "gemv_rows" in route(16, path=1) and "mr=16" in route(16, path=1)
+    assert route(2).startswith("tproj_f16") and "gemv_mfma_b4_zpx_f16 grid=256 rows=16 mr=8" in route(2)
+    assert "gemv_mfma_b4" in route(5) and "mr=8" in route(5)
+    assert "gemv_mfma_b4" in route(9) and "mr=16" in route(9)
+    assert "gemv_mfma_b4" in route(16) and "mr=16" in route(16)
+    assert route(17).startswith("tproj_f16") and "gemm_b4_zpx_f16" in route(17)
     assert route(1024, kind=2).startswith("tproj_q8") and "gemm_b4_zpx_q8" in route(1024, kind=2)
-    assert route(4, N=49152, K=576, bits=8, kind=0).startswith("gemv_rows_b8_zpx_none")
-    assert route(8, N=49152, K=576, bits=8, kind=0).startswith("gemm_b8_zpx_none")
+    assert route(4, N=49152, K=576, bits=8, kind=0) == "gemv_mfma_wide_b8_zpx_none grid=768 rows=64 mr=8"
+    assert route(16, N=49152, K=576, bits=8, kind=0) == "gemv_mfma_wide_b8_zpx_none grid=768 rows=64 mr=16"
+    # the wide form needs >= 256 row groups, <= 16 wave loads per row and X within 64 KiB
+    assert "gemv_mfma_b8" in route(8, N=16320, K=576, bits=8, kind=0)        # 255 row groups
+    assert "gemv_mfma_wide_b8" in route(8, N=16321, K=576, bits=8, kind=0)   # 256
+    assert "gemv_mfma_b4" in route(8, N=49152, K=2080, bits=4, kind=0)       # 17 wave loads
+    assert "gemv_mfma_wide_b2" in route(8, N=49152, K=2048, bits=2, kind=0)
+    assert "gemv_mfma_b2" in route(16, N=49152, K=2048, bits=2, kind=0)      # X staging 72 KiB
+    # X past one 32-bit buffer range (M * K * 2 > 2^31 - 1) goes to the GEMM, forced or not
+    assert "gemm" in route(16, K=1 << 26) and "gemm" in route(16, K=1 << 26, path=1)
+    assert "gemv_mfma" in route(15, K=1 << 26, path=1)
     # overrides, as the pages keep explicit path overrides for comparisons
     assert route(1, path=2).startswith("tproj_f16") and "gemm" in route(1, path=2)
     assert route(7, path=2).startswith("tproj_f16") and "gemm" in route(7, path=2)
-    assert route(7, path=1).startswith("tproj_f16") and "gemv_rows_b4_zpx_f16" in route(7, path=1)
+    assert route(7, path=1).startswith("tproj_f16") and "gemv_mfma_b4_zpx_f16" in route(7, path=1)
     assert route(40, path=1).startswith("tproj_f16") and "gemv_b4_zpx_f16_tprecomp" in route(40, path=1)
     assert "tprecomp" in route(1, flags=1) and route(1, flags=1).startswith("tproj")
     assert route(0) == "noop" and route(3, K=0) == "fill"

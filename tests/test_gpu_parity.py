@@ -225,6 +225,29 @@ def test_decode_x_range(bits, zp, x_std, s_lo, s_hi):
             compare(run(case, path, 0, pw=pw), ref, what="path %d M=%d N=%d K=%d" % (path, M, N, K))
 
 
+# small-M matrix-core GEMV, both forms: 16 rows per workgroup (8 waves splitting K), and one
+# 64-row group per workgroup when the rows are many and short (>= 256 row groups, <= 16 wave
+# loads per row); ragged N (last row group partial) and K (wave loads past the row), X rows
+# 2..16 (the MFMA's rows past M padded)
+SMALL_M_SHAPES = [(2, 200, 1056), (5, 130, 96), (9, 16400, 576), (16, 16400, 160), (3, 20000, 2080)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("zp", [True, False], ids=["zp", "zpdef"])
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_small_m_matrix_core_forms(bits, zp, adapter):
+    forms = set()
+    for i, (M, N, K) in enumerate(SMALL_M_SHAPES):
+        case = si.make_random(500 + i, M, N, K, bits, zp, adapter)
+        kind = {None: 0, "f16": 1, "q8": 2}[adapter]
+        st, text = mnb.mnb_describe_route(M, N, K, bits, int(zp), kind, None)
+        assert st == 0 and "gemv_mfma" in text, text
+        forms.add("wide" in text)
+        ref = oracle.matmul(case)
+        compare(run(case, 0, 0), ref, what="%s M=%d N=%d K=%d" % (text, M, N, K))
+    assert forms == {True, False}, "both forms exercised"
+
+
 SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
 
 
