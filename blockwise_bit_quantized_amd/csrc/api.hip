@@ -128,10 +128,8 @@ Route route(int M, int K, int lora, const mnb_options *opt) {
   // automatic rule: the GEMV family for M <= kSmallM (M == 1 decode, the small-M
   // matrix-core variant above it: both stream the weights once), the MFMA GEMM above
   r.path = path != MNB_PATH_AUTO ? path : (M <= kSmallM ? MNB_PATH_GEMV : MNB_PATH_GEMM);
-  // the small-M kernel reads X through one 32-bit buffer range: beyond it, the GEMM
-  if (!(flags & MNB_FLAG_ACC4) && r.path == MNB_PATH_GEMV && M > 1 && M <= kRowsMaxM &&
-      (long)M * K * 2 > INT_MAX)
-    r.path = MNB_PATH_GEMM;
+  // the small-M kernel reads all of X through one 32-bit buffer range
+  static_assert((long)kRowsMaxM * kMaxK * 2 <= INT_MAX, "X of the small-M kernel exceeds one buffer range");
   r.lora = lora;
   r.tmode = 1;
   r.tproj = false;

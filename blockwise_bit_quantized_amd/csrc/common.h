@@ -204,9 +204,10 @@ int gemm_splits(int M, int N, int K);         // K ranges per output tile of the
 int gemm_tail_splits(int M, int N, int K, int *tail0);
 int gemm_bm(int M, int N);                    // tile rows of the prefill GEMM (64 or 128)
 constexpr int kMaxSplits = 16;
-// K limit: the GEMM's direct loads address X as a uniform row base plus a 32-bit lane
-// offset of up to 7 rows (7 * 2K + 112 bytes)
-constexpr int kMaxK = 1 << 28;
+// K limit: the GEMM's direct loads go through buffer descriptors whose 32-bit offsets reach
+// one packed row group's codes (8-bit: 64 K bytes) and, for X, up to 8 rows (16 K + 112
+// bytes); both stay below 2^31 - 1 for K < 2^25
+constexpr int kMaxK = 1 << 25;
 hipError_t launch_pack(int bits, bool kn, const PackParams &p, hipStream_t s);  // kn: [K, N] source
 hipError_t launch_unpack(int bits, const PackParams &p, uint8_t *codes, uint16_t *scales,
                          uint8_t *zp, hipStream_t s);

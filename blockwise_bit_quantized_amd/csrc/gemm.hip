@@ -78,6 +78,18 @@ __device__ __forceinline__ void dma(const void *src, uint8_t *dst, int size) {
   if (size == 16) __builtin_amdgcn_global_load_lds(src, d, 16, 0, 0);
   else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
 }
+// The same through a buffer descriptor: address = descriptor base + soff (SGPR, per step) +
+// voff (VGPR, loop-invariant), so a step costs no vector address arithmetic.  The
+// descriptors here span 2^31 - 1 bytes: every address is valid by construction, no range
+// check is relied on.
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *dst, int size) {
+  lds_void *d = (lds_void *)(dst);
+  if (size == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 16, voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, d, 4, voff, soff, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wide_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
+}
 
 // s_waitcnt with vmcnt = N (gfx9 encoding: vmcnt bits 3:0 and 15:14), other counters free
 template <int N>
@@ -168,7 +180,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   // X chunk load q of this wave covers tile rows r0 = (BMT/4) wave + 8 q .. r0 + 7 (8 lanes
   // per row): uniform base row min(m0 + r0, M - 1); lane offset = (its row, clamped to
   // M - 1, minus the base row) * 2K bytes + 16 c, with chunk c = position ^ ((r >> 1) & 7)
-  // of the swizzle (at most 7 * 2K + 112 bytes: K < 2^28 is checked by the host)
+  // of the swizzle (at most 7 * 2K + 112 bytes; K < 2^25 is checked by the host)
   const uint8_t *X = reinterpret_cast<const uint8_t *>(p.X);
   const uint8_t *xrow[XQ];
   uint32_t xoff[XQ], xoffr[XQ];
@@ -184,43 +196,49 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     // (c >= 4) re-read the first block (any valid address; the block's scales are 0)
     xoffr[q] = xoff[q] - (c >= 4 ? 64u : 0u);
   }
+  __amdgpu_buffer_rsrc_t xr[XQ];
+#pragma unroll
+  for (int q = 0; q < XQ; ++q) xr[q] = wide_rsrc(xrow[q]);
   auto issue_x = [&](int step, int slot, int half) {
     const int sv = sbase + (step < nsteps ? step : nsteps - 1);   // past the end: a valid address
     const bool ragged = 2 * sv + 1 >= p.KB;
     uint8_t *base = smem + slot * SL::kBytes;
+    const uint32_t so = (uint32_t)sv * BK * 2;
     if (ragged) {
 #pragma unroll
       for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q)
-        dma(xrow[q] + (size_t)sv * BK * 2 + xoffr[q], base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
+        dma_buf(xr[q], xoffr[q], so, base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
     } else {
 #pragma unroll
       for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q)
-        dma(xrow[q] + (size_t)sv * BK * 2 + xoff[q], base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
+        dma_buf(xr[q], xoff[q], so, base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
     }
   };
-  // per-lane byte offsets of the weight loads (uniform bases are per step)
+  // per-lane byte offsets of the weight loads; descriptors based at this wave's packed row
+  // group (row group 0 when the group lies past N: any valid address, never used)
   const uint32_t lo16 = (uint32_t)lane * 16u, lo_sc = (uint32_t)l32 * 4u;
   const uint32_t lo_zp = 4u * (uint32_t)(BITS == 2 ? (lane & 3) : BITS == 4 ? (lane & 7) : (lane & 15));
+  constexpr int kZpB = BITS == 2 ? 16 : BITS == 4 ? 32 : kGroup;   // zero-point bytes per block
+  const size_t wgb = wrow_ok ? (size_t)wg : 0;
+  const auto wr = wide_rsrc(p.wq + wgb * (BITS == 2 ? (size_t)tsteps : (size_t)p.KB * C) * kGroup * 16);
+  const auto sr = wide_rsrc(reinterpret_cast<const uint8_t *>(p.sc) + wgb * p.KB * kGroup * 2);
+  const auto zr = wide_rsrc(HAS_ZP ? p.zp + wgb * p.KB * kZpB : p.wq);
   auto issue_w = [&](int step, int slot) {
     const int sv = sbase + (step < nsteps ? step : nsteps - 1);
     uint8_t *base = smem + slot * SL::kBytes;
     const int kb = 2 * sv + kh;
     const bool ok = wrow_ok && kb < p.KB;
-    const size_t t = ok ? (size_t)wg * p.KB + kb : 0;
+    const uint32_t kbo = ok ? (uint32_t)kb : 0u;
     if constexpr (BITS == 2) {
       // one chunk holds both blocks of the step (each wave uses its half)
-      const size_t ch = wrow_ok ? (size_t)wg * tsteps + sv : 0;
-      dma(p.wq + ch * kGroup * 16 + lo16, base + SL::kCodes + wave * SL::kCodesWave, 16);
+      dma_buf(wr, lo16, wrow_ok ? (uint32_t)sv * kGroup * 16 : 0u, base + SL::kCodes + wave * SL::kCodesWave, 16);
     } else {
 #pragma unroll
       for (int c = 0; c < C; ++c)
-        dma(p.wq + (t * C + c) * kGroup * 16 + lo16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+        dma_buf(wr, lo16, (kbo * C + c) * kGroup * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
     }
-    dma(reinterpret_cast<const uint8_t *>(p.sc + t * kGroup) + lo_sc, base + SL::kScale + wave * 256, 4);
-    if constexpr (HAS_ZP) {
-      const uint8_t *zrow = BITS == 2 ? p.zp + t * 16 : BITS == 4 ? p.zp + t * 32 : p.zp + t * kGroup;
-      dma(zrow + lo_zp, base + SL::kZp + wave * 256, 4);
-    }
+    dma_buf(sr, lo_sc, kbo * kGroup * 2, base + SL::kScale + wave * 256, 4);
+    if constexpr (HAS_ZP) dma_buf(zr, lo_zp, kbo * kZpB, base + SL::kZp + wave * 256, 4);
   };
   auto issue = [&](int step, int slot) {
     issue_x(step, slot, 0);
@@ -270,9 +288,11 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     uint32_t z = 1u << (BITS - 1);
     if constexpr (HAS_ZP)
       z = BITS == 2 ? (rw.zb[nb] >> ((r & 3) * 2)) & 3u : BITS == 4 ? (rw.zb[nb] >> ((r & 1) * 4)) & 0xFu : rw.zb[nb];
-    // binary16 of 1024 + z is 0x6400 | z (z < 1024): both halves at once
-    const h2_t zz2 = as_h2((z * 0x00010001u) | 0x64006400u);
-    const h2_t s2 = as_h2((wok ? rw.sraw[nb] : 0u) * 0x00010001u);
+    // binary16 of 1024 + z is 0x6400 | z (z < 1024): both halves at once, one v_perm_b32
+    // (bytes z, 0x64, z, 0x64; 8-bit z up to 255 sits in the low byte alone)
+    const h2_t zz2 = as_h2(__builtin_amdgcn_perm(0x64646464u, z, 0x04000400u));
+    // the scale in both halves (bytes 0, 1, 0, 1 of the raw word), 0 past K
+    const h2_t s2 = as_h2(__builtin_amdgcn_perm(0u, wok ? rw.sraw[nb] : 0u, 0x01000100u));
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if constexpr (BITS == 2) {
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
         // exact and so is the small integer result.  Both kinds are then multiplied by the
         // same s, so each weight is (q - z) s rounded once, for every finite scale
         // (subnormal ones included).
-        const h2_t nz64 = as_h2(((z << 4) * 0x00010001u) | 0xD400D400u);   // -(64 + z), both halves
+        const h2_t nz64 = h2_t{(_Float16)960.f, (_Float16)960.f} - zz2;   // 960 - (1024 + z) = -(64 + z), exact
         const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         const uint32_t w = rw.cw[nb][kk];
         const uint32_t w8 = w >> 8;

@@ -45,7 +45,7 @@ extern "C" {
 enum {
   MNB_OK = 0,
   MNB_ERR_INVALID_ARG = 1,  /* negative size, NULL required pointer, bad enum */
-  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, K >= 2^28, rank not 0/32,
+  MNB_ERR_UNSUPPORTED = 2,  /* bits not 2/4/8, block not 32, K % 32 != 0, K >= 2^25, rank not 0/32,
                                or a launch grid past INT_MAX: ceil(M/64) * ceil(N/128) * 16 or
                                ceil(M/32) * ceil(K/256) */
   MNB_ERR_MISALIGNED = 3,   /* a tensor pointer is not 16-byte aligned */
@@ -169,7 +169,7 @@ int mnb_unpack(const void *wq, const void *sc, const void *zpp, int N, int K, in
  * Workspace bytes needed by mnb_matmul / mnb_matmul_ex for these sizes, for any path, any
  * adapter kind and any flags (host only).  No page defines a workspace: it is this library's own
  * scratch, passed in by the caller so that the library allocates nothing.  Returns 0 for
- * M or N <= 0 and for sizes every call rejects (K % 32 != 0, K >= 2^28, grids past INT_MAX).  The workspace holds partial sums (among them the prefill
+ * M or N <= 0 and for sizes every call rejects (K % 32 != 0, K >= 2^25, grids past INT_MAX).  The workspace holds partial sums (among them the prefill
  * GEMM's FP32 partial outputs when it splits K over several workgroups per output tile),
  * the LoRA down-projection T, accuracy level 4's block-quantized X for the GEMM path
  * (fp16 [M, K]) and a few counters.  It must be ZERO-FILLED before its first use; every call that
@@ -197,14 +197,13 @@ int mnb_workspace_error(void *workspace, void *stream);
  *   ad     adapter or NULL (see mnb_adapter for when it counts as empty)
  *   Y      fp16 [M, N] row-major; must not overlap X, wq, sc, zpp, the adapter or the
  *          workspace (MNB_ERR_ALIAS)
- *   bits 2, 4 or 8, block 32, K % 32 == 0, K < 2^28
+ *   bits 2, 4 or 8, block 32, K % 32 == 0, K < 2^25
  *   workspace, ws_bytes   see mnb_workspace_bytes
  * M == 0 or N == 0: nothing is enqueued, MNB_OK.  K == 0: Y is filled with zeros.
  * Path (PR #33370 commit list, auto mode by the row count M): M == 1 runs the decode GEMV
  * with T computed in the same launch; 2 <= M <= 16 the T projection, then a GEMV that
  * streams the weights once for all rows and multiplies them with the rows on the matrix
  * cores; M > 16 the T projection, then the MFMA GEMM with the LoRA term in its epilogue.
- * A forced GEMV path with 2 <= M <= 16 and M * K * 2 > 2^31 - 1 runs the GEMM.
  */
 int mnb_matmul(const void *X, const void *wq, const void *sc, const void *zpp,
                const mnb_adapter *ad, void *Y, int M, int N, int K, int bits, int block,

@@ -37,7 +37,7 @@ int main() {
                       1024, 2048, 2560, 4096, 8192, 9728, 49152, 65535, 65536, 1 << 20, 1 << 24, INT_MAX / 2,
                       INT_MAX - 63, INT_MAX};
   const int ks[] = {0, 32, 64, 96, 160, 576, 896, 1024, 2048, 2560, 4096, 8192, 16384, 16416, 1 << 20,
-                    (1 << 28) - 32, 1 << 28, INT_MAX - 31, -32};
+                    (1 << 25) - 32, 1 << 25, (1 << 28) - 32, 1 << 28, INT_MAX - 31, -32};
   const int bits_list[] = {2, 4, 8, 3};
   char buf[256];
 

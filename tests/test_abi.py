@@ -59,8 +59,8 @@ def test_packed_sizes_rejects():
     assert mnb.mnb_packed_sizes(64, 33, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
     assert mnb.mnb_packed_sizes(64, 64, 3, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
     assert mnb.mnb_packed_sizes(64, 64, 4, 64, 0)[0] == mnb.MNB_ERR_UNSUPPORTED
-    assert mnb.mnb_packed_sizes(64, 1 << 28, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED   # K < 2^28
-    assert mnb.mnb_packed_sizes(64, (1 << 28) - 32, 4, 32, 0)[0] == mnb.MNB_OK
+    assert mnb.mnb_packed_sizes(64, 1 << 25, 4, 32, 0)[0] == mnb.MNB_ERR_UNSUPPORTED   # K < 2^25
+    assert mnb.mnb_packed_sizes(64, (1 << 25) - 32, 4, 32, 0)[0] == mnb.MNB_OK
     assert mnb.mnb_packed_sizes(-1, 64, 4, 32, 0)[0] == mnb.MNB_ERR_INVALID_ARG
 
 
@@ -88,7 +88,7 @@ def test_validation_status_codes():
     assert call(bits=3) == E.MNB_ERR_UNSUPPORTED
     assert call(block=64) == E.MNB_ERR_UNSUPPORTED
     assert call(K=48) == E.MNB_ERR_UNSUPPORTED
-    assert call(K=1 << 28) == E.MNB_ERR_UNSUPPORTED
+    assert call(K=1 << 25) == E.MNB_ERR_UNSUPPORTED
     assert call(M=-1) == E.MNB_ERR_INVALID_ARG
     assert call(N=-5) == E.MNB_ERR_INVALID_ARG
     assert call(x=None) == E.MNB_ERR_INVALID_ARG
@@ -231,9 +231,8 @@ def test_dispatcher_rule():
     assert "gemv_mfma_b4" in route(8, N=49152, K=2080, bits=4, kind=0)       # 17 wave loads
     assert "gemv_mfma_wide_b2" in route(8, N=49152, K=2048, bits=2, kind=0)
     assert "gemv_mfma_b2" in route(16, N=49152, K=2048, bits=2, kind=0)      # X staging 72 KiB
-    # X past one 32-bit buffer range (M * K * 2 > 2^31 - 1) goes to the GEMM, forced or not
-    assert "gemm" in route(16, K=1 << 26) and "gemm" in route(16, K=1 << 26, path=1)
-    assert "gemv_mfma" in route(15, K=1 << 26, path=1)
+    # at the largest K every small-M X still fits one 32-bit buffer range (16 * 2K < 2^31)
+    assert "gemv_mfma_b4" in route(16, K=(1 << 25) - 32) and "gemv_mfma" in route(15, K=(1 << 25) - 32, path=1)
     # overrides, as the pages keep explicit path overrides for comparisons
     assert route(1, path=2).startswith("tproj_f16") and "gemm" in route(1, path=2)
     assert route(7, path=2).startswith("tproj_f16") and "gemm" in route(7, path=2)
