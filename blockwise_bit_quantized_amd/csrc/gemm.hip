@@ -39,6 +39,7 @@
 // The finished tile is staged in LDS and stored by all four waves as whole row pieces
 // (16 bytes per lane, 256 contiguous bytes per row), not as the accumulator layout's
 // 16 bytes in each of 32 rows.
+#include <type_traits>
 #include "common.h"
 
 namespace mnb {
@@ -71,15 +72,10 @@ struct Lds {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-// direct-to-LDS load of 16 or 4 bytes per lane (lane i lands at dst + i * size); a plain
-// device function, so kernel templates instantiate for the host pass as well
-__device__ __forceinline__ void dma(const void *src, uint8_t *dst, int size) {
-  lds_void *d = (lds_void *)(dst);
-  if (size == 16) __builtin_amdgcn_global_load_lds(src, d, 16, 0, 0);
-  else __builtin_amdgcn_global_load_lds(src, d, 4, 0, 0);
-}
-// The same through a buffer descriptor: address = descriptor base + soff (SGPR, per step) +
-// voff (VGPR, loop-invariant), so a step costs no vector address arithmetic.  The
+// Direct-to-LDS load of 16 or 4 bytes per lane (lane i lands at dst + i * size) through a
+// buffer descriptor: address = descriptor base + soff (SGPR, per step) + voff (VGPR,
+// loop-invariant), so a step costs no vector address arithmetic.  A plain device function,
+// so kernel templates instantiate for the host pass as well.  The
 // descriptors here span 2^31 - 1 bytes: every address is valid by construction, no range
 // check is relied on.
 __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t *dst, int size) {
@@ -495,22 +491,37 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   wait_vmcnt<0>();                        // the trailing loads into free slots are done
   lds_barrier();
 
-  // ---- the kh = 1 wave of each column half hands its partial to the kh = 0 wave ----
+  // ---- epilogue: the two waves of a column half (kh = 0, 1) hold K-half partials of the
+  // same 64 columns over all tile rows.  Each keeps half of the row blocks (own: kh MBH ..
+  // kh MBH + MBH - 1) and hands the other half to its partner (wave ^ 2) through LDS, so
+  // both finish, convert and store a quarter of the tile. ----
+  // Accumulator register v of block [mb][nb] holds tile row 32 mb + lane % 32 and tile
+  // column 64 nh + 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4 (the MFMAs computed Y^T blocks,
+  // weights as the row operand): four consecutive columns per register quad.
+  constexpr int MBH = MB / 2;
+  constexpr int kGive = MBH * 2 * 4;         // float4 per lane handed over (MBH blocks x 2 nb x 4)
   float4 *red = reinterpret_cast<float4 *>(smem);
-  if (kh == 1) {
+  static_assert(4 * kGive * 64 * 16 <= Lds<BMT, C>::kRed, "handed-over partials fit their region");
+  // (the block offsets are compile-time constants in both instances, so the accumulators
+  // stay in registers)
+  auto give = [&](auto give_c) {
+    constexpr int give0 = decltype(give_c)::value;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int b = 0; b < MBH; ++b)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4)
-          red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane] =
-              float4{acc[mb][nb][4 * v4], acc[mb][nb][4 * v4 + 1], acc[mb][nb][4 * v4 + 2], acc[mb][nb][4 * v4 + 3]};
-  }
+          red[(wave * kGive + (b * 2 + nb) * 4 + v4) * 64 + lane] =
+              float4{acc[give0 + b][nb][4 * v4], acc[give0 + b][nb][4 * v4 + 1], acc[give0 + b][nb][4 * v4 + 2],
+                     acc[give0 + b][nb][4 * v4 + 3]};
+  };
+  if (kh == 0) give(std::integral_constant<int, MBH>{});
+  else give(std::integral_constant<int, 0>{});
   _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
   _Float16 *sB = sT + BMT * LDT;
   if (lora_here) {
-    // epilogue operands: T tile [128 m][32 r] (fp16, rounded once from the FP32 sum) and
+    // epilogue operands: T tile [BMT m][32 r] (fp16, rounded once from the FP32 sum) and
     // the B tile transposed to [128 n][32 r]
     u4_t o[2];
 #pragma unroll
@@ -546,137 +557,132 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     }
   }
   __syncthreads();
-  if (kh == 0) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const float4 o = red[((nh * (8 * MB) + (mb * 2 + nb) * 4 + v4) * 64) + lane];
-          acc[mb][nb][4 * v4] += o.x;
-          acc[mb][nb][4 * v4 + 1] += o.y;
-          acc[mb][nb][4 * v4 + 2] += o.z;
-          acc[mb][nb][4 * v4 + 3] += o.w;
-        }
 
+  // own row blocks: + the LoRA term (two MFMA k-steps of 16 over the rank), then + the
+  // partner's partial; the sum is ((own K half + T B) + other K half) in FP32
+  const int own0 = kh * MBH;
+  float y[MBH][2][16];
+  const float4 *mine = red + (size_t)(wave ^ 2) * kGive * 64;   // the partner's hand-over
+  auto finish = [&](auto own_c) {
+    constexpr int ob = decltype(own_c)::value;   // first own block
     if (lora_here) {
       const int akof = 8 * hi;
 #pragma unroll
       for (int kk = 0; kk < kRank / 16; ++kk) {
-        h8_t af[MB], bf[2];
+        h8_t af[MBH], bf[2];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          af[mb] = *reinterpret_cast<const h8_t *>(&sT[(mb * 32 + l32) * LDT + kk * 16 + akof]);
+        for (int b = 0; b < MBH; ++b)
+          af[b] = *reinterpret_cast<const h8_t *>(&sT[((ob + b) * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
           bf[nb] = *reinterpret_cast<const h8_t *>(&sB[(nh * 64 + nb * 32 + l32) * LDT + kk * 16 + akof]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int b = 0; b < MBH; ++b)
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[mb], acc[mb][nb], 0, 0, 0);
+            acc[ob + b][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[b], acc[ob + b][nb], 0, 0, 0);
       }
     }
-  }
-  __syncthreads();   // the partials and the epilogue operands are consumed
+#pragma unroll
+    for (int b = 0; b < MBH; ++b)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const float4 o = mine[((b * 2 + nb) * 4 + v4) * 64 + lane];
+          y[b][nb][4 * v4] = acc[ob + b][nb][4 * v4] + o.x;
+          y[b][nb][4 * v4 + 1] = acc[ob + b][nb][4 * v4 + 1] + o.y;
+          y[b][nb][4 * v4 + 2] = acc[ob + b][nb][4 * v4 + 2] + o.z;
+          y[b][nb][4 * v4 + 3] = acc[ob + b][nb][4 * v4 + 3] + o.w;
+        }
+  };
+  if (kh == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, MBH>{});
 
-  // ---- the finished tile goes through LDS so that all four waves store whole rows ----
-  // The MFMAs computed Y^T blocks (weights as the row operand), so accumulator register v
-  // of block [mb][nb] holds tile row 32 mb + lane % 32 and tile column
-  // 64 nh + 32 nb + 8 (v / 4) + 4 (lane / 32) + v % 4: four consecutive columns per
-  // register quad.  The kh = 0 waves write the tile to LDS (padded rows), then every thread
-  // copies 16 contiguous bytes of a row, so a store instruction covers whole 256-byte (fp16)
-  // or 512-byte (FP32) row pieces instead of 16 bytes in each of 32 rows.
-  constexpr int kPitchH = BN + 8;    // halfs per LDS row of the fp16 tile (rows stay 16-byte aligned)
-  constexpr int kPitchF = BN + 4;    // floats per LDS row of the FP32 partial tile
-  static_assert(BMT * kPitchF * 4 <= kLdsBytes, "the staged output tile fits the ring");
+  // The partner's hand-over region is read by this wave alone, and its reads precede
+  // these writes in LDS order: it stages this wave's quarter of the tile (MBH 32 rows x 64
+  // columns), which the wave then stores as whole row pieces.  16-byte chunks are swizzled
+  // by row so that the 32 rows of one write spread over the banks.
+  uint8_t *stage = reinterpret_cast<uint8_t *>(smem) + (size_t)(wave ^ 2) * kGive * 64 * 16;
+  const int mrow0 = m0 + own0 * 32;          // first tile row of this wave's quarter
+  const int ncol0 = n0 + nh * 64;            // first column
   if (nranges > 1) {
-    // this K range's FP32 partial; the reduction launch adds the ranges in order
-    float *tileF = reinterpret_cast<float *>(smem);
-    if (kh == 0) {
+    // this K range's FP32 partial (256-byte rows, 16 chunks); the reduction launch adds the
+    // ranges in order, and the bias
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+    for (int b = 0; b < MBH; ++b)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            *reinterpret_cast<float4 *>(&tileF[(mb * 32 + l32) * kPitchF + nh * 64 + nb * 32 + 8 * j + 4 * hi]) =
-                float4{acc[mb][nb][4 * j], acc[mb][nb][4 * j + 1], acc[mb][nb][4 * j + 2], acc[mb][nb][4 * j + 3]};
-    }
-    __syncthreads();
-    const int c4 = tid & 31;                 // 16-byte chunk of a 512-byte row
+        for (int j = 0; j < 4; ++j) {
+          const int r = b * 32 + l32, ch = 8 * nb + 2 * j + hi;
+          *reinterpret_cast<float4 *>(stage + r * 256 + ((ch ^ (r & 15)) << 4)) =
+              float4{y[b][nb][4 * j], y[b][nb][4 * j + 1], y[b][nb][4 * j + 2], y[b][nb][4 * j + 3]};
+        }
+    const int c16 = lane & 15;
+    float *dst0;
+    size_t pitch;
     if (tailw) {
       // tail tile: the whole BMT x 128 partial, compact (rows and columns past M and N are
       // written too and never read)
-      float *tp = p.ypart + ((size_t)ks * (ntiles - p.tail0) + (tile - p.tail0)) * (BMT * BN);
-#pragma unroll
-      for (int pass = 0; pass < BMT / 8; ++pass) {
-        const int row = pass * 8 + (tid >> 5);
-        *reinterpret_cast<float4 *>(tp + row * BN + 4 * c4) =
-            *reinterpret_cast<const float4 *>(&tileF[row * kPitchF + 4 * c4]);
-      }
-      return;
+      dst0 = p.ypart + ((size_t)ks * (ntiles - p.tail0) + (tile - p.tail0)) * (BMT * BN) + (size_t)own0 * 32 * BN +
+             nh * 64;
+      pitch = BN;
+    } else {
+      dst0 = p.ypart + (size_t)ks * p.M * p.N + (size_t)mrow0 * p.N + ncol0;
+      pitch = p.N;
     }
-    float *part = p.ypart + (size_t)ks * p.M * p.N;
-    const bool vec = (p.N & 3) == 0;
+    const bool vec = tailw || (p.N & 3) == 0;
 #pragma unroll
-    for (int pass = 0; pass < BMT / 8; ++pass) {
-      const int row = pass * 8 + (tid >> 5);
-      const int m = m0 + row;
-      const int n = n0 + 4 * c4;
-      if (m >= p.M || n >= p.N) continue;
-      const float4 v = *reinterpret_cast<const float4 *>(&tileF[row * kPitchF + 4 * c4]);
-      float *dst = part + (size_t)m * p.N + n;
-      if (vec && n + 4 <= p.N) {
+    for (int pass = 0; pass < MBH * 8; ++pass) {
+      const int r = pass * 4 + (lane >> 4);
+      const float4 v = *reinterpret_cast<const float4 *>(stage + r * 256 + ((c16 ^ (r & 15)) << 4));
+      if (!tailw && (mrow0 + r >= p.M || ncol0 + 4 * c16 >= p.N)) continue;
+      float *dst = dst0 + (size_t)r * pitch + 4 * c16;
+      if (vec && (tailw || ncol0 + 4 * c16 + 4 <= p.N)) {
         *reinterpret_cast<float4 *>(dst) = v;
       } else {
         const float e4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (n + e < p.N) dst[e] = e4[e];
+          if (ncol0 + 4 * c16 + e < p.N) dst[e] = e4[e];
       }
     }
     return;
   }
-  uint16_t *tileH = reinterpret_cast<uint16_t *>(smem);
-  if (kh == 0) {
-    // broadcast bias of this lane's columns, added in FP32 before the rounding
-    float bv[2][4][4];
+  // whole K: + bias in FP32, one rounding to fp16 (128-byte rows, 8 chunks)
+  if (p.bias) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = n0 + nh * 64 + nb * 32 + 8 * j + 4 * hi + e;
-          bv[nb][j][e] = (p.bias && n < p.N) ? h2f(p.bias[n]) : 0.f;
-        }
+          const int n = ncol0 + nb * 32 + 8 * j + 4 * hi + e;
+          const float bv = n < p.N ? h2f(p.bias[n]) : 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = p.bias ? acc[mb][nb][4 * j + e] + bv[nb][j][e] : acc[mb][nb][4 * j + e];
-          const h2_t lo = {(_Float16)y[0], (_Float16)y[1]};
-          const h2_t hi2 = {(_Float16)y[2], (_Float16)y[3]};
-          *reinterpret_cast<u2_t *>(&tileH[(mb * 32 + l32) * kPitchH + nh * 64 + nb * 32 + 8 * j + 4 * hi]) =
-              u2_t{as_u32(lo), as_u32(hi2)};
+          for (int b = 0; b < MBH; ++b) y[b][nb][4 * j + e] += bv;
         }
   }
-  __syncthreads();
-  const bool vec = (p.N & 7) == 0;
-  const int c8 = tid & 15;                   // 16-byte chunk of a 256-byte row
 #pragma unroll
-  for (int pass = 0; pass < BMT / 16; ++pass) {
-    const int row = pass * 16 + (tid >> 4);
-    const int m = m0 + row;
-    const int n = n0 + 8 * c8;
+  for (int b = 0; b < MBH; ++b)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = b * 32 + l32, ch = 4 * nb + j;
+        const h2_t lo = {(_Float16)y[b][nb][4 * j], (_Float16)y[b][nb][4 * j + 1]};
+        const h2_t hi2 = {(_Float16)y[b][nb][4 * j + 2], (_Float16)y[b][nb][4 * j + 3]};
+        *reinterpret_cast<u2_t *>(stage + r * 128 + ((ch ^ (r & 7)) << 4) + 8 * hi) = u2_t{as_u32(lo), as_u32(hi2)};
+      }
+  const bool vec = (p.N & 7) == 0;
+  const int c8 = lane & 7;
+#pragma unroll
+  for (int pass = 0; pass < MBH * 4; ++pass) {
+    const int r = pass * 8 + (lane >> 3);
+    const int m = mrow0 + r, n = ncol0 + 8 * c8;
+    const u4_t v = *reinterpret_cast<const u4_t *>(stage + r * 128 + ((c8 ^ (r & 7)) << 4));
     if (m >= p.M || n >= p.N) continue;
-    const u4_t v = *reinterpret_cast<const u4_t *>(&tileH[row * kPitchH + 8 * c8]);
     uint16_t *dst = p.Y + (size_t)m * p.N + n;
     if (vec && n + 8 <= p.N) {
       *reinterpret_cast<u4_t *>(dst) = v;
