@@ -241,6 +241,30 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     issue_x(step, slot, 1);
     issue_w(step, slot);
   };
+  // The same loads for a step before the last one of the range (so neither past the end
+  // nor ragged, and its blocks lie before KB): no clamps or selects, offsets linear in the
+  // step.
+  const uint32_t kb_base = wrow_ok ? (uint32_t)(2 * sbase + kh) : 0u, kb_inc = wrow_ok ? 2u : 0u;
+  auto issue_x_mid = [&](int step, int slot, int half) {
+    uint8_t *base = smem + slot * SL::kBytes;
+    const uint32_t so = (uint32_t)(sbase + step) * BK * 2;
+#pragma unroll
+    for (int q = half * (XQ / 2); q < (half + 1) * (XQ / 2); ++q)
+      dma_buf(xr[q], xoff[q], so, base + SL::kX + ((BMT / 4) * wave + 8 * q) * 128, 16);
+  };
+  auto issue_w_mid = [&](int step, int slot) {
+    uint8_t *base = smem + slot * SL::kBytes;
+    const uint32_t kbo = kb_base + (uint32_t)step * kb_inc;
+    if constexpr (BITS == 2) {
+      dma_buf(wr, lo16, (kbo >> 1) * kGroup * 16, base + SL::kCodes + wave * SL::kCodesWave, 16);
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        dma_buf(wr, lo16, (kbo * C + c) * kGroup * 16, base + SL::kCodes + wave * SL::kCodesWave + c * 1024, 16);
+    }
+    dma_buf(sr, lo_sc, kbo * kGroup * 2, base + SL::kScale + wave * 256, 4);
+    if constexpr (HAS_ZP) dma_buf(zr, lo_zp, kbo * kZpB, base + SL::kZp + wave * 256, 4);
+  };
 
   // ---- dequantize this wave's block of one step into B operands [nb][kk] ----
   // The k index of an MFMA is a summation index, so any assignment of the block's k to
@@ -451,7 +475,9 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   // the step's 16 MFMAs come in quarters with the next step's dequantization arithmetic
   // between them, so the VALU work runs while the matrix core is busy.
   // slot: s mod kSlots, a compile-time constant at every call
-  auto body = [&](int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2], const int slot) {
+  // mid: the step issued here (s + kSlots - 1) is before the range's last step
+  auto body = [&](auto mid_c, int s, u4_t (&bc)[2][2], u4_t (&bn)[2][2], const int slot) {
+    constexpr bool mid = decltype(mid_c)::value;
     const int ls = (slot + kSlots - 1) % kSlots;
     const int ns = (slot + 1) % kSlots;
     wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();   // own loads of step s+1 have landed (later ones may not)
@@ -459,14 +485,20 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     dq_read(ns, rw);                      // past the end: unused, from a loaded slot
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 0);
-    issue_x(s + kSlots - 1, ls, 0);
+    if constexpr (mid) issue_x_mid(s + kSlots - 1, ls, 0);
+    else issue_x(s + kSlots - 1, ls, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 1);
     dq_compute(s + 1, rw, 0, bn);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 1, 0);
-    issue_x(s + kSlots - 1, ls, 1);
-    issue_w(s + kSlots - 1, ls);
+    if constexpr (mid) {
+      issue_x_mid(s + kSlots - 1, ls, 1);
+      issue_w_mid(s + kSlots - 1, ls);
+    } else {
+      issue_x(s + kSlots - 1, ls, 1);
+      issue_w(s + kSlots - 1, ls);
+    }
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 1, 1);
     dq_compute(s + 1, rw, 1, bn);
@@ -475,18 +507,29 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     read_a(ns, acur);                     // past the end: unused
   };
   // unrolled by the ring depth, so ring slots are compile-time constants
+  // (first the iterations whose loads are all for steps before the last: s + 2 kSlots - 2
+  // <= nsteps - 2)
+  constexpr std::integral_constant<bool, true> kMid{};
+  constexpr std::integral_constant<bool, false> kEdge{};
   int s = 0;
+  for (; s + 2 * kSlots <= nsteps; s += kSlots) {
+#pragma unroll
+    for (int i = 0; i < kSlots; i += 2) {
+      body(kMid, s + i, bcur, bnext, i);
+      body(kMid, s + i + 1, bnext, bcur, i + 1);
+    }
+  }
   for (; s + kSlots - 1 < nsteps; s += kSlots) {
 #pragma unroll
     for (int i = 0; i < kSlots; i += 2) {
-      body(s + i, bcur, bnext, i);
-      body(s + i + 1, bnext, bcur, i + 1);
+      body(kEdge, s + i, bcur, bnext, i);
+      body(kEdge, s + i + 1, bnext, bcur, i + 1);
     }
   }
 #pragma unroll
   for (int i = 0; i < kSlots - 1; i += 2) {   // at most kSlots - 1 steps remain
-    if (s + i < nsteps) body(s + i, bcur, bnext, i);
-    if (i + 1 < kSlots - 1 && s + i + 1 < nsteps) body(s + i + 1, bnext, bcur, i + 1);
+    if (s + i < nsteps) body(kEdge, s + i, bcur, bnext, i);
+    if (i + 1 < kSlots - 1 && s + i + 1 < nsteps) body(kEdge, s + i + 1, bnext, bcur, i + 1);
   }
   wait_vmcnt<0>();                        // the trailing loads into free slots are done
   lds_barrier();
