@@ -13,11 +13,13 @@
 // block's 32 k (4 x 2 v_mfma_f32_32x32x16_f16 blocks, two k16 steps).  So every weight is
 // dequantized exactly once, by the wave that multiplies it, directly into the B-operand
 // registers -- no fp16 weight tile goes through LDS -- and each X operand read from LDS
-// feeds two MFMAs.  After the K loop the two waves of a column half meet in LDS and the
-// kh = 0 wave adds the kh = 1 partial (fixed order: the result does not depend on timing).
+// feeds two MFMAs.  After the K loop the two waves of a column half (K halves of the same
+// 64 columns) each finish half of the row blocks: each hands the other half of its partials
+// to its partner through LDS, adds the LoRA term and then the partner's partial on its own
+// rows (fixed order: the result does not depend on timing), and stores that quarter.
 //
 // Memory pipeline.  Each K-step's inputs travel by direct-to-LDS loads
-// (global_load_lds_dwordx4 / _dword) into a 4-slot ring, three steps ahead of the MFMAs,
+// (buffer_load_dwordx4 / _dword ... lds) into a 4-slot ring, three steps ahead of the MFMAs,
 // so the load latency (L2 / Infinity Cache / HBM) hides behind three steps of matrix work
 // without holding any of it in registers:
 //   * the X tile (128 rows x 64 halfs), shared by all waves: each 16-byte chunk is
@@ -33,12 +35,13 @@
 // rounding) from the ring into registers.  Waits are explicit (s_waitcnt vmcnt for the
 // wave's own loads, then one barrier per step for the shared X tile); the compiler is kept
 // from moving memory accesses across the barrier.  Steps past the end issue loads from
-// clamped addresses into free slots, so every step has the same loads in flight.
+// clamped addresses into free slots, so every step has the same loads in flight; loop
+// iterations that load only steps before the last one skip the clamps.
 // Without an adapter the two epilogue k-steps are skipped, so the base accumulation order
 // is the same in every variant and a zero adapter reproduces the base output bitwise.
-// The finished tile is staged in LDS and stored by all four waves as whole row pieces
-// (16 bytes per lane, 256 contiguous bytes per row), not as the accumulator layout's
-// 16 bytes in each of 32 rows.
+// Each wave's finished quarter is staged in LDS and stored as whole row pieces (16 bytes
+// per lane, 128 contiguous bytes per row), not as the accumulator layout's 8 bytes in each
+// of 32 rows.
 #include <type_traits>
 #include "common.h"
 
