@@ -277,6 +277,25 @@ def test_gemm_split_k_ranges(bits, adapter):
         compare(run(case, 2, 0)[rows], oracle.matmul(rows_case(case, rows)), what="split M=%d N=%d K=%d" % (M, N, K))
 
 
+LOOP_SHAPES = [(1024, 4096, 1056), (1024, 4096, 544), (1024, 4096, 512)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("adapter", [None, "f16"], ids=["base", "f16"])
+def test_gemm_whole_k_loop_paths(bits, adapter):
+    """128-row tiles over whole K, so that one K range runs both forms of the main loop (the
+    iterations whose loads are all before the last step, then the clamped ones and the
+    tail): 17 steps with an odd block count (the last step ragged), 9 steps (odd), 8 steps;
+    rows sampled in every 32-row block of a tile, i.e. from every wave's quarter of the
+    epilogue."""
+    for i, (M, N, K) in enumerate(LOOP_SHAPES):
+        _, desc = mnb.mnb_describe_route(M, N, K, bits, 1, 1 if adapter else 0, mnb.mnb_options(2, 0))
+        assert desc.endswith("tile=128x128x64 splits=1"), desc
+        case = si.make_random(250 + i, M, N, K, bits, i != 1, adapter, bias=i == 2)
+        rows = [0, 1, 31, 32, 63, 64, 95, 96, 127, 128, 300, 511, 512, 700, M - 33, M - 1]
+        compare(run(case, 2, 0)[rows], oracle.matmul(rows_case(case, rows)), what="loop M=%d N=%d K=%d" % (M, N, K))
+
+
 TAIL_SHAPES = [(1000, 4202, 1056), (960, 4354, 1056), (1000, 4100, 640)]
 
 
