@@ -495,7 +495,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
     }
     if (M > 1 && M <= kRowsMaxM) {
       // small M: one pass over the weights for all rows on the matrix cores (T from the
-      // projection launch; route() sends X beyond one 32-bit buffer range to the GEMM)
+      // projection launch; X of up to 16 rows fits one 32-bit buffer range at every K)
       p.M = M;
       p.gt = 0;
       p.q = 4;
