@@ -121,7 +121,7 @@ struct Route {
   bool acc4;     // block-quantized int8 activations for the base product
 };
 
-Route route(int M, int K, int lora, const mnb_options *opt) {
+Route route(int M, int lora, const mnb_options *opt) {
   Route r{};
   const int path = opt ? opt->path : MNB_PATH_AUTO;
   const int flags = opt ? opt->flags : 0;
@@ -395,7 +395,7 @@ int mnb_describe_route(int M, int N, int K, int bits, int has_zp, int has_adapte
     snprintf(buf, buf_len, "fill");
     return MNB_OK;
   }
-  describe(buf, buf_len, M, N, K, bits, has_zp, route(M, K, has_adapter_kind, opt));
+  describe(buf, buf_len, M, N, K, bits, has_zp, route(M, has_adapter_kind, opt));
   return MNB_OK;
 }
 
@@ -417,7 +417,7 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   if (K == 0) return launch_fill(Yh, bh, M, N, s) == hipSuccess ? MNB_OK : MNB_ERR_HIP;
 
   const int lora = effective_lora(ad);
-  const Route r = route(M, K, lora, opt);
+  const Route r = route(M, lora, opt);
   const WsLayout w = ws_layout(M, N, K, lora ? kRank : 0);
   char *ws = static_cast<char *>(workspace);
   const int NG = cdiv(N, kGroup), KB = K / kBlock;

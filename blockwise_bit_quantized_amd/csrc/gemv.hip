@@ -378,7 +378,6 @@ __global__ __launch_bounds__(kThreads + 64) void gemv_kernel(GemvParams p) {
   constexpr int kPieces = XW / 8;
   constexpr int kPiecesPerChunk = KPC / 8;
   constexpr int kPiecesPerSum = BITS == 8 ? 2 : 4;       // one sum per 32-k block (8-bit: per chunk)
-  constexpr int kSums = kPieces / kPiecesPerSum;
 
 
   // LoRA: this lane's column of B, loaded ahead of the weight stream (independent of T)
