@@ -377,6 +377,7 @@ hipError_t launch_bits(const GemvParams &p, int lora, int gx, hipStream_t s) {
 template <int BITS, int MR>
 hipError_t launch_wide_mr(const GemvParams &p, int lora, int nloads, hipStream_t s) {
   if (nloads <= 8) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 8>), dim3(p.NG), dim3(256), 0, s, p, lora);
+  else if (nloads <= 9) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 9>), dim3(p.NG), dim3(256), 0, s, p, lora);
   else if (nloads <= 12) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 12>), dim3(p.NG), dim3(256), 0, s, p, lora);
   else hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 16>), dim3(p.NG), dim3(256), 0, s, p, lora);
   return hipGetLastError();
@@ -390,12 +391,13 @@ hipError_t launch_wide(const GemvParams &p, int lora, int nloads, hipStream_t s)
 }  // namespace
 
 // The wide form when the rows are many and short: at least 256 row groups (one workgroup
-// each), at most 16 wave loads per row (a 576-k int8 row has 9) and X staging within 64 KiB
+// each), at most 16 wave loads per row (a 576-k int8 row has 9, instantiated exactly: three
+// idle loads of the next size up cost 0.7 us there at M = 8) and X staging within 64 KiB
 // (room for two workgroups per CU); else 8 waves split K.
 bool gemv_mfma_wide(int M, int N, int K, int bits) {
   const int NG = (int)(((long)N + kGroup - 1) / kGroup);
   const int nloads = (chunk_cols(bits, K / kBlock) + kQ - 1) / kQ;
-  const int lpw = nloads <= 8 ? 8 : (nloads <= 12 ? 12 : 16);
+  const int lpw = nloads <= 8 ? 8 : (nloads <= 9 ? 9 : (nloads <= 12 ? 12 : 16));
   const int mr = M <= 8 ? 8 : 16;
   const int kpc = bits == 2 ? 64 : 32 / (bits / 4);
   const long lds = (long)lpw * kQ * mr * (kpc + 8) * 2;
