@@ -9,14 +9,22 @@
 //  * the A-part [kp, 32] is read once with 16-byte loads and written transposed into LDS
 //    (8x8 half tiles transposed in registers, one ds_write_b128 per rank row), so the
 //    MFMA B operand (8 consecutive k of one rank) is a single ds_read_b128;
-//  * each wave owns kp/4 consecutive k and issues all of its X loads (MFMA A operand,
-//    8 consecutive k of one row per lane) before waiting on anything;
-//  * v_mfma_f32_32x32x16_f16 per 16 k; the four waves meet in LDS in fixed order.
-// No counters and no cross-workgroup waits.
+//  * each thread issues its A loads, then its wave's X loads (MFMA A operand, 8
+//    consecutive k of one row per lane; a wave owns kp/4 consecutive k), before waiting
+//    on anything: loads return in issue order, so the transposes run while X streams in
+//    (at 1024 x 4096 the stamped A phase went from 1.9 to 1.0 us of a ~3.9 us pass);
+//  * v_mfma_f32_32x32x16_f16 per 16 k, all B operands read from LDS first, one chain in
+//    k order; the four waves meet in LDS in fixed order.
+// No cross-workgroup waits (with `reduce`, an arrival counter per M tile picks the
+// workgroup that adds the parts).
 #include "common.h"
 
 namespace mnb {
 namespace {
+
+typedef float f4_t __attribute__((ext_vector_type(4)));
+// cache-policy operand of the buffer-load builtins for an agent-scope coherent load: sc1
+constexpr int kCoherentSc1 = 16;
 
 // KIND 1: F16 A, 2: INT8 A with block-32 fp16 scales; KP: K per part (256, 512 or 1024,
 // see tproj_kp)
@@ -38,8 +46,43 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
   const bool mok = mrow < p.M;
   const int hk = 8 * (lane >> 5);
 
-  // X operand loads for this wave's k range (all issued first)
   const int kw = kbeg + wave * (kKP / 4);
+
+  // 1. this thread's 8x8 tiles (k octet, r octet) of the A part, raw, into registers.  They
+  //    are issued before X: a wave's loads return in issue order, so the transposes below
+  //    run while X is still streaming in instead of after it.
+  constexpr int kTiles = kKP / 8 * 4;
+  constexpr int kTilesPerThread = (kTiles + 255) / 256;
+  u4_t araw[kTilesPerThread][8];       // F16: row e of the tile; INT8: .xy = row e's 8 bytes
+  u4_t asc[kTilesPerThread];           // INT8: the tile's 8 block scales
+#pragma unroll
+  for (int i = 0; i < kTilesPerThread; ++i) {
+    const int t = tid + 256 * i;
+    const int ko = t >> 2, ro = t & 3;
+    const int k0 = kbeg + ko * 8;
+    if (t < kTiles && k0 < kend) {
+      if constexpr (KIND == 1) {
+        const uint16_t *A = static_cast<const uint16_t *>(p.A);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          araw[i][e] = *reinterpret_cast<const u4_t *>(A + (size_t)(k0 + e) * kRank + ro * 8);
+      } else {
+        const int8_t *A = static_cast<const int8_t *>(p.A);
+        asc[i] = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k0 / kBlock) * kRank + ro * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint2 a = *reinterpret_cast<const uint2 *>(A + (size_t)(k0 + e) * kRank + ro * 8);
+          araw[i][e] = u4_t{a.x, a.y, 0u, 0u};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) araw[i][e] = u4_t{0u, 0u, 0u, 0u};
+      asc[i] = u4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // 2. X operand loads for this wave's k range (8 consecutive k of one row per lane)
   const _Float16 *xr = reinterpret_cast<const _Float16 *>(p.X) + (size_t)(mok ? mrow : 0) * p.K;
   h8_t xa[kStepsPerWave];
 #pragma unroll
@@ -48,44 +91,30 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
     xa[s] = *reinterpret_cast<const h8_t *>(xr + (k < kend ? k : 0));
   }
 
-  // A part -> LDS transposed: thread handles 8x8 tiles (k octet, r octet)
-  constexpr int kTiles = kKP / 8 * 4;
+  // 3. A part -> LDS transposed, so that the MFMA B operand (8 consecutive k of one rank) is
+  //    a single ds_read_b128
 #pragma unroll
-  for (int t = tid; t < kTiles; t += 256) {
+  for (int i = 0; i < kTilesPerThread; ++i) {
+    const int t = tid + 256 * i;
+    if (t >= kTiles) continue;
     const int ko = t >> 2, ro = t & 3;
-    const int k0 = kbeg + ko * 8;
     uint32_t v[8][4];   // v[row e][dword d] = halves (r = 2d, 2d+1) of A[k0+e][8*ro ..]
-    if (k0 < kend) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
       if constexpr (KIND == 1) {
-        const uint16_t *A = static_cast<const uint16_t *>(p.A);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const u4_t a = *reinterpret_cast<const u4_t *>(A + (size_t)(k0 + e) * kRank + ro * 8);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) v[e][d] = a[d];
-        }
+        for (int d = 0; d < 4; ++d) v[e][d] = araw[i][e][d];
       } else {
-        const int8_t *A = static_cast<const int8_t *>(p.A);
-        const u4_t sv = *reinterpret_cast<const u4_t *>(p.sA + (size_t)(k0 / kBlock) * kRank + ro * 8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint2 a = *reinterpret_cast<const uint2 *>(A + (size_t)(k0 + e) * kRank + ro * 8);
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint32_t bytes = d < 2 ? a.x : a.y;
-            const int8_t lo = (int8_t)((bytes >> (16 * (d & 1))) & 0xff);
-            const int8_t hi = (int8_t)((bytes >> (16 * (d & 1) + 8)) & 0xff);
-            const h2_t s2 = as_h2(sv[d]);
-            const h2_t q = {(_Float16)((float)lo * (float)s2[0]), (_Float16)((float)hi * (float)s2[1])};
-            v[e][d] = as_u32(q);
-          }
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t bytes = d < 2 ? araw[i][e][0] : araw[i][e][1];
+          const int8_t lo = (int8_t)((bytes >> (16 * (d & 1))) & 0xff);
+          const int8_t hi = (int8_t)((bytes >> (16 * (d & 1) + 8)) & 0xff);
+          const h2_t s2 = as_h2(asc[i][d]);
+          const h2_t q = {(_Float16)((float)lo * (float)s2[0]), (_Float16)((float)hi * (float)s2[1])};
+          v[e][d] = as_u32(q);
         }
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) v[e][d] = 0u;
     }
     // transpose: rank row rr = 2d + h gets k = e (8 halves) -> one 16-byte store
 #pragma unroll
@@ -104,21 +133,26 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
   }
   __syncthreads();
 
+  // 4. this wave's k-steps inside the part (a wave-uniform count): all B operands read
+  //    first, then one MFMA chain in k order
+  const int nst = __builtin_amdgcn_readfirstlane(min(kStepsPerWave, max(0, (kend - kw + 15) / 16)));
   f16x_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.f;
   const int r = lane & 31;
+  h8_t bq[kStepsPerWave];
+#pragma unroll
+  for (int s = 0; s < kStepsPerWave; ++s)
+    if (s < nst) bq[s] = *reinterpret_cast<const h8_t *>(&sAT[r * kLdA + (kw - kbeg) + 16 * s + hk]);
 #pragma unroll
   for (int s = 0; s < kStepsPerWave; ++s) {
-    const int k = kw + 16 * s;
-    if (k < kend) {
-      const h8_t b = *reinterpret_cast<const h8_t *>(&sAT[r * kLdA + (k - kbeg) + hk]);
+    if (s < nst) {
       h8_t a = xa[s];
       if (!mok) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = (_Float16)0.f;
       }
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bq[s], acc, 0, 0, 0);
     }
   }
   __syncthreads();   // sAT no longer needed: reuse it for the cross-wave sum
@@ -159,26 +193,31 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
            p.parts - 1;
   __syncthreads();
   if (!last) return;
+  // Thread tid adds 4 consecutive ranks of one row (row tid / 8 of the tile) over the parts,
+  // in part order: 16-byte device-coherent loads (sc1: they miss in this XCD's L2 rather
+  // than hit a stale line), up to kB parts in flight at once.  Measured per small-M call
+  // against one dword per lane and part, four parts at a time: 0.3-1.6 us faster at 10
+  // and 16 parts, 0.15 us slower at 8 (8192 x 2048, M <= 8); dwords with every part in
+  // flight were slower than both.  The 32-bit offsets reach parts * M * 128 bytes, below
+  // 2^31 for the M <= 16 that reduce (K < 2^25).
+  const int m = mt * 32 + (tid >> 3);
+  if (m < p.M) {
+    constexpr int kB = 16;
+    const auto rt = buffer_rsrc(p.tpart, (long)p.parts * p.M * kRank * 4);
+    const uint32_t off = ((uint32_t)m * kRank + (tid & 7) * 4) * 4u;
+    const uint32_t pstride = (uint32_t)p.M * kRank * 4u;
+    f4_t tot = {0.f, 0.f, 0.f, 0.f};
+    for (int pp = 0; pp < p.parts; pp += kB) {
+      const int n = min(kB, p.parts - pp);  // wave-uniform: scalar branches, no lane masks
+      f4_t v[kB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + 256 * q;
-    const int m = mt * 32 + e / kRank;
-    if (m < p.M) {
-      const float *src = p.tpart + (size_t)m * kRank + (e % kRank);
-      float v[4];
-      float t = 0.f;
-      int pp = 0;
-      for (; pp + 4 <= p.parts; pp += 4) {     // four loads in flight, added in order
+      for (int u = 0; u < kB; ++u)
+        if (u < n) v[u] = __builtin_amdgcn_raw_buffer_load_b128(rt, off + (uint32_t)(pp + u) * pstride, 0, kCoherentSc1);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = __hip_atomic_load(src + (size_t)(pp + u) * p.M * kRank, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) t += v[u];
-      }
-      for (; pp < p.parts; ++pp)
-        t += __hip_atomic_load(src + (size_t)pp * p.M * kRank, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      p.tfinal[(size_t)m * kRank + (e % kRank)] = t;
+      for (int u = 0; u < kB; ++u)
+        if (u < n) tot += v[u];
     }
+    *reinterpret_cast<f4_t *>(p.tfinal + (size_t)m * kRank + (tid & 7) * 4) = tot;
   }
   if (tid == 0) __hip_atomic_store(&p.ctrl[ctrl_tproj_word(mt)], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -248,6 +248,30 @@ def test_small_m_matrix_core_forms(bits, zp, adapter):
     assert forms == {True, False}, "both forms exercised"
 
 
+# T projection part layouts: the part reduction in the projection (2 <= M <= 16) across
+# its 16-part load batches with a ragged last part, both 8-row blocks of a 16-row tile,
+# the 1024-k parts (two A tiles per thread), and the parts the GEMM adds (M > 16, ragged)
+TPROJ_CASES = [(5, 136, 4640, "f16", 19), (5, 136, 4640, "q8", 19), (16, 200, 8192, "q8", 32),
+               (2, 64, 131072, "f16", 128), (40, 96, 2592, "q8", 6)]
+
+
+@pytest.mark.parametrize("M,N,K,adapter,parts", TPROJ_CASES)
+def test_t_projection_parts(M, N, K, adapter, parts):
+    kind = {"f16": 1, "q8": 2}[adapter]
+    _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, kind, None)
+    assert "parts=%d;" % parts in desc, desc
+    case = si.make_random(260 + M, M, N, K, 4, True, adapter)
+    ref = oracle.matmul(case)
+    peak = float(np.abs(ref).max())
+    if peak > 8.0:
+        # long K: scales shrunk so that the fp16 outputs' own rounding stays below the
+        # absolute bound (|y| <= 8: half an ulp is at most 2^-8)
+        sc = case["scales"].view(np.float16).astype(np.float32) * np.float32(8.0 / peak)
+        case["scales"] = sc.astype(np.float16).view(np.uint16)
+        ref = oracle.matmul(case)
+    compare(run(case), ref, what="%s M=%d N=%d K=%d" % (adapter, M, N, K))
+
+
 SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 2080)]
 
 
