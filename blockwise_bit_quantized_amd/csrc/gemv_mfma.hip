@@ -270,25 +270,35 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvParams p, int l
   finish_tile(p, lora, total, n, M);
 }
 
-// Short K and many row groups: a workgroup of 4 waves owns one 64-row group, wave w its
-// rows 16 w .. 16 w + 15 over the whole of K, so no partial sums cross waves.  X for all of
-// K (at most LPW * 4 chunk-columns) is staged once per workgroup, and each wave issues all
-// of its LPW loads before it waits on anything.  (With 8 waves splitting K, a 576-k row
-// gives each 16-row workgroup 9 wave loads for 8 waves and 4 workgroups per 64 rows: the
-// 49152 x 576 lm_head then ran 3072 small workgroups in four dispatch rounds.)
+// Short K and many row groups: a workgroup owns one 64-row group, with X for all of K (at
+// most LPW * 4 chunk-columns) staged once per workgroup.  With up to 8 X rows it has 8
+// waves: waves w and w + 4 own rows 16 w .. 16 w + 15 and take the even and the odd wave
+// loads of those rows, and the odd half's partial sums reach the even half through LDS
+// (added in that order).  With 16 X rows it has 4 waves, each over the whole of K.  Every
+// wave issues all of its loads before it waits on anything.  A wave's loads in flight are
+// what bounds this form: on the 49152 x 576 int8 lm_head (9 wave loads per row) splitting
+// each row slice over two waves took M = 2-8 from 10.7 to 9.4 us; at 16 X rows (larger
+// staging and MFMA operands per wave) the split measured slower (11.1 -> 12.2 us).  (With 8
+// waves splitting K over 16 rows instead, a 576-k row gives each 16-row workgroup 9 wave
+// loads for 8 waves and 4 workgroups per 64 rows: the lm_head then ran 3072 small
+// workgroups in four dispatch rounds.)
 template <int BITS, int MR, int LPW>
-__global__ __launch_bounds__(256) void gemv_mfma_wide_kernel(GemvParams p, int lora) {
+__global__ __launch_bounds__(MR <= 8 ? 512 : 256) void gemv_mfma_wide_kernel(GemvParams p, int lora) {
   using S = Shape<BITS>;
   constexpr int KPC = S::KPC, kRowH = S::kRowH, kZpB = S::kZpB;
   constexpr int kSlotH = MR * kRowH;
   constexpr int kCC = LPW * kQ;                              // chunk-columns of X staged
+  constexpr int kHalves = MR <= 8 ? 2 : 1;                   // waves per 16-row slice
+  constexpr int kNT = 256 * kHalves;                         // threads
   __shared__ __attribute__((aligned(16))) _Float16 xs[kCC * kSlotH];
+  __shared__ f4_t red[kHalves == 2 ? 4 : 1][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = wave >> 2;                                // 0 with kHalves == 1
   const int g = blockIdx.x;
   const int nl = lane & 15, gq = lane >> 4;
-  const int row = wave * kRowsWG + nl;
+  const int row = (wave & 3) * kRowsWG + nl;
   const int n = g * kGroup + row;
   const int M = p.M;
   const bool has_zp = p.zp != nullptr;
@@ -312,24 +322,26 @@ __global__ __launch_bounds__(256) void gemv_mfma_wide_kernel(GemvParams p, int l
   const auto rs = buffer_rsrc(p.sc + (size_t)g * p.KB * kGroup, (long)p.KB * kGroup * 2);
   const auto rz = buffer_rsrc(has_zp ? p.zp + (size_t)g * p.KB * kZpB : p.wq, has_zp ? (long)p.KB * kZpB : 0);
 
-  // 1. X pieces (chunk-column, X row m, 8 halfs) over the workgroup's 256 threads
+  // 1. X pieces (chunk-column, X row m, 8 halfs) over the workgroup's threads
   constexpr int kPieces = kCC * MR * (KPC / 8);
-  constexpr int kIter = (kPieces + 255) / 256;
+  constexpr int kIter = (kPieces + kNT - 1) / kNT;
   u4_t xv[kIter];
 #pragma unroll
   for (int t = 0; t < kIter; ++t) {
-    const int pc = threadIdx.x + 256 * t;
+    const int pc = threadIdx.x + kNT * t;
     const int sub = pc % (KPC / 8), rest = pc / (KPC / 8);
     const int m = rest % MR, cc = rest / MR;
     const int k = cc * KPC + sub * 8;
     const bool in = pc < kPieces && m < M && k < p.K;
     xv[t] = __builtin_amdgcn_raw_buffer_load_b128(rx, in ? (uint32_t)((size_t)m * p.K + k) * 2u : 0x7ffffff0u, 0, 0);
   }
-  // 2. this wave's weight stream: wave load i covers chunk-columns 4 i .. 4 i + 3 of its rows
+  // 2. this wave's weight stream: wave load i covers chunk-columns 4 i .. 4 i + 3 of its
+  //    rows (with two halves, this wave's loads are those with i % 2 == half)
   u4_t cw[LPW];
   uint32_t sraw[LPW], zraw[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
+    if (kHalves == 2 && (i & 1) != half) continue;           // uniform
     const uint32_t rel = (uint32_t)i;
     cw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_lane + rel * (kQ * kGroup * 16), 0, 0);
     if constexpr (BITS == 4) {
@@ -348,10 +360,10 @@ __global__ __launch_bounds__(256) void gemv_mfma_wide_kernel(GemvParams p, int l
                        : 0u;
     }
   }
-  // 3. X to LDS, shared by the four waves
+  // 3. X to LDS, shared by the waves
 #pragma unroll
   for (int t = 0; t < kIter; ++t) {
-    const int pc = threadIdx.x + 256 * t;
+    const int pc = threadIdx.x + kNT * t;
     const int sub = pc % (KPC / 8), rest = pc / (KPC / 8);
     const int m = rest % MR, cc = rest / MR;
     if (pc < kPieces) *reinterpret_cast<u4_t *>(&xs[cc * kSlotH + m * kRowH + sub * 8]) = xv[t];
@@ -361,8 +373,15 @@ __global__ __launch_bounds__(256) void gemv_mfma_wide_kernel(GemvParams p, int l
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    if (i >= nloads) continue;                               // uniform
+    if (i >= nloads || (kHalves == 2 && (i & 1) != half)) continue;   // uniform
     slot_mfma<BITS>(acc, cw[i], sraw[i], zraw[i], has_zp, row, &xs[(i * kQ + gq) * kSlotH], kRowH, MR, M);
+  }
+  if constexpr (kHalves == 2) {
+    // the odd loads' partial sums to the even half, added in that order
+    if (half) red[wave & 3][lane] = acc;
+    __syncthreads();
+    if (half) return;
+    acc += red[wave][lane];
   }
   finish_tile(p, lora, acc, n, M);
 }
@@ -376,10 +395,11 @@ hipError_t launch_bits(const GemvParams &p, int lora, int gx, hipStream_t s) {
 
 template <int BITS, int MR>
 hipError_t launch_wide_mr(const GemvParams &p, int lora, int nloads, hipStream_t s) {
-  if (nloads <= 8) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 8>), dim3(p.NG), dim3(256), 0, s, p, lora);
-  else if (nloads <= 9) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 9>), dim3(p.NG), dim3(256), 0, s, p, lora);
-  else if (nloads <= 12) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 12>), dim3(p.NG), dim3(256), 0, s, p, lora);
-  else hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 16>), dim3(p.NG), dim3(256), 0, s, p, lora);
+  const dim3 block(MR <= 8 ? 512 : 256);                    // the kernel's two halves at up to 8 X rows
+  if (nloads <= 8) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 8>), dim3(p.NG), block, 0, s, p, lora);
+  else if (nloads <= 9) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 9>), dim3(p.NG), block, 0, s, p, lora);
+  else if (nloads <= 12) hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 12>), dim3(p.NG), block, 0, s, p, lora);
+  else hipLaunchKernelGGL((gemv_mfma_wide_kernel<BITS, MR, 16>), dim3(p.NG), block, 0, s, p, lora);
   return hipGetLastError();
 }
 

@@ -228,8 +228,11 @@ def test_decode_x_range(bits, zp, x_std, s_lo, s_hi):
 # small-M matrix-core GEMV, both forms: 16 rows per workgroup (8 waves splitting K), and one
 # 64-row group per workgroup when the rows are many and short (>= 256 row groups, <= 16 wave
 # loads per row); ragged N (last row group partial) and K (wave loads past the row), X rows
-# 2..16 (the MFMA's rows past M padded)
-SMALL_M_SHAPES = [(2, 200, 1056), (5, 130, 96), (9, 16400, 576), (16, 16400, 160), (3, 20000, 2080)]
+# 2..16 (the MFMA's rows past M padded).  The one-group form at up to 8 X rows splits each
+# row slice's wave loads over two waves: odd load counts (9, 5, 3 at 8, 4, 2 bits for
+# K = 576: uneven halves) and a single load (K = 64: the odd half has none)
+SMALL_M_SHAPES = [(2, 200, 1056), (5, 130, 96), (9, 16400, 576), (16, 16400, 160), (3, 20000, 2080),
+                  (5, 16400, 576), (2, 16400, 64)]
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
