@@ -429,16 +429,16 @@ int mnb_matmul_bias(const void *X, const void *wq, const void *sc, const void *z
   }
 
   // T projection output: FP32 partials per K-part; consumers read `tparts` parts.  For
-  // 2 <= M <= 16, whose consumers would add the parts row by row, the projection reduces
-  // them itself (per-tile arrival counter; device-coherent stores and loads, no fences).
-  // Above that the reduction costs more than the consumer's part loads it saves (measured
-  // for every M: 1024 x 4096 x 4096 49.7 -> 54.1 us), so the projection uses 512-k parts
-  // and the GEMM adds them (eight loads in flight, then one at a time); the M == 1 GEMV
-  // adds up to 8 with its loads in flight together.
+  // 2 <= M <= 16 and K <= 2048 the parts are at most 4, which the small-M GEMV loads ahead
+  // of its weight stream and adds itself; more parts are reduced by the projection
+  // (per-tile arrival counter; device-coherent stores and loads, no fences).  Above 16 rows the reduction costs more than the
+  // consumer's part loads it saves (measured for every M: 1024 x 4096 x 4096 49.7 -> 54.1
+  // us), so the projection uses 512-k parts and the GEMM adds them (eight loads in flight,
+  // then one at a time); the M == 1 GEMV adds up to 8 with its loads in flight together.
   float *tproj_out = lora ? reinterpret_cast<float *>(ws + w.tproj) : nullptr;
   int tparts = w.tparts;
   if (r.tproj) {
-    const int reduce = w.tparts > 1 && w.tmt <= kTprojCounters && M > 1 && M <= kRowsMaxM;
+    const int reduce = w.tparts > 4 && w.tmt <= kTprojCounters && M > 1 && M <= kRowsMaxM;
     TprojParams tp{static_cast<const uint16_t *>(X), ad->A, static_cast<const uint16_t *>(ad->A_scales), tproj_out,
                    reinterpret_cast<float *>(ws + w.tfinal), reinterpret_cast<int *>(ws + w.ctrl),
                    M, K, w.tmt, w.tparts, reduce};

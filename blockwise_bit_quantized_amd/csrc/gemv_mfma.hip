@@ -112,17 +112,50 @@ __device__ __forceinline__ void slot_mfma(f4_t &acc, const u4_t cw, uint32_t sra
 // ranks 8 (lane / 16) .., fp16 rounded once from the FP32 sum over parts) by the B column as
 // the B operand (INT8 B is exact in fp16; its column scale multiplies the product) -- plus
 // the bias, stored as fp16 for the rows below M.
-__device__ __forceinline__ void finish_tile(const GemvParams &p, int lora, f4_t total, int n, int M) {
+// T parts of the projection launch for the epilogue lane (X row lane % 16, ranks
+// 8 (lane / 16) .. + 7): in the 16-row form with an adapter the first kTPre are loaded when
+// the kernel starts, ahead of the weight stream, so their round trip passes with it (the
+// projection keeps its parts to at most 4 when K allows, and reduces them itself beyond
+// that); their registers are live throughout, so the form is instantiated without them for
+// calls with one part or none, and the one-group form loads T in its epilogue
+constexpr int kTPre = 4;
+struct TPre {
+  float4 v[kTPre][2];
+};
+__device__ __forceinline__ void t_prefetch(const GemvParams &p, int lora, int M, TPre &t) {
+  const int lane = threadIdx.x & 63;
+  const int tm = lane & 15, r0 = 8 * (lane >> 4);
+  if (lora == LORA_NONE || tm >= M) return;
+#pragma unroll
+  for (int pp = 0; pp < kTPre; ++pp) {
+    if (pp >= p.tparts) break;
+    const float *src = p.tin + ((size_t)pp * p.tmpad + tm) * kRank + r0;
+    t.v[pp][0] = *reinterpret_cast<const float4 *>(src);
+    t.v[pp][1] = *reinterpret_cast<const float4 *>(src + 4);
+  }
+}
+
+__device__ __forceinline__ void finish_tile(const GemvParams &p, int lora, f4_t total, int n, int M, const TPre *tp) {
   const int lane = threadIdx.x & 63;
   if (lora != LORA_NONE) {
     const int tm = lane & 15, r0 = 8 * (lane >> 4);
     float tv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (tm < M) {
-      for (int pp = 0; pp < p.tparts; ++pp) {
-        const float *src = p.tin + ((size_t)pp * p.tmpad + tm) * kRank + r0;
-        const float4 a = *reinterpret_cast<const float4 *>(src), b = *reinterpret_cast<const float4 *>(src + 4);
+      // the parts in part order: the prefetched ones, then any beyond them
+      auto add = [&](const float4 &a, const float4 &b) {
         tv[0] += a.x; tv[1] += a.y; tv[2] += a.z; tv[3] += a.w;
         tv[4] += b.x; tv[5] += b.y; tv[6] += b.z; tv[7] += b.w;
+      };
+      int pp = 0;
+      if (tp) {
+#pragma unroll
+        for (int q = 0; q < kTPre; ++q)
+          if (q < p.tparts) add(tp->v[q][0], tp->v[q][1]);
+        pp = kTPre;
+      }
+      for (; pp < p.tparts; ++pp) {
+        const float *src = p.tin + ((size_t)pp * p.tmpad + tm) * kRank + r0;
+        add(*reinterpret_cast<const float4 *>(src), *reinterpret_cast<const float4 *>(src + 4));
       }
     }
     h8_t ta, tb;
@@ -153,7 +186,7 @@ __device__ __forceinline__ void finish_tile(const GemvParams &p, int lora, f4_t 
   }
 }
 
-template <int BITS, int MR>
+template <int BITS, int MR, bool TP>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvParams p, int lora) {
   using S = Shape<BITS>;
   constexpr int KPC = S::KPC, LPW = S::LPW, kRowH = S::kRowH, kZpB = S::kZpB;
@@ -195,6 +228,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvParams p, int l
   }
   // all of X through one descriptor: a piece of a row past M, or of k past K, reads zeros
   const auto rx = buffer_rsrc(p.X, (long)M * p.K * 2);
+  TPre tpre;                               // wave 0 finishes the tile: its T parts first
+  if constexpr (TP)
+    if (wave == 0) t_prefetch(p, lora, M, tpre);
 
   f4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int l0 = 0; l0 < nloads; l0 += kWaves * LPW) {
@@ -267,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvParams p, int l
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) total += red[w][lane];
 
-  finish_tile(p, lora, total, n, M);
+  finish_tile(p, lora, total, n, M, TP ? &tpre : nullptr);
 }
 
 // Short K and many row groups: a workgroup owns one 64-row group, with X for all of K (at
@@ -383,13 +419,20 @@ __global__ __launch_bounds__(MR <= 8 ? 512 : 256) void gemv_mfma_wide_kernel(Gem
     if (half) return;
     acc += red[wave][lane];
   }
-  finish_tile(p, lora, acc, n, M);
+  finish_tile(p, lora, acc, n, M, nullptr);
 }
 
+template <int BITS, bool TP>
+void launch_bits_tp(const GemvParams &p, int lora, int gx, hipStream_t s) {
+  if (p.M <= 8) hipLaunchKernelGGL((gemv_mfma_kernel<BITS, 8, TP>), dim3(gx), dim3(kThreads), 0, s, p, lora);
+  else hipLaunchKernelGGL((gemv_mfma_kernel<BITS, 16, TP>), dim3(gx), dim3(kThreads), 0, s, p, lora);
+}
 template <int BITS>
 hipError_t launch_bits(const GemvParams &p, int lora, int gx, hipStream_t s) {
-  if (p.M <= 8) hipLaunchKernelGGL((gemv_mfma_kernel<BITS, 8>), dim3(gx), dim3(kThreads), 0, s, p, lora);
-  else hipLaunchKernelGGL((gemv_mfma_kernel<BITS, 16>), dim3(gx), dim3(kThreads), 0, s, p, lora);
+  // the prefetch only where there are parts to add: its registers cost occupancy (with them
+  // 9728 x 2560 at M <= 8 fits two workgroups per CU, not three, and ran two rounds)
+  if (lora != LORA_NONE && p.tparts > 1) launch_bits_tp<BITS, true>(p, lora, gx, s);
+  else launch_bits_tp<BITS, false>(p, lora, gx, s);
   return hipGetLastError();
 }
 

@@ -225,11 +225,17 @@ __global__ __launch_bounds__(256) void tproj_kernel(TprojParams p) {
 }  // namespace
 
 // K per part: above M = 16 512 (the GEMM adds up to 8 parts with their loads issued before
-// its ring starts; measured 1-2 us faster per prefill call than 1024, 256 slower); for
-// M <= 16 (whose parts the projection adds itself) 1024, or 256 when that would give fewer
-// than 128 workgroups
+// its ring starts; measured 1-2 us faster per prefill call than 1024, 256 slower).  Up to
+// 16 rows and K <= 2048, 256 or 512: at most 4 parts, which the small-M GEMV loads ahead of
+// its weight stream and adds itself, with no reduction round trips in the projection
+// (8192 x 2048 with an F16 adapter at M = 2-16: 1.1-1.3 us faster per call than 8 parts
+// reduced).  Longer K: 1024, or 256 when that would give fewer than 128 workgroups, and the
+// projection reduces the parts (`reduce`): 4 parts of 1024 k measured 0.2-0.4 us faster at
+// 4096 x 4096 but 1.3-2.1 us slower with the INT8 adapter of 9728 x 2560 (3 workgroups,
+// each converting 1024 rows of A).
 int tproj_kp(int M, int K) {
   if (M > kRowsMaxM) return 512;
+  if (K <= 2048) return K <= 1024 ? 256 : 512;
   return (((long)M + 31) / 32) * ((K + 1023) / 1024) < 128 ? 256 : 1024;
 }
 int tproj_parts(int M, int K) {

@@ -251,11 +251,14 @@ def test_small_m_matrix_core_forms(bits, zp, adapter):
     assert forms == {True, False}, "both forms exercised"
 
 
-# T projection part layouts: the part reduction in the projection (2 <= M <= 16) across
-# its 16-part load batches with a ragged last part, both 8-row blocks of a 16-row tile,
-# the 1024-k parts (two A tiles per thread), and the parts the GEMM adds (M > 16, ragged)
+# T projection part layouts: the part reduction in the projection (2 <= M <= 16, K > 2048)
+# across its 16-part load batches with a ragged last part, both 8-row blocks of a 16-row
+# tile, the 1024-k parts (two A tiles per thread); up to 4 parts added by the small-M GEMV
+# from its prefetch (K <= 2048, ragged last part, both X-row forms); and the parts the GEMM
+# adds (M > 16, ragged)
 TPROJ_CASES = [(5, 136, 4640, "f16", 19), (5, 136, 4640, "q8", 19), (16, 200, 8192, "q8", 32),
-               (2, 64, 131072, "f16", 128), (40, 96, 2592, "q8", 6)]
+               (2, 64, 131072, "f16", 128), (6, 136, 2016, "f16", 4), (9, 200, 1056, "q8", 3),
+               (40, 96, 2592, "q8", 6)]
 
 
 @pytest.mark.parametrize("M,N,K,adapter,parts", TPROJ_CASES)
