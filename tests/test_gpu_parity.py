@@ -666,15 +666,19 @@ def test_determinism_and_workspace_reuse():
 
 def test_graph_replay_matches_eager():
     """Calls captured in a HIP graph (decode with the in-pass T handoff, small M with the T
-    reduction in the projection, split-K prefill, a prefill whose last round of tiles splits
-    K, accuracy level 4 with one and with four X rows per workgroup and on the GEMM path) give, on every replay, exactly the eager results, with eager calls
-    on the same workspace between the replays: the library enqueues no memset and keeps its
-    per-call state (the T epoch, the counters) in the workspace."""
+    parts added by the small-M GEMV and with the T reduction in the projection, split-K
+    prefill, a prefill whose last round of tiles splits K, accuracy level 4 with one and with
+    four X rows per workgroup and on the GEMM path) give, on every replay, exactly the eager
+    results, with eager calls on the same workspace between the replays: the library
+    enqueues no memset and keeps its per-call state (the T epoch, the counters) in the
+    workspace."""
     specs = [(1, 4096, 2048, 4, False, "f16", 0), (3, 1000, 1024, 4, True, "q8", 0),
              (200, 512, 1024, 8, True, "f16", 0), (1000, 4100, 640, 4, False, "f16", 0),
              (1, 896, 896, 4, True, None, mnb.MNB_FLAG_ACC4), (6, 4096, 640, 4, True, "f16", mnb.MNB_FLAG_ACC4),
-             (300, 640, 512, 4, True, "f16", mnb.MNB_FLAG_ACC4)]
+             (300, 640, 512, 4, True, "f16", mnb.MNB_FLAG_ACC4), (3, 1000, 2560, 4, True, "q8", 0)]
     assert mnb.mnb_describe_route(6, 4096, 640, 4, 1, 1, mnb.mnb_options(0, mnb.MNB_FLAG_ACC4))[1].endswith("mr=4")
+    assert "parts=4;" in mnb.mnb_describe_route(3, 1000, 1024, 4, 1, 2)[1]      # added by the GEMV
+    assert "parts=10;" in mnb.mnb_describe_route(3, 1000, 2560, 4, 1, 2)[1]     # reduced in the projection
     assert " tail=" in mnb.mnb_describe_route(1000, 4100, 640, 4, 0, 1)[1]
     ws = torch.zeros(max(mnb.mnb_workspace_bytes(M, N, K, b, 32) for M, N, K, b, *_ in specs), dtype=torch.uint8,
                      device=DEV)
