@@ -313,8 +313,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvParams p, int l
 // (added in that order).  With 16 X rows it has 4 waves, each over the whole of K.  Every
 // wave issues all of its loads before it waits on anything.  A wave's loads in flight are
 // what bounds this form: on the 49152 x 576 int8 lm_head (9 wave loads per row) splitting
-// each row slice over two waves took M = 2-8 from 10.7 to 9.4 us; at 16 X rows (larger
-// staging and MFMA operands per wave) the split measured slower (11.1 -> 12.2 us).  (With 8
+// each row slice over two waves took M = 2-8 from 10.7 to 9.6 us; at 16 X rows (larger
+// staging and MFMA operands per wave) a timing copy of the split without the halves' sum
+// (so at best) was slower, 11.1 -> 12.2 us.  (With 8
 // waves splitting K over 16 rows instead, a 576-k row gives each 16-row workgroup 9 wave
 // loads for 8 waves and 4 workgroups per 64 rows: the lm_head then ran 3072 small
 // workgroups in four dispatch rounds.)
