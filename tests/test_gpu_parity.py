@@ -463,7 +463,7 @@ def test_exact_arithmetic_with_bias_bit_exact(kind, M):
 
 
 BIAS_SHAPES = [(1, 64, 32), (1, 100, 96), (3, 130, 160), (8, 257, 320), (13, 96, 256), (16, 70, 192),
-               (129, 257, 320), (1, 4096, 2048)]
+               (129, 257, 320), (1, 4096, 2048), (5, 16400, 576)]   # the last: the one-group small-M form
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
