@@ -21,20 +21,25 @@
 // Memory pipeline.  Each K-step's inputs travel by direct-to-LDS loads
 // (buffer_load_dwordx4 / _dword ... lds) into a 4-slot ring, three steps ahead of the MFMAs,
 // so the load latency (L2 / Infinity Cache / HBM) hides behind three steps of matrix work
-// without holding any of it in registers:
+// without holding any of it in registers.  With 128-row tiles the ring is filled by four
+// load waves (one per SIMD, beside the compute wave whose loads it issues), so the compute
+// waves' instruction streams hold no global loads: a wave that issues its own loads issues
+// no MFMAs while it waits to get them accepted, and one wave per SIMD moves only about half
+// the bytes per clock that the CU's load path carries with two.  64-row tiles (two
+// workgroups per CU) issue their own loads.
 //   * the X tile (128 rows x 64 halfs), shared by all waves: each 16-byte chunk is
 //     fetched into slot position chunk ^ ((row >> 1) & 7) (an XOR swizzle chosen through
 //     the source address, since a DMA writes lanes consecutively), so MFMA operand reads
 //     of 16 consecutive rows (256 bytes, one pass over the 64 LDS banks) hit distinct
 //     banks without padding;
-//   * the codes, scales and zero points of the wave's own 64 rows and block; the wave
-//     later reads only bytes its own lanes fetched, so it waits only on its own load
-//     counter.  Every lane issues every direct load (lanes past the useful ones fetch
+//   * the codes, scales and zero points of the wave's own 64 rows and block; without load
+//     waves the wave later reads only bytes its own lanes fetched, so it waits only on its
+//     own load counter (with them, the step barrier publishes these as well).  Every lane issues every direct load (lanes past the useful ones fetch
 //     copies): loads narrower than 4 bytes, or under a lane mask, are not used.
 // One step ahead of its MFMAs each wave dequantizes (q - z) * s (exact subtraction, one
 // rounding) from the ring into registers.  Waits are explicit (s_waitcnt vmcnt for the
-// wave's own loads, then one barrier per step for the shared X tile); the compiler is kept
-// from moving memory accesses across the barrier.  Steps past the end issue loads from
+// loads, then one barrier per step for the shared X tile); the compiler is kept from moving
+// memory accesses across the barrier.  Steps past the end issue loads from
 // clamped addresses into free slots, so every step has the same loads in flight; loop
 // iterations that load only steps before the last one skip the clamps.
 // Without an adapter the two epilogue k-steps are skipped, so the base accumulation order
@@ -104,7 +109,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int BITS, bool HAS_ZP, int LORA, int BMT>
-__global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(BMT == 128 ? 2 * kThreads : kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmParams p) {
+  // 128-row tiles: waves 4-7 are load waves.  Load wave 4 + w issues, for compute wave w,
+  // the ring loads that wave w would issue (the same addresses: every per-wave quantity
+  // below is computed from w), plus the LoRA operands, and arrives at every barrier the
+  // compute waves do; the compute waves issue no global loads in the K loop.
+  constexpr bool LW = BMT == 128;
   constexpr int C = BITS == 8 ? 2 : 1;       // 16-byte code chunks per wave and step
   constexpr int MB = BMT / 32;               // 32-row MFMA blocks per wave
   constexpr int XQ = BMT / 32;               // X loads per wave and step (1 KiB each)
@@ -115,9 +125,10 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
   constexpr int kLoadsPerStep = XQ + C + 1 + (HAS_ZP ? 1 : 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & (kThreads - 1);
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool loader = LW && __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) != 0;
   const int nh = wave & 1;                   // column half: one packed 64-row group
   const int kh = wave >> 1;                  // block of the K-step
   const int l32 = lane & 31, hi = lane >> 5;
@@ -350,6 +361,182 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     }
   };
 
+  // LoRA epilogue operands, fetched first (ordinary loads that complete ahead of the ring
+  // loads): T rows (FP32 K-part partials, added in part order) and this thread's B slice.
+  // Two threads per tile row: for 64-row tiles only waves 0 and 1 load T, and only the
+  // parts that exist (the others' loads would be wasted L2 traffic in every tile).
+  float tsum[16];
+  u4_t braw[2];
+  uint32_t bsc[8];
+  bool bvec = false;
+  const int trow = tid >> 1, thh = (tid & 1) * 16;
+  const bool t_loader = trow < BMT;            // wave-uniform
+  const int br = tid >> 3, bnc = (tid & 7) * 16;
+  constexpr int kTPartsAhead = 8;            // T parts loaded before the ring starts
+  // (with load waves these are theirs: B here, the T parts one per step of their loop)
+  float4 tv[LW ? 1 : kTPartsAhead][4];
+  float4 tw[2][4];                           // load waves: T parts in flight, two steps deep
+  if (lora_here && (!LW || loader)) {
+    const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
+    if constexpr (!LW) {
+      if (t_loader) {
+#pragma unroll
+        for (int pp = 0; pp < kTPartsAhead; ++pp) {
+          if (pp < p.tparts) {
+            const float *src = p.tpart + ((size_t)pp * p.M + mrow) * kRank + thh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tv[pp][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
+          }
+        }
+      }
+    }
+    const int n = n0 + bnc;
+    if constexpr (LORA == 1) {
+      bvec = (p.N % 8) == 0 && n + 16 <= p.N;
+      if (bvec) {
+        const uint16_t *src = static_cast<const uint16_t *>(p.B) + (size_t)br * p.N + n;
+        braw[0] = *reinterpret_cast<const u4_t *>(src);
+        braw[1] = *reinterpret_cast<const u4_t *>(src + 8);
+      }
+    } else {
+      bvec = (p.N % 16) == 0 && n + 16 <= p.N;
+      if (bvec) {
+        braw[0] = *reinterpret_cast<const u4_t *>(static_cast<const int8_t *>(p.B) + (size_t)br * p.N + n);
+        const u4_t s0 = *reinterpret_cast<const u4_t *>(p.sB + n);
+        const u4_t s1 = *reinterpret_cast<const u4_t *>(p.sB + n + 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bsc[q] = s0[q];
+          bsc[4 + q] = s1[q];
+        }
+      }
+    }
+  }
+
+  _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
+  _Float16 *sB = sT + BMT * LDT;
+  auto write_lora_operands = [&]() {
+    // epilogue operands: T tile [BMT m][32 r] (fp16, rounded once from the FP32 sum) and
+    // the B tile transposed to [128 n][32 r]
+    u4_t o[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const h2_t hv = {(_Float16)tsum[8 * q + 2 * d], (_Float16)tsum[8 * q + 2 * d + 1]};
+        o[q][d] = as_u32(hv);
+      }
+    if (trow < BMT) {
+      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
+      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int n = n0 + bnc + e;
+      _Float16 v = (_Float16)0.f;
+      if (bvec) {
+        if constexpr (LORA == 1) {
+          v = as_h2(braw[e >> 3][(e & 7) >> 1])[e & 1];
+        } else {
+          const int8_t b8 = (int8_t)((braw[0][e >> 2] >> (8 * (e & 3))) & 0xff);
+          v = (_Float16)((float)b8 * (float)as_h2(bsc[e >> 1])[e & 1]);
+        }
+      } else if (n < p.N) {
+        if constexpr (LORA == 1) {
+          v = __builtin_bit_cast(_Float16, static_cast<const uint16_t *>(p.B)[(size_t)br * p.N + n]);
+        } else {
+          v = (_Float16)((float)static_cast<const int8_t *>(p.B)[(size_t)br * p.N + n] * h2f(p.sB[n]));
+        }
+      }
+      sB[(bnc + e) * LDT + br] = v;
+    }
+    };
+  if constexpr (LW) {
+    if (loader) {
+      // the ring's first kSlots - 1 steps; steps 0 and 1 landed before the first barrier
+      if (lora_here) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
+      }
+#pragma unroll
+      for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
+      wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();
+      lds_barrier();
+      // load waves: step s + kSlots - 1 into the slot freed by the previous barrier, then
+      // wait until step s + 2 has landed (the compute waves read its weights right after
+      // this step's barrier, its X one step later).  The T parts of the LoRA term come one
+      // per step, in part order, each added two steps after it is issued (by then the wait
+      // for a later ring step has covered it).
+      auto lstep = [&](int s, auto buf_c) {
+        constexpr int b = decltype(buf_c)::value;
+        const bool tl = lora_here && t_loader;
+        if (tl && s >= 2 && s - 2 < p.tparts) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            tsum[4 * q + 0] += tw[b][q].x;
+            tsum[4 * q + 1] += tw[b][q].y;
+            tsum[4 * q + 2] += tw[b][q].z;
+            tsum[4 * q + 3] += tw[b][q].w;
+          }
+        }
+        const bool tnew = lora_here && s < p.tparts;   // uniform: the wait below counts its loads
+        if (tnew) {
+          const float *src = p.tpart + ((size_t)s * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) tw[b][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
+        }
+        issue(s + kSlots - 1, (s + kSlots - 1) % kSlots);
+        if (tnew) wait_vmcnt<(kSlots - 3) * kLoadsPerStep + 4>();
+        else wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();
+        lds_barrier();
+      };
+      constexpr std::integral_constant<int, 0> kB0{};
+      constexpr std::integral_constant<int, 1> kB1{};
+      int s = 0;
+      for (; s + 1 < nsteps; s += 2) {
+        lstep(s, kB0);
+        lstep(s + 1, kB1);
+      }
+      if (s < nsteps) lstep(s, kB0);
+      wait_vmcnt<0>();
+      if (lora_here && t_loader) {
+        // the parts issued in the last two steps, then any beyond the K range's steps
+  #pragma unroll
+        for (int d = 2; d >= 1; --d) {
+          const int pp = nsteps - d;
+          if (pp >= 0 && pp < p.tparts) {
+            const int b = pp & 1;
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 v = b ? tw[1][q] : tw[0][q];
+              tsum[4 * q + 0] += v.x;
+              tsum[4 * q + 1] += v.y;
+              tsum[4 * q + 2] += v.z;
+              tsum[4 * q + 3] += v.w;
+            }
+          }
+        }
+        for (int pp = nsteps; pp < p.tparts; ++pp) {
+          const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
+            tsum[4 * q + 0] += v.x;
+            tsum[4 * q + 1] += v.y;
+            tsum[4 * q + 2] += v.z;
+            tsum[4 * q + 3] += v.w;
+          }
+        }
+      }
+
+      wait_vmcnt<0>();
+      lds_barrier();                        // the compute waves' last step
+      if (lora_here) write_lora_operands();
+      __syncthreads();                      // the compute waves' epilogue barrier
+      return;
+    }
+  }
+
   f16x_t acc[MB][2];
 #pragma unroll
   for (int a = 0; a < MB; ++a)
@@ -383,95 +570,59 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
                                                              acc[mb][nb], 0, 0, 0);
   };
 
-  // LoRA epilogue operands, fetched first (ordinary loads that complete ahead of the ring
-  // loads): T rows (FP32 K-part partials, added in part order) and this thread's B slice.
-  // Two threads per tile row: for 64-row tiles only waves 0 and 1 load T, and only the
-  // parts that exist (the others' loads would be wasted L2 traffic in every tile).
-  float tsum[16];
-  u4_t braw[2];
-  uint32_t bsc[8];
-  bool bvec = false;
-  const int trow = tid >> 1, thh = (tid & 1) * 16;
-  const bool t_loader = trow < BMT;            // wave-uniform
-  const int br = tid >> 3, bnc = (tid & 7) * 16;
-  constexpr int kTPartsAhead = 8;            // T parts loaded before the ring starts
-  float4 tv[kTPartsAhead][4];
-  if (lora_here) {
-    const size_t mrow = (size_t)min(m0 + trow, p.M - 1);
-    if (t_loader) {
-#pragma unroll
-      for (int pp = 0; pp < kTPartsAhead; ++pp) {
-        if (pp < p.tparts) {
-          const float *src = p.tpart + ((size_t)pp * p.M + mrow) * kRank + thh;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) tv[pp][q] = *reinterpret_cast<const float4 *>(src + 4 * q);
-        }
-      }
-    }
-    const int n = n0 + bnc;
-    if constexpr (LORA == 1) {
-      bvec = (p.N % 8) == 0 && n + 16 <= p.N;
-      if (bvec) {
-        const uint16_t *src = static_cast<const uint16_t *>(p.B) + (size_t)br * p.N + n;
-        braw[0] = *reinterpret_cast<const u4_t *>(src);
-        braw[1] = *reinterpret_cast<const u4_t *>(src + 8);
-      }
-    } else {
-      bvec = (p.N % 16) == 0 && n + 16 <= p.N;
-      if (bvec) {
-        braw[0] = *reinterpret_cast<const u4_t *>(static_cast<const int8_t *>(p.B) + (size_t)br * p.N + n);
-        const u4_t s0 = *reinterpret_cast<const u4_t *>(p.sB + n);
-        const u4_t s1 = *reinterpret_cast<const u4_t *>(p.sB + n + 8);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bsc[q] = s0[q];
-          bsc[4 + q] = s1[q];
-        }
-      }
-    }
-  }
-
   // ---- prologue: steps 0 .. kSlots - 2 in flight, step 0 dequantized ----
-#pragma unroll
-  for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
-  if (lora_here) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
-#pragma unroll
-    for (int pp = 0; pp < kTPartsAhead; ++pp) {
-      if (t_loader && pp < p.tparts) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          tsum[4 * q + 0] += tv[pp][q].x;
-          tsum[4 * q + 1] += tv[pp][q].y;
-          tsum[4 * q + 2] += tv[pp][q].z;
-          tsum[4 * q + 3] += tv[pp][q].w;
-        }
-      }
-    }
-    for (int pp = kTPartsAhead; t_loader && pp < p.tparts; ++pp) {
-      const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
-        tsum[4 * q + 0] += v.x;
-        tsum[4 * q + 1] += v.y;
-        tsum[4 * q + 2] += v.z;
-        tsum[4 * q + 3] += v.w;
-      }
-    }
-  }
   u4_t bcur[2][2], bnext[2][2];
   h8_t acur[2][MB];
-  wait_vmcnt<(kSlots - 2) * kLoadsPerStep>();   // own loads of step 0 have landed
-  {
-    Raw rw;
-    dq_read(0, rw);
-    dq_compute(0, rw, 0, bcur);
-    dq_compute(0, rw, 1, bcur);
+  if constexpr (LW) {
+    {
+      lds_barrier();                        // steps 0 and 1 (X and weights) are in LDS
+      Raw rw;
+      dq_read(0, rw);
+      dq_compute(0, rw, 0, bcur);
+      dq_compute(0, rw, 1, bcur);
+      read_a(0, acur);
+    }
+  } else {
+  #pragma unroll
+    for (int st = 0; st < kSlots - 1; ++st) issue(st, st);
+    if (lora_here) {
+  #pragma unroll
+      for (int e = 0; e < 16; ++e) tsum[e] = 0.f;
+  #pragma unroll
+      for (int pp = 0; pp < kTPartsAhead; ++pp) {
+        if (t_loader && pp < p.tparts) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            tsum[4 * q + 0] += tv[pp][q].x;
+            tsum[4 * q + 1] += tv[pp][q].y;
+            tsum[4 * q + 2] += tv[pp][q].z;
+            tsum[4 * q + 3] += tv[pp][q].w;
+          }
+        }
+      }
+      for (int pp = kTPartsAhead; t_loader && pp < p.tparts; ++pp) {
+        const float *src = p.tpart + ((size_t)pp * p.M + (size_t)min(m0 + trow, p.M - 1)) * kRank + thh;
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4 *>(src + 4 * q);
+          tsum[4 * q + 0] += v.x;
+          tsum[4 * q + 1] += v.y;
+          tsum[4 * q + 2] += v.z;
+          tsum[4 * q + 3] += v.w;
+        }
+      }
+    }
+    wait_vmcnt<(kSlots - 2) * kLoadsPerStep>();   // own loads of step 0 have landed
+    {
+      Raw rw;
+      dq_read(0, rw);
+      dq_compute(0, rw, 0, bcur);
+      dq_compute(0, rw, 1, bcur);
+    }
+    lds_barrier();                          // step 0's X tile (all waves) is in LDS
+    read_a(0, acur);
+
   }
-  lds_barrier();                          // step 0's X tile (all waves) is in LDS
-  read_a(0, acur);
 
   // ---- main loop: step s computes; step s+1 is dequantized; step s+3 is loaded ----
   // Source order is issue order (scheduling barriers keep the compiler from regrouping):
@@ -483,19 +634,21 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     constexpr bool mid = decltype(mid_c)::value;
     const int ls = (slot + kSlots - 1) % kSlots;
     const int ns = (slot + 1) % kSlots;
-    wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();   // own loads of step s+1 have landed (later ones may not)
+    if constexpr (!LW) wait_vmcnt<(kSlots - 3) * kLoadsPerStep>();   // own loads of step s+1 have landed (later ones may not)
     Raw rw;
     dq_read(ns, rw);                      // past the end: unused, from a loaded slot
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 0);
-    if constexpr (mid) issue_x_mid(s + kSlots - 1, ls, 0);
+    if constexpr (LW) {
+    } else if constexpr (mid) issue_x_mid(s + kSlots - 1, ls, 0);
     else issue_x(s + kSlots - 1, ls, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 1);
     dq_compute(s + 1, rw, 0, bn);
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 1, 0);
-    if constexpr (mid) {
+    if constexpr (LW) {
+    } else if constexpr (mid) {
       issue_x_mid(s + kSlots - 1, ls, 1);
       issue_w_mid(s + kSlots - 1, ls);
     } else {
@@ -534,6 +687,7 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
     if (s + i < nsteps) body(kEdge, s + i, bcur, bnext, i);
     if (i + 1 < kSlots - 1 && s + i + 1 < nsteps) body(kEdge, s + i + 1, bnext, bcur, i + 1);
   }
+
   wait_vmcnt<0>();                        // the trailing loads into free slots are done
   lds_barrier();
 
@@ -562,46 +716,11 @@ __global__ __launch_bounds__(kThreads, BMT == 64 ? 2 : 1) void gemm_kernel(GemmP
               float4{acc[give0 + b][nb][4 * v4], acc[give0 + b][nb][4 * v4 + 1], acc[give0 + b][nb][4 * v4 + 2],
                      acc[give0 + b][nb][4 * v4 + 3]};
   };
-  if (kh == 0) give(std::integral_constant<int, MBH>{});
-  else give(std::integral_constant<int, 0>{});
-  _Float16 *sT = reinterpret_cast<_Float16 *>(smem + kEpiOff);
-  _Float16 *sB = sT + BMT * LDT;
-  if (lora_here) {
-    // epilogue operands: T tile [BMT m][32 r] (fp16, rounded once from the FP32 sum) and
-    // the B tile transposed to [128 n][32 r]
-    u4_t o[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const h2_t hv = {(_Float16)tsum[8 * q + 2 * d], (_Float16)tsum[8 * q + 2 * d + 1]};
-        o[q][d] = as_u32(hv);
-      }
-    if (trow < BMT) {
-      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh]) = o[0];
-      *reinterpret_cast<u4_t *>(&sT[trow * LDT + thh + 8]) = o[1];
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int n = n0 + bnc + e;
-      _Float16 v = (_Float16)0.f;
-      if (bvec) {
-        if constexpr (LORA == 1) {
-          v = as_h2(braw[e >> 3][(e & 7) >> 1])[e & 1];
-        } else {
-          const int8_t b8 = (int8_t)((braw[0][e >> 2] >> (8 * (e & 3))) & 0xff);
-          v = (_Float16)((float)b8 * (float)as_h2(bsc[e >> 1])[e & 1]);
-        }
-      } else if (n < p.N) {
-        if constexpr (LORA == 1) {
-          v = __builtin_bit_cast(_Float16, static_cast<const uint16_t *>(p.B)[(size_t)br * p.N + n]);
-        } else {
-          v = (_Float16)((float)static_cast<const int8_t *>(p.B)[(size_t)br * p.N + n] * h2f(p.sB[n]));
-        }
-      }
-      sB[(bnc + e) * LDT + br] = v;
-    }
+  if (!loader) {
+    if (kh == 0) give(std::integral_constant<int, MBH>{});
+    else give(std::integral_constant<int, 0>{});
   }
+  if (!LW && lora_here) write_lora_operands();
   __syncthreads();
 
   // own row blocks: + the LoRA term (two MFMA k-steps of 16 over the rank), then + the
@@ -829,7 +948,8 @@ __global__ __launch_bounds__(256) void tail_reduce_kernel(const float *part, int
 template <int BITS, bool HAS_ZP>
 hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
   const int ntiles = p.MT * p.NT;
-  const dim3 grid(p.tsplits > 1 ? p.tail0 + (ntiles - p.tail0) * p.tsplits : ntiles * p.splits), block(kThreads);
+  const dim3 grid(p.tsplits > 1 ? p.tail0 + (ntiles - p.tail0) * p.tsplits : ntiles * p.splits);
+  const dim3 block(p.bm == 64 ? kThreads : 2 * kThreads);   // 128-row tiles: 4 compute + 4 load waves
   if (p.bm == 64) {
     switch (lora) {
       case 0: hipLaunchKernelGGL((gemm_kernel<BITS, HAS_ZP, 0, 64>), grid, block, 0, s, p); break;
