@@ -293,6 +293,28 @@ def test_gemm_tile_rows_both(adapter):
         compare(run(case)[rows], oracle.matmul(rows_case(case, rows)), what="tiles M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
+def test_gemm_load_waves_split_k(bits, adapter):
+    """128-row tiles, whose load waves issue the ring's loads and fetch the LoRA operands
+    (B, and the T parts one per step), with K split over 3 ranges (11, 11 and 10 steps; the
+    first range adds the LoRA term) and a ragged last row tile: every output checked."""
+    M, N, K = 134, 9728, 4096
+    kind = {None: 0, "f16": 1, "q8": 2}[adapter]
+    _, desc = mnb.mnb_describe_route(M, N, K, bits, 1, kind)
+    assert "tile=128x128x64 splits=3" in desc, desc
+    case = si.make_random(270 + bits, M, N, K, bits, True, adapter)
+    ref = oracle.matmul(case)
+    peak = float(np.abs(ref).max())
+    if peak > 8.0:
+        # scales shrunk so that the fp16 outputs' own rounding stays below the absolute
+        # bound (|y| <= 8: half an ulp is at most 2^-8)
+        sc = case["scales"].view(np.float16).astype(np.float32) * np.float32(8.0 / peak)
+        case["scales"] = sc.astype(np.float16).view(np.uint16)
+        ref = oracle.matmul(case)
+    compare(run(case), ref, what="%s M=%d N=%d K=%d" % (desc, M, N, K))
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("adapter", [None, "f16", "q8"], ids=["base", "f16", "q8"])
 def test_gemm_split_k_ranges(bits, adapter):
