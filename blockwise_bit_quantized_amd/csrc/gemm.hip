@@ -545,8 +545,10 @@ __global__ __launch_bounds__(BMT == 128 ? 2 * kThreads : kThreads, BMT == 64 ? 2
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
 
-  // ---- X operands of this wave's block of one K-step (read right after the barrier
-  // that publishes the step, so their latency passes while the next step is prepared) ----
+  // ---- X operands of this wave's block of one K-step: the first k16 half right after
+  // the barrier that publishes the step, the second from the same slot once the step's
+  // first MFMAs are issued (the slot is reused only after the step's own barrier), so
+  // only half of the reads stand between the barrier and the first MFMA ----
   auto read_a_kk = [&](int slot, h8_t (&af)[2][MB], int kk) {
     const uint8_t *xs = smem + slot * SL::kBytes + SL::kX;
     const int c = 4 * kh + 2 * hi + kk;        // 8-k chunk of the step (see the B operand)
@@ -639,6 +641,7 @@ __global__ __launch_bounds__(BMT == 128 ? 2 * kThreads : kThreads, BMT == 64 ? 2
     dq_read(ns, rw);                      // past the end: unused, from a loaded slot
     __builtin_amdgcn_sched_barrier(0);
     mfma_q(acur, bc, 0, 0);
+    read_a_kk(slot, acur, 1);             // this step's second k16 half, from its own slot
     if constexpr (LW) {
     } else if constexpr (mid) issue_x_mid(s + kSlots - 1, ls, 0);
     else issue_x(s + kSlots - 1, ls, 0);
@@ -660,7 +663,7 @@ __global__ __launch_bounds__(BMT == 128 ? 2 * kThreads : kThreads, BMT == 64 ? 2
     dq_compute(s + 1, rw, 1, bn);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();                        // step s+1's X ready for all; slot s free
-    read_a(ns, acur);                     // past the end: unused
+    read_a_kk(ns, acur, 0);               // past the end: unused
   };
   // unrolled by the ring depth, so ring slots are compile-time constants
   // (first the iterations whose loads are all for steps before the last: s + 2 kSlots - 2
