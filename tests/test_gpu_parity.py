@@ -284,8 +284,10 @@ SPLIT_SHAPES = [(40, 136, 1056), (300, 130, 800), (2, 200, 1024), (200, 1000, 20
 @pytest.mark.parametrize("adapter", [None, "f16"], ids=["base", "f16"])
 def test_gemm_tile_rows_both(adapter):
     """Both tile heights: 128-row tiles when they fill the CUs' rounds (and most of a
-    last one), 64-row tiles otherwise."""
-    for i, (M, N, K, bm) in enumerate([(256, 12800, 512, 128), (260, 200, 320, 64), (1024, 4096, 256, 128)]):
+    last one), 64-row tiles otherwise; the 128-row tiles' load waves also with K ranges of
+    one step (K = 32) and two steps, the second ragged (K = 96)."""
+    for i, (M, N, K, bm) in enumerate([(256, 12800, 512, 128), (260, 200, 320, 64), (1024, 4096, 256, 128),
+                                       (1024, 4096, 32, 128), (1024, 4096, 96, 128)]):
         _, desc = mnb.mnb_describe_route(M, N, K, 4, 1, 1 if adapter else 0)
         assert "tile=%dx128x64" % bm in desc, desc
         case = si.make_random(210 + i, M, N, K, 4, True, adapter, bias=i == 1)
