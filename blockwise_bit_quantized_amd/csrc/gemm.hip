@@ -971,16 +971,18 @@ hipError_t launch2(int lora, const GemmParams &p, hipStream_t s) {
 
 }  // namespace
 
-// Tile rows.  128-row tiles (one workgroup per CU) dequantize each weight once per 128
-// rows; 64-row tiles dequantize it twice as often but run two workgroups per CU, whose
-// loads, waits and matrix work interleave.  Measured: 128 wins when the tiles fill whole
-// rounds of the 256 CUs (1024 x 4096: 56 against 60 us); 64 wins when the last round of
-// 128-row tiles would be at most half full (1024 x 9728 at M = 512: 59 against 74 us; small
-// M by 10-20%).
+// Tile rows.  128-row tiles (one workgroup per CU, with load waves) dequantize each weight
+// once per 128 rows; 64-row tiles dequantize it twice as often but run two workgroups per
+// CU, whose loads, waits and matrix work interleave.  Measured: 128 wins when the tiles fill
+// whole rounds of the 256 CUs (1024 x 4096: 56 against 60 us), and from M = 256 up when all
+// of them fit one round, K split to fill it (x 4096 x 4096 with the adapter: M = 256 / 384 /
+// 512 29.4 / 34.6 / 38.1 against 28.7 / 31.2 / 34.2 us; M = 32 / 64 / 128 lose: 16.6 / 17.6 /
+// 25.1 against 17.4 / 20.1 / 25.3); 64 wins when the last round of 128-row tiles would be at
+// most half full (1024 x 9728 at M = 512: 59 against 74 us).
 int gemm_bm(int M, int N) {
   const long t128 = (((long)M + 127) / 128) * (((long)N + BN - 1) / BN);
   const long rem = t128 % kCUs;
-  return (rem == 0 || rem > kCUs / 2) ? 128 : 64;
+  return (rem == 0 || rem > kCUs / 2 || (t128 <= kCUs && M >= 256)) ? 128 : 64;
 }
 
 hipError_t launch_gemm(int bits, bool has_zp, int lora, const GemmParams &p, hipStream_t s) {
